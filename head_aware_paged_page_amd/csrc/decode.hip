@@ -1,0 +1,302 @@
+// segpaged_decode for bf16: one query token per sequence attends over each
+// head's own page table, split over the page list, merged by log-sum-exp.
+//
+// Follows the RedKnot product profile, section 3 (each head reads only its own
+// pages / visible window, no mask) and the RedKnot HotpotQA tutorial page, which
+// notes the decode side is left essentially unchanged: it is the ordinary
+// split-K paged decode, walking the per-head table.  Decode is bound by memory
+// bandwidth (the Prefill/Decode explainer listed on the PagedAttention &
+// RadixAttention page), so the kernel is built around streaming K/V pages
+// straight from HBM into MFMA operand registers, with no LDS staging:
+//   K pages are token-major: lane (key, 8-dim group) loads 16 B = the A operand
+//   of S^T = K Q^T (v_mfma_f32_16x16x32_bf16, keys x heads);
+//   V pages are dim-major: lane (dim, 8-key group) loads 16 B = the A operand of
+//   O^T = V^T P^T (same instruction, dims x heads).
+// The keys fed to the first product are permuted so that each lane's scores are
+// the 8 consecutive keys its B operand of the second product needs.  Each wave
+// streams 32-key blocks (one or two pages) with the next block's loads in
+// flight; the four waves of a workgroup merge through LDS at the end.
+#include "device_common.hpp"
+
+namespace sp {
+namespace {
+
+constexpr int KB = kDecodeKeysPerBlock;   // 32 keys per block
+constexpr int NWD = kDecodeWaves;
+
+struct DecodeParams {
+    const bf16 *q, *kp, *vp;
+    bf16 *out;
+    float *lse;
+    const int32_t *q_pos, *cls, *window, *row_ptr;
+    const int4 *entries;
+    const int32_t *item_ptr, *part_ptr, *nsplit;
+    float *part_o, *part_lse;
+    int n_seq, n_rows, G, ps, Hq;
+    int64_t n_phys;
+    float scale_log2;
+};
+
+template <int D>
+struct Block {
+    u32x4 k[2][D / 32];   // S^T A operands: [key tile][k-step]
+    u32x4 v[D / 16];      // O^T A operands: [dim tile]
+    int pos[2][4];        // position of each of this lane's 8 keys (kPosInvalid if none)
+};
+
+template <int D>
+__device__ __forceinline__ void load_block(const DecodeParams &P, int e0, int e_hi, Block<D> &B) {
+    const int lane = threadIdx.x & 63;
+    const int m = lane & 15, grp = lane >> 4;
+    const int ps = P.ps;
+    // entries of the block's pages (one or two)
+    int4 en[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int e = e0 + i;
+        en[i] = int4{-1, 0, 0, 0};
+        if (i * ps < KB && e < e_hi) {
+            en[i] = P.entries[e];
+            if (en[i].x < 0 || en[i].x >= P.n_phys) en[i].z = 0;
+        }
+    }
+    // K: A operand row m of key tile kt is key 8*(m/4) + 4*kt + m%4; dims 32*s + 8*grp
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+        const int j = 8 * (m >> 2) + 4 * kt + (m & 3);
+        const int pg = j / ps, tk = j % ps;
+        const int4 e = pg ? en[1] : en[0];
+        const bool ok = tk < e.z;
+        const bf16 *src = P.kp + ((int64_t)e.x * ps + tk) * D + 8 * grp;
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) B.k[kt][s] = ok ? *(const u32x4 *)(src + 32 * s) : u32x4{0, 0, 0, 0};
+    }
+    // V^T: A operand row = dim 16*dt + m, keys 8*grp .. 8*grp+7
+    {
+        const int j = 8 * grp;
+        const int pg = j / ps, tk = j % ps;
+        const int4 e = pg ? en[1] : en[0];
+        const int keep = e.z - tk;
+        const bf16 *src = P.vp + ((int64_t)e.x * D + m) * ps + tk;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+            B.v[dt] = keep > 0 ? keep_first_bf16(*(const u32x4 *)(src + (int64_t)16 * dt * ps), keep)
+                               : u32x4{0, 0, 0, 0};
+    }
+    // positions of this lane's score keys: 8*grp + 4*kt + v
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int j = 8 * grp + 4 * kt + v;
+            const int pg = j / ps, tk = j % ps;
+            const int4 e = pg ? en[1] : en[0];
+            B.pos[kt][v] = tk < e.z ? e.y + tk : kPosInvalid;
+        }
+}
+
+template <int D>
+__global__ __launch_bounds__(NWD * 64) void decode_bf16_kernel(DecodeParams P) {
+    constexpr int DS = D / 32;   // k-steps of S^T
+    constexpr int DT = D / 16;   // dim tiles of O^T
+    __shared__ float sM[NWD][16], sL[NWD][16];
+    __shared__ float sO[NWD][D][17];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, grp = lane >> 4;
+
+    const int b = blockIdx.x;
+    const int r = find_row(P.item_ptr, P.n_rows, b);
+    const int ns = P.nsplit[r];
+    const int sp_i = b - P.item_ptr[r];
+    const int seq = r % P.n_seq, slot = r / P.n_seq;
+    const int G = P.G, ps = P.ps;
+    const int p = P.q_pos[seq];
+    const bool is_local = P.cls[slot] == SP_LOCAL;
+    const int low = is_local ? p - P.window[slot] : INT32_MIN;   // visible iff low < pos <= p
+
+    const int e_beg = P.row_ptr[r], e_end = P.row_ptr[r + 1];
+    const int4 *E = P.entries;
+    const int hi = first_greater(e_beg, e_end, p, [&](int e) { return E[e].y; });
+    int lo = e_beg;
+    if (is_local) lo = first_greater(e_beg, hi, low, [&](int e) { return E[e].y + E[e].z - 1; });
+    const int ppb = KB / ps;                          // pages per 32-key block (page_size 16 or 32)
+    int chunk = (hi - lo + ns - 1) / ns;
+    chunk = (chunk + ppb - 1) / ppb * ppb;
+    const int my_lo = min(hi, lo + sp_i * chunk);
+    const int my_hi = min(hi, my_lo + chunk);
+    const int n_blocks = (my_hi - my_lo + ppb - 1) / ppb;
+
+    // Q^T B operand: head n of the slot, dims 32*s + 8*grp
+    bf16x8 qf[DS];
+    {
+        const bool ok = n < G;
+        const bf16 *qrow = P.q + ((int64_t)seq * P.Hq + (int64_t)slot * G + (ok ? n : 0)) * D + 8 * grp;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) qf[s] = u4_as_bf16x8(ok ? *(const u32x4 *)(qrow + 32 * s) : u32x4{0, 0, 0, 0});
+    }
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    Block<D> cur, nxt;
+    int blk = wave;
+    if (blk < n_blocks) load_block<D>(P, my_lo + blk * ppb, my_hi, cur);
+    for (; blk < n_blocks; blk += NWD) {
+        if (blk + NWD < n_blocks) load_block<D>(P, my_lo + (blk + NWD) * ppb, my_hi, nxt);
+
+        f32x4 S[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < DS; ++s) S[kt] = mfma16x16x32(u4_as_bf16x8(cur.k[kt][s]), qf[s], S[kt]);
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int kpos = cur.pos[kt][v];
+                float x = S[kt][v] * P.scale_log2;
+                if (!(kpos <= p && kpos > low)) x = -INFINITY;
+                S[kt][v] = x;
+                mx = fmaxf(mx, x);
+            }
+        mx = fmaxf(mx, xor_lane(mx, 16));
+        mx = fmaxf(mx, xor_lane(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = exp2f(m_run - m_use);
+        float rs = 0.f;
+        u32x4 pk;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            float pv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                pv[v] = exp2f(S[kt][v] - m_use);
+                rs += pv[v];
+            }
+            pk[2 * kt] = pack_bf16x2(pv[0], pv[1]);
+            pk[2 * kt + 1] = pack_bf16x2(pv[2], pv[3]);
+        }
+        l_run = l_run * alpha + rs;
+        m_run = m_new;
+        const bf16x8 pb = u4_as_bf16x8(pk);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma16x16x32(u4_as_bf16x8(cur.v[dt]), pb, acc[dt] * alpha);
+        cur = nxt;
+    }
+
+    // ---- combine the four waves
+    float l = l_run + xor_lane(l_run, 16);
+    l += xor_lane(l, 32);
+    if (grp == 0) {
+        sM[wave][n] = m_run;
+        sL[wave][n] = l;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sO[wave][16 * dt + 4 * grp + v][n] = acc[dt][v];
+    __syncthreads();
+    const int64_t part = ns > 1 ? (int64_t)P.part_ptr[r] + sp_i : 0;
+    for (int idx = threadIdx.x; idx < G * D; idx += NWD * 64) {
+        const int hh = idx / D, d = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NWD; ++w) M = fmaxf(M, sM[w][hh]);
+        float o = 0.f, z = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < NWD; ++w) {
+                const float f = exp2f(sM[w][hh] - M);
+                o += f * sO[w][d][hh];
+                z += f * sL[w][hh];
+            }
+        }
+        const float inv = z > 0.f ? 1.f / z : 0.f;
+        const float lse = z > 0.f ? (M + log2f(z)) * kLn2 : -INFINITY;
+        const int64_t orow = (int64_t)seq * P.Hq + (int64_t)slot * G + hh;
+        if (ns == 1) {
+            P.out[orow * D + d] = f32_to_bf16(o * inv);
+            if (P.lse && d == 0) P.lse[orow] = lse;
+        } else {
+            P.part_o[(part * G + hh) * D + d] = o * inv;
+            if (d == 0) P.part_lse[part * G + hh] = lse;
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams P) {
+    const int r = blockIdx.x;
+    const int ns = P.nsplit[r];
+    if (ns == 1) return;
+    const int seq = r % P.n_seq, slot = r / P.n_seq, G = P.G;
+    const int64_t part0 = P.part_ptr[r];
+    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+        const int hh = idx / D, d = idx % D;
+        float M = -INFINITY;
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, P.part_lse[(part0 + s) * G + hh]);
+        float o = 0.f, z = 0.f;
+        if (M != -INFINITY)
+            for (int s = 0; s < ns; ++s) {
+                const float w = __expf(P.part_lse[(part0 + s) * G + hh] - M);
+                o += w * P.part_o[((part0 + s) * G + hh) * D + d];
+                z += w;
+            }
+        const int64_t orow = (int64_t)seq * P.Hq + (int64_t)slot * G + hh;
+        P.out[orow * D + d] = f32_to_bf16(z > 0.f ? o / z : 0.f);
+        if (P.lse && d == 0) P.lse[orow] = z > 0.f ? M + logf(z) : -INFINITY;
+    }
+}
+
+}  // namespace
+
+int launch_plan(const Plan &p, const int32_t *d_row_ptr, const int32_t *d_tok_ptr, int n_seq, void *ws,
+                hipStream_t stream);
+int launch_decode_f32(const AttnArgs &a, hipStream_t stream);
+
+int launch_decode(const AttnArgs &a, const Plan &p, hipStream_t stream) {
+    if (a.dtype == SP_F32) return launch_decode_f32(a, stream);
+    int rc = launch_plan(p, a.d_row_ptr, nullptr, a.n_seq, a.ws, stream);
+    if (rc) return rc;
+    char *w = (char *)a.ws;
+    DecodeParams P;
+    P.q = (const bf16 *)a.q;
+    P.kp = (const bf16 *)a.k_pool;
+    P.vp = (const bf16 *)a.v_pool;
+    P.out = (bf16 *)a.out;
+    P.lse = a.lse;
+    P.q_pos = a.d_q_pos;
+    P.cls = a.d_cls;
+    P.window = a.d_window;
+    P.row_ptr = a.d_row_ptr;
+    P.entries = (const int4 *)a.d_entries;
+    P.item_ptr = (const int32_t *)(w + p.off_item_ptr);
+    P.part_ptr = (const int32_t *)(w + p.off_part_ptr);
+    P.nsplit = (const int32_t *)(w + p.off_nsplit);
+    P.part_o = (float *)(w + p.off_part_o);
+    P.part_lse = (float *)(w + p.off_part_lse);
+    P.n_seq = a.n_seq;
+    P.n_rows = p.n_rows;
+    P.G = a.group;
+    P.ps = a.page_size;
+    P.Hq = a.n_slot * a.group;
+    P.n_phys = a.n_phys;
+    P.scale_log2 = a.scale * kLog2e;
+    if (a.head_dim == 128) {
+        hipLaunchKernelGGL(decode_bf16_kernel<128>, dim3((unsigned)p.n_items), dim3(NWD * 64), 0, stream, P);
+        if (p.n_parts) hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(p.n_rows), dim3(256), 0, stream, P);
+    } else {
+        hipLaunchKernelGGL(decode_bf16_kernel<64>, dim3((unsigned)p.n_items), dim3(NWD * 64), 0, stream, P);
+        if (p.n_parts) hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(p.n_rows), dim3(256), 0, stream, P);
+    }
+    return check_hip(hipGetLastError(), "decode launch");
+}
+
+}  // namespace sp

@@ -1,0 +1,100 @@
+// Device-side helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "internal.hpp"
+
+namespace sp {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kPosInvalid = 0x7fffffff;   // position of a key slot that holds no token
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (lowers to v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16 f32_to_bf16(float x) { return (bf16)x; }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16 a = (bf16)lo, b = (bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ bf16x8 u4_as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Zeroes the bf16 elements i >= keep of a 16-byte chunk of 8 bf16.
+__device__ __forceinline__ u32x4 keep_first_bf16(u32x4 v, int keep) {
+    if (keep >= 8) return v;
+    u32x4 r;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t x = v[w];
+        const int e0 = 2 * w, e1 = 2 * w + 1;
+        if (e0 >= keep) x &= 0xffff0000u;
+        if (e1 >= keep) x &= 0x0000ffffu;
+        r[w] = x;
+    }
+    return r;
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Index of the work item's row: the largest r with item_ptr[r] <= b
+// (item_ptr ascending, item_ptr[n_rows] > b).  Wave-parallel 64-ary search.
+__device__ __forceinline__ int find_row(const int32_t *item_ptr, int n_rows, int b) {
+    const int lane = threadIdx.x & 63;
+    int lo = 0, hi = n_rows;   // answer in [lo, hi)
+    while (hi - lo > 1) {
+        const int span = hi - lo;
+        const int step = (span + 63) / 64;
+        const int idx = lo + lane * step;
+        const bool le = idx < hi && item_ptr[idx] <= b;
+        const uint64_t m = __ballot(le);
+        // lanes 0..k-1 satisfy le (prefix); the answer lies in [lo + (k-1)*step, lo + k*step)
+        const int k = __popcll(m);
+        const int nlo = lo + (k - 1) * step;
+        const int nhi = min(hi, lo + k * step);
+        lo = nlo;
+        hi = nhi;
+        if (step == 1) break;
+    }
+    return lo;
+}
+
+// First index e in [a, b) whose key(e) > x, keys ascending in e; b if none.
+template <class Key>
+__device__ __forceinline__ int first_greater(int a, int b, int x, Key key) {
+    const int lane = threadIdx.x & 63;
+    while (b - a > 0) {
+        const int span = b - a;
+        const int step = (span + 63) / 64;
+        const int idx = a + lane * step;
+        const bool le = idx < b && key(idx) <= x;
+        const int k = __popcll(__ballot(le));     // lanes 0..k-1 have key <= x
+        if (step == 1) return a + k;
+        if (k == 0) return a;
+        a = a + (k - 1) * step + 1;               // key(a-1) <= x
+        b = min(b, a - 1 + step);
+    }
+    return a;
+}
+
+}  // namespace sp

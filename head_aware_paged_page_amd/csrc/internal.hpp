@@ -1,0 +1,81 @@
+// Internal declarations shared by the host runtime and the kernels of libsegpaged.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "segpaged.h"
+
+namespace sp {
+
+// ---------------------------------------------------------------- errors
+// Records a printf-style message for segpaged_last_error() and returns `code`.
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+int check_hip(hipError_t e, const char *what);
+
+// ---------------------------------------------------------------- launch plan
+// Tile shapes of the bf16 MFMA kernels.
+constexpr int kPrefillRowsPerWave = 32;   // query rows (token x head) per wave
+constexpr int kPrefillKeysPerTile = 64;   // keys staged in LDS per iteration
+constexpr int kDecodeKeysPerBlock = 32;   // keys one wave consumes per step
+constexpr int kDecodeWaves = 4;
+
+// Split planning targets: enough work items to fill 256 CUs a few times over,
+// while each split still streams at least kMinSplitKeys keys.
+constexpr int kTargetItems = 1024;
+constexpr int kMinSplitKeys = 512;
+constexpr int kMaxSplits = 1024;
+
+// Number of kv splits and work items of one row; identical on host and device.
+__host__ __device__ inline void row_items(int n_entries, int n_qtiles, int chunk_pages,
+                                          int *nsplit, int *items) {
+    int ns = 1;
+    if (n_entries > chunk_pages) {
+        ns = (n_entries + chunk_pages - 1) / chunk_pages;
+        if (ns > kMaxSplits) ns = kMaxSplits;
+    }
+    *nsplit = ns;
+    *items = ns * n_qtiles;
+}
+
+struct Plan {
+    int kind = 0;            // SP_WS_PREFILL / SP_WS_DECODE
+    int n_rows = 0;
+    int waves = 4;           // waves per prefill workgroup
+    int rows_per_tile = 0;   // query rows of one work item (prefill BM, decode group)
+    int tok_per_tile = 1;    // query tokens of one prefill work item
+    int chunk_pages = 0;     // pages per kv split (INT32_MAX = no split)
+    int64_t n_items = 0;     // work items (= workgroups of the attention kernel)
+    int64_t n_parts = 0;     // work items whose result is a partial to merge
+    size_t off_item_ptr = 0, off_part_ptr = 0, off_nsplit = 0, off_part_o = 0, off_part_lse = 0;
+    size_t bytes = 0;        // workspace bytes
+};
+
+int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n_seq, int n_slot,
+              const int32_t *h_tok_ptr, const int32_t *h_row_ptr, Plan *plan);
+
+// ---------------------------------------------------------------- launchers (device code)
+int launch_relocate(const void *k_in, void *k_out, int dtype, int page_size, int head_dim,
+                    int64_t n_phys, int n, const sp_reloc *d_list, double theta, hipStream_t s);
+
+struct AttnArgs {
+    int dtype, head_dim, page_size, group, n_seq, n_slot;
+    const int32_t *d_tok_ptr;   // prefill: [n_seq+1]; decode: nullptr
+    const int32_t *d_q_pos;     // prefill: first query position per seq; decode: query position
+    const int32_t *d_cls, *d_window, *d_row_ptr;
+    const sp_entry *d_entries;
+    const void *q, *k_pool, *v_pool;
+    int64_t n_phys;
+    float scale;
+    void *out;
+    float *lse;
+    void *ws;
+};
+
+int launch_prefill(const AttnArgs &a, const Plan &p, int64_t n_tok, hipStream_t s);
+int launch_decode(const AttnArgs &a, const Plan &p, hipStream_t s);
+
+}  // namespace sp

@@ -1,0 +1,243 @@
+// Host runtime of libsegpaged: errors, launch planning, argument validation and
+// the device entry points (the kernels live in the .hip files).
+#include <algorithm>
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.hpp"
+
+namespace sp {
+
+static thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+int check_hip(hipError_t e, const char *what) {
+    if (e == hipSuccess) return SP_OK;
+    return fail(SP_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static bool bf16_supported(int head_dim) { return head_dim == 64 || head_dim == 128; }
+
+int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n_seq, int n_slot,
+              const int32_t *h_tok_ptr, const int32_t *h_row_ptr, Plan *plan) {
+    if (kind != SP_WS_PREFILL && kind != SP_WS_DECODE) return fail(SP_EINVAL, "workspace kind %d", kind);
+    if (dtype != SP_F32 && dtype != SP_BF16) return fail(SP_EINVAL, "dtype %d", dtype);
+    if (n_seq < 1 || n_slot < 1) return fail(SP_EINVAL, "n_seq=%d n_slot=%d must be >= 1", n_seq, n_slot);
+    if (group < 1 || group > 16) return fail(SP_EUNSUPPORTED, "group %d outside 1..16", group);
+    if (head_dim < 16 || head_dim > 256 || head_dim % 16) return fail(SP_EUNSUPPORTED, "head_dim %d", head_dim);
+    if (page_size < 1) return fail(SP_EINVAL, "page_size %d", page_size);
+    if (!h_row_ptr) return fail(SP_EINVAL, "h_row_ptr is NULL");
+    if (kind == SP_WS_PREFILL && !h_tok_ptr) return fail(SP_EINVAL, "h_tok_ptr is NULL");
+    if ((int64_t)n_slot * n_seq > INT32_MAX - 1) return fail(SP_EINVAL, "too many rows");
+    const int n_rows = n_slot * n_seq;
+    if (h_row_ptr[0] != 0) return fail(SP_EINVAL, "row_ptr[0] must be 0");
+    for (int r = 0; r < n_rows; ++r)
+        if (h_row_ptr[r + 1] <= h_row_ptr[r]) return fail(SP_EINVAL, "row %d has an empty or negative table", r);
+    if (kind == SP_WS_PREFILL) {
+        if (h_tok_ptr[0] != 0) return fail(SP_EINVAL, "tok_ptr[0] must be 0");
+        for (int q = 0; q < n_seq; ++q)
+            if (h_tok_ptr[q + 1] < h_tok_ptr[q]) return fail(SP_EINVAL, "tok_ptr not ascending at %d", q);
+    }
+
+    Plan p;
+    p.kind = kind;
+    p.n_rows = n_rows;
+    size_t off = 0;
+    p.off_item_ptr = off; off += sizeof(int32_t) * (n_rows + 1);
+    p.off_part_ptr = off; off += sizeof(int32_t) * (n_rows + 1);
+    p.off_nsplit = off;   off += sizeof(int32_t) * n_rows;
+    off = align_up(off, 256);
+
+    if (dtype == SP_F32) {
+        // The fp32 kernels take one query token per workgroup and never split.
+        p.rows_per_tile = group;
+        p.tok_per_tile = 1;
+        p.chunk_pages = INT_MAX;
+        p.bytes = off + 256;
+        p.off_part_o = p.off_part_lse = off;
+        *plan = p;
+        return SP_OK;
+    }
+    if (!bf16_supported(head_dim)) return fail(SP_EUNSUPPORTED, "bf16 head_dim %d (64 or 128)", head_dim);
+
+    // work units (row, q-tile) and their page counts
+    int64_t units = 0, work = 0;
+    if (kind == SP_WS_PREFILL) {
+        p.waves = 4;
+        p.rows_per_tile = kPrefillRowsPerWave * p.waves;
+        p.tok_per_tile = p.rows_per_tile / group;
+        for (int r = 0; r < n_rows; ++r) {
+            const int q = r % n_seq;
+            const int64_t nt = h_tok_ptr[q + 1] - h_tok_ptr[q];
+            const int64_t nq = (nt + p.tok_per_tile - 1) / p.tok_per_tile;
+            units += nq;
+            work += nq * (h_row_ptr[r + 1] - h_row_ptr[r]);
+        }
+    } else {
+        p.rows_per_tile = group;
+        p.tok_per_tile = 1;
+        for (int r = 0; r < n_rows; ++r) {
+            units += 1;
+            work += h_row_ptr[r + 1] - h_row_ptr[r];
+        }
+    }
+    const int min_chunk = std::max(1, kMinSplitKeys / page_size);
+    if (units >= kTargetItems / 2) {
+        p.chunk_pages = INT_MAX;
+    } else {
+        const int64_t c = (work + kTargetItems - 1) / kTargetItems;
+        p.chunk_pages = (int)std::min<int64_t>(INT_MAX, std::max<int64_t>(min_chunk, c));
+    }
+    int64_t items = 0, parts = 0;
+    for (int r = 0; r < n_rows; ++r) {
+        int nq = 1;
+        if (kind == SP_WS_PREFILL) {
+            const int q = r % n_seq;
+            const int nt = h_tok_ptr[q + 1] - h_tok_ptr[q];
+            nq = (nt + p.tok_per_tile - 1) / p.tok_per_tile;
+        }
+        int ns, it;
+        row_items(h_row_ptr[r + 1] - h_row_ptr[r], nq, p.chunk_pages, &ns, &it);
+        items += it;
+        if (ns > 1) parts += it;
+    }
+    if (items > INT32_MAX) return fail(SP_EINVAL, "too many work items");
+    p.n_items = items;
+    p.n_parts = parts;
+    p.off_part_o = off;
+    off += align_up(sizeof(float) * (size_t)parts * p.rows_per_tile * head_dim, 256);
+    p.off_part_lse = off;
+    off += align_up(sizeof(float) * (size_t)parts * p.rows_per_tile, 256);
+    p.bytes = std::max<size_t>(off, 256);
+    *plan = p;
+    return SP_OK;
+}
+
+}  // namespace sp
+
+using sp::fail;
+
+extern "C" const char *segpaged_strerror(int status) {
+    switch (status) {
+        case SP_OK: return "ok";
+        case SP_EINVAL: return "invalid argument";
+        case SP_ENOMEM: return "free list too short";
+        case SP_EHIP: return "HIP runtime error";
+        case SP_EUNSUPPORTED: return "unsupported configuration";
+        case SP_EWORKSPACE: return "workspace too small";
+        default: return "unknown status";
+    }
+}
+
+extern "C" const char *segpaged_last_error(void) { return sp::g_err; }
+
+extern "C" int segpaged_version(void) { return 100; }
+
+extern "C" int segpaged_workspace_bytes(int kind, int dtype, int head_dim, int page_size, int group, int n_seq,
+                                        int n_slot, const int32_t *h_tok_ptr, const int32_t *h_row_ptr,
+                                        size_t *bytes) {
+    sp::clear_error();
+    if (!bytes) return fail(SP_EINVAL, "bytes is NULL");
+    sp::Plan p;
+    const int rc = sp::make_plan(kind, dtype, head_dim, page_size, group, n_seq, n_slot, h_tok_ptr, h_row_ptr, &p);
+    if (rc) return rc;
+    *bytes = p.bytes;
+    return SP_OK;
+}
+
+extern "C" int rope_relocate(const void *k_in, void *k_out, int dtype, int page_size, int head_dim, int64_t n_phys,
+                             int n, const sp_reloc *d_list, double rope_theta, void *stream) {
+    sp::clear_error();
+    if (dtype != SP_F32 && dtype != SP_BF16) return fail(SP_EINVAL, "dtype %d", dtype);
+    if (head_dim < 16 || head_dim > 256 || head_dim % 16)
+        return fail(SP_EUNSUPPORTED, "head_dim %d (16..256, multiple of 16)", head_dim);
+    if (page_size < 1 || page_size > 1024) return fail(SP_EUNSUPPORTED, "page_size %d (1..1024)", page_size);
+    if (n < 0 || n_phys < 0) return fail(SP_EINVAL, "n=%d n_phys=%lld", n, (long long)n_phys);
+    if (!(rope_theta > 0.0)) return fail(SP_EINVAL, "rope_theta must be > 0");
+    if (n == 0) return SP_OK;
+    if (!k_in || !k_out || !d_list) return fail(SP_EINVAL, "a pointer is NULL");
+    const size_t esz = dtype == SP_F32 ? 4 : 2;
+    const size_t pool = (size_t)n_phys * page_size * head_dim * esz;
+    const char *a = (const char *)k_in, *b = (const char *)k_out;
+    if (a != b && a < b + pool && b < a + pool) return fail(SP_EINVAL, "k_in and k_out partially overlap");
+    return sp::launch_relocate(k_in, k_out, dtype, page_size, head_dim, n_phys, n, d_list, rope_theta,
+                               (hipStream_t)stream);
+}
+
+static int check_attn(int dtype, int head_dim, int page_size, int group, int n_seq, int n_slot, const void *q,
+                      const void *k, const void *v, int64_t n_phys, float scale, const void *out, const int32_t *cls,
+                      const int32_t *win, const int32_t *row_ptr, const sp_entry *ent, const int32_t *pos,
+                      const void *ws, bool decode) {
+    if (dtype != SP_F32 && dtype != SP_BF16) return fail(SP_EINVAL, "dtype %d", dtype);
+    if (dtype == SP_BF16) {
+        if (head_dim != 64 && head_dim != 128) return fail(SP_EUNSUPPORTED, "bf16 head_dim %d (64 or 128)", head_dim);
+        const bool ok = decode ? (page_size == 16 || page_size == 32)
+                               : (page_size == 16 || page_size == 32 || page_size == 64);
+        if (!ok) return fail(SP_EUNSUPPORTED, "bf16 page_size %d", page_size);
+    }
+    if (group < 1 || group > 16) return fail(SP_EUNSUPPORTED, "group %d outside 1..16", group);
+    if (!(scale > 0.0f) || scale != scale) return fail(SP_EINVAL, "softmax_scale must be > 0");
+    if (n_phys < 1) return fail(SP_EINVAL, "n_phys %lld", (long long)n_phys);
+    if (!q || !k || !v || !out || !cls || !win || !row_ptr || !ent || !pos || !ws)
+        return fail(SP_EINVAL, "a pointer is NULL");
+    (void)n_seq; (void)n_slot;
+    return SP_OK;
+}
+
+extern "C" int segpaged_prefill(int dtype, int head_dim, int page_size, int group, int n_seq, int n_slot,
+                                const int32_t *h_tok_ptr, const int32_t *h_row_ptr, const int32_t *d_tok_ptr,
+                                const int32_t *d_q_pos0, const int32_t *d_cls, const int32_t *d_window,
+                                const int32_t *d_row_ptr, const sp_entry *d_entries, const void *q,
+                                const void *k_pool, const void *v_pool, int64_t n_phys, float softmax_scale,
+                                void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+    sp::clear_error();
+    sp::Plan p;
+    int rc = sp::make_plan(SP_WS_PREFILL, dtype, head_dim, page_size, group, n_seq, n_slot, h_tok_ptr, h_row_ptr, &p);
+    if (rc) return rc;
+    rc = check_attn(dtype, head_dim, page_size, group, n_seq, n_slot, q, k_pool, v_pool, n_phys, softmax_scale, out,
+                    d_cls, d_window, d_row_ptr, d_entries, d_q_pos0, workspace, false);
+    if (rc) return rc;
+    if (!d_tok_ptr) return fail(SP_EINVAL, "d_tok_ptr is NULL");
+    if (workspace_bytes < p.bytes)
+        return fail(SP_EWORKSPACE, "workspace %zu bytes, %zu needed", workspace_bytes, p.bytes);
+    if (((uintptr_t)workspace) % 256) return fail(SP_EINVAL, "workspace must be 256-byte aligned");
+    const int64_t n_tok = h_tok_ptr[n_seq];
+    if (n_tok == 0) return SP_OK;
+    sp::AttnArgs a{dtype, head_dim, page_size, group, n_seq, n_slot, d_tok_ptr, d_q_pos0, d_cls, d_window,
+                   d_row_ptr, d_entries, q, k_pool, v_pool, n_phys, softmax_scale, out, lse, workspace};
+    return sp::launch_prefill(a, p, n_tok, (hipStream_t)stream);
+}
+
+extern "C" int segpaged_decode(int dtype, int head_dim, int page_size, int group, int n_seq, int n_slot,
+                               const int32_t *h_row_ptr, const int32_t *d_q_pos, const int32_t *d_cls,
+                               const int32_t *d_window, const int32_t *d_row_ptr, const sp_entry *d_entries,
+                               const void *q, const void *k_pool, const void *v_pool, int64_t n_phys,
+                               float softmax_scale, void *out, float *lse, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+    sp::clear_error();
+    sp::Plan p;
+    int rc = sp::make_plan(SP_WS_DECODE, dtype, head_dim, page_size, group, n_seq, n_slot, nullptr, h_row_ptr, &p);
+    if (rc) return rc;
+    rc = check_attn(dtype, head_dim, page_size, group, n_seq, n_slot, q, k_pool, v_pool, n_phys, softmax_scale, out,
+                    d_cls, d_window, d_row_ptr, d_entries, d_q_pos, workspace, true);
+    if (rc) return rc;
+    if (workspace_bytes < p.bytes)
+        return fail(SP_EWORKSPACE, "workspace %zu bytes, %zu needed", workspace_bytes, p.bytes);
+    if (((uintptr_t)workspace) % 256) return fail(SP_EINVAL, "workspace must be 256-byte aligned");
+    sp::AttnArgs a{dtype, head_dim, page_size, group, n_seq, n_slot, nullptr, d_q_pos, d_cls, d_window,
+                   d_row_ptr, d_entries, q, k_pool, v_pool, n_phys, softmax_scale, out, lse, workspace};
+    return sp::launch_decode(a, p, (hipStream_t)stream);
+}

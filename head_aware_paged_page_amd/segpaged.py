@@ -1,0 +1,180 @@
+"""ctypes binding of libsegpaged.so - argument marshalling only.
+
+Every call maps one-to-one onto an ``extern "C"`` entry point declared in
+``include/segpaged.h``; all work happens in the library (host table builder)
+and its HIP kernels.  Device arguments are torch tensors on the GPU (torch only
+supplies device memory and the current stream).  If the library has not been
+built this module raises at import of the library, it never falls back.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libsegpaged.so")
+
+SP_OK, SP_EINVAL, SP_ENOMEM, SP_EHIP, SP_EUNSUPPORTED, SP_EWORKSPACE = 0, -1, -2, -3, -4, -5
+SP_GLOBAL, SP_LOCAL, SP_RETRIEVAL, SP_DENSE = 0, 1, 2, 3
+SP_F32, SP_BF16 = 0, 1
+SP_WS_PREFILL, SP_WS_DECODE = 0, 1
+
+ENTRY_FIELDS = 4   # sp_entry / sp_reloc are 4 x int32
+
+
+class SegPagedError(RuntimeError):
+    def __init__(self, status: int, call: str, msg: str):
+        super().__init__(f"{call} failed: status {status} ({msg})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"libsegpaged.so not built at {_LIB_PATH}; run head_aware_paged_page_amd/build.py")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I, I64, D, F, SZ = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_float,
+                               ctypes.c_size_t)
+        L.segpaged_build_tables.argtypes = [I, P, P, P, P, P, I, P, P, P, P, I, I64, P, P, P, P, P, P, P]
+        L.rope_relocate.argtypes = [P, P, I, I, I, I64, I, P, D, P]
+        L.segpaged_workspace_bytes.argtypes = [I, I, I, I, I, I, I, P, P, ctypes.POINTER(SZ)]
+        L.segpaged_prefill.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, I64, F, P, P, P, SZ, P]
+        L.segpaged_decode.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, I64, F, P, P, P, SZ, P]
+        L.segpaged_strerror.restype = ctypes.c_char_p
+        L.segpaged_strerror.argtypes = [I]
+        L.segpaged_last_error.restype = ctypes.c_char_p
+        L.segpaged_last_error.argtypes = []
+        L.segpaged_version.restype = I
+        for fn in ("segpaged_build_tables", "rope_relocate", "segpaged_workspace_bytes", "segpaged_prefill",
+                   "segpaged_decode"):
+            getattr(L, fn).restype = I
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, call: str):
+    if rc != SP_OK:
+        L = lib()
+        msg = L.segpaged_last_error().decode() or L.segpaged_strerror(rc).decode()
+        raise SegPagedError(rc, call, msg)
+
+
+def _i32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return SP_F32
+    if t.dtype == torch.bfloat16:
+        return SP_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# --------------------------------------------------------------------------- host table builder
+
+def build_tables(seg_ptr, segs, n_new, q_lo, q_hi, cls, window, ret_ptr, ret_pages, page_size, free_list,
+                 counts_only=False):
+    """segpaged_build_tables.  ``segs`` is [n_seg, 3] (len, online_base, offline_base).
+
+    Returns dict(counts, chain_ptr, storage, row_ptr, entries [n, 4], reloc [n, 4]) as int32
+    arrays (only ``counts`` when counts_only)."""
+    L = lib()
+    seg_ptr, segs, n_new, q_lo, q_hi = map(_i32, (seg_ptr, segs, n_new, q_lo, q_hi))
+    cls, window, ret_ptr, ret_pages = map(_i32, (cls, window, ret_ptr, ret_pages))
+    free_list = _i32(free_list)
+    n_seq = len(n_new)
+    n_slot = len(cls)
+    counts = np.zeros(3, np.int64)
+    n_free = 0 if free_list is None else len(free_list)
+    args = [n_seq, _ptr(seg_ptr), _ptr(segs), _ptr(n_new), _ptr(q_lo), _ptr(q_hi), n_slot, _ptr(cls),
+            _ptr(window), _ptr(ret_ptr), _ptr(ret_pages), page_size, n_free, _ptr(free_list)]
+    rc = L.segpaged_build_tables(*args, None, None, None, None, None, _ptr(counts))
+    _check(rc, "segpaged_build_tables")
+    if counts_only:
+        return dict(counts=counts)
+    n_rows = n_slot * n_seq
+    chain_ptr = np.zeros(n_rows + 1, np.int32)
+    storage = np.zeros(max(1, counts[0]), np.int32)
+    row_ptr = np.zeros(n_rows + 1, np.int32)
+    entries = np.zeros((max(1, counts[1]), ENTRY_FIELDS), np.int32)
+    reloc = np.zeros((max(1, counts[2]), ENTRY_FIELDS), np.int32)
+    rc = L.segpaged_build_tables(*args, _ptr(chain_ptr), _ptr(storage), _ptr(row_ptr), _ptr(entries),
+                                 _ptr(reloc), _ptr(counts))
+    _check(rc, "segpaged_build_tables")
+    return dict(counts=counts, chain_ptr=chain_ptr, storage=storage[: counts[0]], row_ptr=row_ptr,
+                entries=entries[: counts[1]], reloc=reloc[: counts[2]])
+
+
+# --------------------------------------------------------------------------- device calls
+
+def rope_relocate(k_in, k_out, page_size: int, reloc_dev, theta: float, stream=None):
+    """rope_relocate on K pools [n_phys, page_size, head_dim]; reloc_dev: int32 [n, 4] on the GPU."""
+    n_phys, ps, D = k_in.shape
+    assert ps == page_size and tuple(k_out.shape) == tuple(k_in.shape) and k_out.dtype == k_in.dtype
+    n = reloc_dev.shape[0]
+    rc = lib().rope_relocate(_dptr(k_in), _dptr(k_out), _dtype_code(k_in), page_size, D, n_phys, n,
+                             _dptr(reloc_dev), float(theta), _stream(stream))
+    _check(rc, "rope_relocate")
+
+
+def workspace_bytes(kind: int, dtype: int, head_dim: int, page_size: int, group: int, n_seq: int, n_slot: int,
+                    h_tok_ptr, h_row_ptr) -> int:
+    out = ctypes.c_size_t(0)
+    tp = _i32(h_tok_ptr)
+    rp = _i32(h_row_ptr)
+    rc = lib().segpaged_workspace_bytes(kind, dtype, head_dim, page_size, group, n_seq, n_slot, _ptr(tp), _ptr(rp),
+                                        ctypes.byref(out))
+    _check(rc, "segpaged_workspace_bytes")
+    return out.value
+
+
+def prefill(q, k_pool, v_pool, *, page_size, group, n_seq, n_slot, h_tok_ptr, h_row_ptr, d_tok_ptr, d_q_pos0,
+            d_cls, d_window, d_row_ptr, d_entries, scale, out, lse, workspace, stream=None):
+    """segpaged_prefill.  q/out [n_tok, n_slot*group, D]; pools [n_phys, ps, D] (K) and [n_phys, D, ps] (V)."""
+    D = q.shape[-1]
+    tp = _i32(h_tok_ptr)
+    rp = _i32(h_row_ptr)
+    rc = lib().segpaged_prefill(_dtype_code(q), D, page_size, group, n_seq, n_slot, _ptr(tp), _ptr(rp),
+                                _dptr(d_tok_ptr), _dptr(d_q_pos0), _dptr(d_cls), _dptr(d_window), _dptr(d_row_ptr),
+                                _dptr(d_entries), _dptr(q), _dptr(k_pool), _dptr(v_pool), k_pool.shape[0],
+                                float(scale), _dptr(out), _dptr(lse), _dptr(workspace), workspace.numel(),
+                                _stream(stream))
+    _check(rc, "segpaged_prefill")
+
+
+def decode(q, k_pool, v_pool, *, page_size, group, n_seq, n_slot, h_row_ptr, d_q_pos, d_cls, d_window, d_row_ptr,
+           d_entries, scale, out, lse, workspace, stream=None):
+    """segpaged_decode.  q/out [n_seq, n_slot*group, D]."""
+    D = q.shape[-1]
+    rp = _i32(h_row_ptr)
+    rc = lib().segpaged_decode(_dtype_code(q), D, page_size, group, n_seq, n_slot, _ptr(rp), _dptr(d_q_pos),
+                               _dptr(d_cls), _dptr(d_window), _dptr(d_row_ptr), _dptr(d_entries), _dptr(q),
+                               _dptr(k_pool), _dptr(v_pool), k_pool.shape[0], float(scale), _dptr(out), _dptr(lse),
+                               _dptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "segpaged_decode")
+
+
+def version() -> int:
+    return lib().segpaged_version()

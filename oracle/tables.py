@@ -77,11 +77,12 @@ def allocate(lay, free):
     slice, with row = slot * n_seq + seq.
     """
     rows = lay.n_slot * lay.n_seq
+    chain_len = [len(chain(lay, seq)) for seq in range(lay.n_seq)]
     chain_ptr = np.zeros(rows + 1, np.int64)
     for slot in range(lay.n_slot):
         for seq in range(lay.n_seq):
             r = slot * lay.n_seq + seq
-            chain_ptr[r + 1] = chain_ptr[r] + len(chain(lay, seq))
+            chain_ptr[r + 1] = chain_ptr[r] + chain_len[seq]
     need = int(chain_ptr[-1])
     if need > len(free):
         raise MemoryError(f"free list holds {len(free)} pages, {need} needed")
@@ -150,13 +151,19 @@ def tables(lay, storage, chain_ptr, q_lo, q_hi):
     return row_ptr, ent
 
 
-def reloc_list(lay, storage, chain_ptr):
-    """[(phys, delta, n_valid)] for every stored segment page, allocation order."""
+def reloc_list(lay, storage, chain_ptr, rows=None):
+    """[(phys, delta, n_valid)] for every stored segment page, allocation order
+    (optionally only for the listed rows, row = slot * n_seq + seq)."""
     out = []
+    chains = {}
     for slot in range(lay.n_slot):
         for seq in range(lay.n_seq):
             r = slot * lay.n_seq + seq
-            for i, pg in enumerate(chain(lay, seq)):
+            if rows is not None and r not in rows:
+                continue
+            if seq not in chains:
+                chains[seq] = chain(lay, seq)
+            for i, pg in enumerate(chains[seq]):
                 if pg["seg"] < 0:
                     continue
                 s = pg["seg"]

@@ -1,0 +1,191 @@
+"""The C ABI on the CPU: the library loads and exports every declared symbol, and
+segpaged_build_tables (host-only) matches the oracle's allocation, tables and
+relocation list bit-exactly, plus its error codes."""
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import tables as otab
+import synth
+from synth import custom_layout, GLOBAL, LOCAL, RETRIEVAL, DENSE
+from head_aware_paged_page_amd import segpaged as sp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "segpaged.h")).read()
+    body = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    names = set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", body, flags=re.M))
+    names.discard("if")
+    assert {"segpaged_build_tables", "rope_relocate", "segpaged_prefill", "segpaged_decode",
+            "segpaged_workspace_bytes", "segpaged_strerror", "segpaged_last_error", "segpaged_version"} <= names
+    L = sp.lib()
+    for n in sorted(names):
+        assert hasattr(L, n), f"{n} declared in segpaged.h but not exported"
+    assert sp.version() == 100
+
+
+def _lib_tables(lay, call, free):
+    return sp.build_tables(**lay.abi_arrays(call), page_size=lay.page_size, free_list=free)
+
+
+def _compare(lay, free, rows=None):
+    """Library vs oracle for the prefill and the decode call; `rows` limits the table rows compared."""
+    storage, chain_ptr = otab.allocate(lay, free)
+    for call in ("prefill", "decode"):
+        a = lay.abi_arrays(call)
+        t = _lib_tables(lay, call, free)
+        assert np.array_equal(t["chain_ptr"], chain_ptr)
+        assert np.array_equal(t["storage"], storage)
+        if rows is None:
+            row_ptr, ent = otab.tables(lay, storage, chain_ptr, a["q_lo"], a["q_hi"])
+            assert np.array_equal(t["row_ptr"], row_ptr)
+            assert np.array_equal(t["entries"][:, :3], ent)
+            assert not t["entries"][:, 3].any()
+        else:
+            for r in rows:
+                slot, seq = divmod(r, lay.n_seq)
+                ent = otab.row_table(lay, storage, chain_ptr, slot, seq, a["q_lo"][seq], a["q_hi"][seq])
+                got = t["entries"][t["row_ptr"][r]:t["row_ptr"][r + 1], :3]
+                assert np.array_equal(got, ent), f"row {r} ({call})"
+    rl = otab.reloc_list(lay, storage, chain_ptr, rows=None if rows is None else set(rows))
+    if rows is None:
+        assert np.array_equal(t["reloc"][:, :3], rl)
+    else:
+        seg_pages = [sum(-(-int(l) // lay.page_size) for l in lay.seg_len[q]) for q in range(lay.n_seq)]
+        got = []
+        off = 0
+        for r in range(lay.n_slot * lay.n_seq):
+            n = seg_pages[r % lay.n_seq]
+            if r in rows:
+                got.append(t["reloc"][off:off + n, :3])
+            off += n
+        assert np.array_equal(np.concatenate(got), rl)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_layouts_bit_exact(seed):
+    r = np.random.default_rng(seed)
+    ps = int(r.choice([1, 2, 3, 4, 8, 16, 32]))
+    n_seq = int(r.integers(1, 4))
+    lens = [list(r.integers(1, 70, size=int(r.integers(0, 4)))) for _ in range(n_seq)]
+    off = [list(r.integers(-300, 300, size=len(l))) for l in lens]
+    classes = [(GLOBAL, 0), (LOCAL, int(r.integers(1, 90))), (RETRIEVAL, 0), (DENSE, 0), (LOCAL, 1)]
+    ret = {}
+    for q in range(n_seq):
+        nsp = sum(-(-l // ps) for l in lens[q])
+        k = int(r.integers(0, nsp + 1))
+        ret[(2, q)] = np.sort(r.choice(nsp, size=k, replace=False))
+    lay = custom_layout(seg_lens=lens, offline=off, n_prefill=int(r.integers(1, 40)), n_decode=1, classes=classes,
+                        page_size=ps, ret_lists=ret)
+    n = sp.build_tables(**lay.abi_arrays("prefill"), page_size=ps, free_list=None, counts_only=True)["counts"][0]
+    free = np.random.default_rng(seed + 100).permutation(int(n) + 7).astype(np.int32)
+    _compare(lay, free)
+
+
+def test_tiny_config_bit_exact():
+    lay = synth.make_layout("tiny")
+    n = sp.build_tables(**lay.abi_arrays("prefill"), page_size=lay.page_size, free_list=None,
+                        counts_only=True)["counts"][0]
+    _compare(lay, synth.free_list(lay, int(n)))
+
+
+@pytest.mark.parametrize("name", ["32k", "16k"])
+def test_full_configs_bit_exact(name):
+    lay = synth.make_layout(name)
+    n = sp.build_tables(**lay.abi_arrays("prefill"), page_size=lay.page_size, free_list=None,
+                        counts_only=True)["counts"][0]
+    _compare(lay, synth.free_list(lay, int(n)))
+
+
+@pytest.mark.parametrize("name", ["128k", "batch"])
+def test_large_configs_sampled_rows_bit_exact(name):
+    lay = synth.make_layout(name)
+    n = sp.build_tables(**lay.abi_arrays("prefill"), page_size=lay.page_size, free_list=None,
+                        counts_only=True)["counts"][0]
+    free = synth.free_list(lay, int(n))
+    rows_all = lay.n_slot * lay.n_seq
+    rng = np.random.default_rng(7)
+    # every class, plus the first and last rows
+    rows = {0, rows_all - 1}
+    for c in (GLOBAL, LOCAL, RETRIEVAL, DENSE):
+        slots = np.nonzero(lay.cls == c)[0]
+        if len(slots):
+            slot = int(rng.choice(slots))
+            rows.add(slot * lay.n_seq + int(rng.integers(0, lay.n_seq)))
+    _compare(lay, free, rows=sorted(rows))
+
+
+def test_hand_fixture_and_block_walkthrough(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "tiny_tables_by_hand.json")))
+    ret = {tuple(int(x) for x in k.split(",")): v for k, v in g["ret_lists"].items()}
+    lay = custom_layout(seg_lens=[g["seg_lens"]], offline=[g["offline"]], n_prefill=g["n_prefill"],
+                        n_decode=g["n_decode"], classes=[tuple(c) for c in g["classes"]],
+                        page_size=g["page_size"], ret_lists=ret)
+    for call in ("prefill", "decode"):
+        t = _lib_tables(lay, call, np.asarray(g["free_list"]))
+        assert t["storage"].tolist() == g["expected_storage"]
+        rows = [t["entries"][t["row_ptr"][r]:t["row_ptr"][r + 1], :3].tolist() for r in range(4)]
+        assert rows == g[f"expected_{call}_rows"]
+        assert t["reloc"][:, :3].tolist() == g["expected_reloc"]
+    w = json.load(open(os.path.join(golden_dir, "paged_block_walkthrough.json")))
+    lay = custom_layout(seg_lens=[[]], offline=[[]], n_prefill=w["prompt_tokens"], n_decode=w["generated_tokens"],
+                        classes=[(GLOBAL, 0)], page_size=w["page_size"])
+    a = lay.abi_arrays("decode")
+    a["q_lo"] = a["q_hi"] = np.array([8], np.int32)   # the second generated token
+    t = sp.build_tables(**a, page_size=w["page_size"], free_list=np.asarray(w["free_list"]))
+    assert t["storage"].tolist() == w["expected_block_table"]
+    assert t["entries"][:, 0].tolist() == w["expected_block_table"]
+    assert sorted(w["free_list"][len(t["storage"]):]) == w["expected_unused_blocks"]
+
+
+def _base_tiny():
+    lay = custom_layout(seg_lens=[[10, 5]], offline=[[0, 0]], n_prefill=4, n_decode=1,
+                        classes=[(GLOBAL, 0), (LOCAL, 3), (RETRIEVAL, 0)], page_size=4,
+                        ret_lists={(2, 0): [0, 3]})
+    return lay, lay.abi_arrays("prefill")
+
+
+def _expect(code, **kw):
+    lay, a = _base_tiny()
+    free = kw.pop("free_list", np.arange(100, dtype=np.int32))
+    a.update(kw)
+    with pytest.raises(sp.SegPagedError) as e:
+        sp.build_tables(**a, page_size=kw.pop("page_size", 4) if "page_size" in kw else 4, free_list=free)
+    assert e.value.status == code
+
+
+def test_error_codes():
+    lay, a = _base_tiny()
+    n = sp.build_tables(**a, page_size=4, free_list=None, counts_only=True)["counts"][0]
+    _expect(sp.SP_ENOMEM, free_list=np.arange(n - 1, dtype=np.int32))
+    _expect(sp.SP_EINVAL, free_list=np.array([0] + list(range(n)), np.int32))          # repeated page id
+    _expect(sp.SP_EINVAL, free_list=np.array([-1] + list(range(n)), np.int32))         # negative page id
+    _expect(sp.SP_EINVAL, cls=np.array([0, 7, 2], np.int32))                           # unknown class
+    _expect(sp.SP_EINVAL, window=np.array([0, 0, 0], np.int32))                        # local window 0
+    _expect(sp.SP_EINVAL, ret_pages=np.array([3, 0], np.int32))                        # not ascending
+    _expect(sp.SP_EINVAL, ret_pages=np.array([0, 5], np.int32))                        # beyond the segment pages
+    _expect(sp.SP_EINVAL, q_lo=np.array([14], np.int32))                               # query inside a segment
+    _expect(sp.SP_EINVAL, q_hi=np.array([20], np.int32))                               # beyond the new tokens
+    _expect(sp.SP_EINVAL, segs=np.array([[10, 0, 0], [5, 3, 0]], np.int32))           # overlapping segments
+    _expect(sp.SP_EINVAL, segs=np.array([[10, 0, 0], [5, 2**31 - 3, 0]], np.int32))   # position overflow
+    _expect(sp.SP_EINVAL, n_new=np.array([0], np.int32))
+    with pytest.raises(sp.SegPagedError) as e:
+        sp.build_tables(**a, page_size=0, free_list=np.arange(100, dtype=np.int32))
+    assert e.value.status == sp.SP_EINVAL
+
+
+def test_workspace_query_and_validation():
+    rp = np.array([0, 3, 5], np.int32)
+    b = sp.workspace_bytes(sp.SP_WS_DECODE, sp.SP_BF16, 128, 16, 4, 1, 2, None, rp)
+    assert b >= 256 and b % 256 == 0
+    with pytest.raises(sp.SegPagedError) as e:
+        sp.workspace_bytes(sp.SP_WS_DECODE, sp.SP_BF16, 96, 16, 4, 1, 2, None, rp)
+    assert e.value.status == sp.SP_EUNSUPPORTED
+    with pytest.raises(sp.SegPagedError) as e:
+        sp.workspace_bytes(sp.SP_WS_DECODE, sp.SP_BF16, 128, 16, 4, 1, 2, None, np.array([0, 3, 3], np.int32))
+    assert e.value.status == sp.SP_EINVAL
