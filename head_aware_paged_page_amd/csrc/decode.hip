@@ -44,21 +44,19 @@ struct Block {
     int pos[2][4];        // position of each of this lane's 8 keys (kPosInvalid if none)
 };
 
-template <int D>
-__device__ __forceinline__ void load_block(const DecodeParams &P, int e0, int e_hi, Block<D> &B) {
+// Loads one 32-key block whose table entries sit in LDS at sE[e0 - base ..]
+// (already sanitised: out-of-range pages have n_valid 0).
+template <int D, int ps>
+__device__ __forceinline__ void load_block(const DecodeParams &P, const int4 *sE, int e0, int e_hi, Block<D> &B) {
     const int lane = threadIdx.x & 63;
     const int m = lane & 15, grp = lane >> 4;
-    const int ps = P.ps;
     // entries of the block's pages (one or two)
     int4 en[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int e = e0 + i;
-        en[i] = int4{-1, 0, 0, 0};
-        if (i * ps < KB && e < e_hi) {
-            en[i] = P.entries[e];
-            if (en[i].x < 0 || en[i].x >= P.n_phys) en[i].z = 0;
-        }
+        en[i] = int4{0, 0, 0, 0};
+        if (i * ps < KB && e < e_hi) en[i] = sE[i];
     }
     // K: A operand row m of key tile kt is key 8*(m/4) + 4*kt + m%4; dims 32*s + 8*grp
 #pragma unroll
@@ -67,9 +65,12 @@ __device__ __forceinline__ void load_block(const DecodeParams &P, int e0, int e_
         const int pg = j / ps, tk = j % ps;
         const int4 e = pg ? en[1] : en[0];
         const bool ok = tk < e.z;
-        const bf16 *src = P.kp + ((int64_t)e.x * ps + tk) * D + 8 * grp;
+        const bf16 *src = P.kp + ((int64_t)(ok ? e.x : 0) * ps + (ok ? tk : 0)) * D + 8 * grp;
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) B.k[kt][s] = ok ? *(const u32x4 *)(src + 32 * s) : u32x4{0, 0, 0, 0};
+        for (int s = 0; s < D / 32; ++s) {
+            const u32x4 v = *(const u32x4 *)(src + 32 * s);
+            B.k[kt][s] = ok ? v : u32x4{0, 0, 0, 0};
+        }
     }
     // V^T: A operand row = dim 16*dt + m, keys 8*grp .. 8*grp+7
     {
@@ -77,11 +78,12 @@ __device__ __forceinline__ void load_block(const DecodeParams &P, int e0, int e_
         const int pg = j / ps, tk = j % ps;
         const int4 e = pg ? en[1] : en[0];
         const int keep = e.z - tk;
-        const bf16 *src = P.vp + ((int64_t)e.x * D + m) * ps + tk;
+        const bf16 *src = P.vp + ((int64_t)(keep > 0 ? e.x : 0) * D + m) * ps + (keep > 0 ? tk : 0);
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
-            B.v[dt] = keep > 0 ? keep_first_bf16(*(const u32x4 *)(src + (int64_t)16 * dt * ps), keep)
-                               : u32x4{0, 0, 0, 0};
+        for (int dt = 0; dt < D / 16; ++dt) {
+            const u32x4 v = *(const u32x4 *)(src + (int64_t)16 * dt * ps);
+            B.v[dt] = keep >= 8 ? v : (keep > 0 ? keep_first_bf16(v, keep) : u32x4{0, 0, 0, 0});
+        }
     }
     // positions of this lane's score keys: 8*grp + 4*kt + v
 #pragma unroll
@@ -95,12 +97,14 @@ __device__ __forceinline__ void load_block(const DecodeParams &P, int e0, int e_
         }
 }
 
-template <int D>
-__global__ __launch_bounds__(NWD * 64) void decode_bf16_kernel(DecodeParams P) {
+template <int D, int PS>
+__global__ __launch_bounds__(NWD * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_bf16_kernel(
+    DecodeParams P) {
     constexpr int DS = D / 32;   // k-steps of S^T
     constexpr int DT = D / 16;   // dim tiles of O^T
     __shared__ float sM[NWD][16], sL[NWD][16];
     __shared__ float sO[NWD][D][17];
+    __shared__ int4 sE[kDecodeMaxChunk + 2];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, grp = lane >> 4;
@@ -110,22 +114,31 @@ __global__ __launch_bounds__(NWD * 64) void decode_bf16_kernel(DecodeParams P) {
     const int ns = P.nsplit[r];
     const int sp_i = b - P.item_ptr[r];
     const int seq = r % P.n_seq, slot = r / P.n_seq;
-    const int G = P.G, ps = P.ps;
+    const int G = P.G;
+    constexpr int ps = PS;
     const int p = P.q_pos[seq];
     const bool is_local = P.cls[slot] == SP_LOCAL;
     const int low = is_local ? p - P.window[slot] : INT32_MIN;   // visible iff low < pos <= p
 
     const int e_beg = P.row_ptr[r], e_end = P.row_ptr[r + 1];
     const int4 *E = P.entries;
-    const int hi = first_greater(e_beg, e_end, p, [&](int e) { return E[e].y; });
-    int lo = e_beg;
-    if (is_local) lo = first_greater(e_beg, hi, low, [&](int e) { return E[e].y + E[e].z - 1; });
-    const int ppb = KB / ps;                          // pages per 32-key block (page_size 16 or 32)
+    int lo, hi;
+    visible_range(E, e_beg, e_end, p, is_local, low, &lo, &hi);
+    constexpr int ppb = KB / ps;                      // pages per 32-key block (page_size 16 or 32)
     int chunk = (hi - lo + ns - 1) / ns;
     chunk = (chunk + ppb - 1) / ppb * ppb;
     const int my_lo = min(hi, lo + sp_i * chunk);
-    const int my_hi = min(hi, my_lo + chunk);
+    const int my_hi = min(hi, my_lo + min(chunk, kDecodeMaxChunk));
     const int n_blocks = (my_hi - my_lo + ppb - 1) / ppb;
+
+    // this split's table entries -> LDS, sanitised (out-of-range pages hold no token)
+    for (int i = threadIdx.x; i < my_hi - my_lo; i += NWD * 64) {
+        int4 en = E[my_lo + i];
+        if (en.x < 0 || en.x >= P.n_phys) en = int4{0, 0, 0, 0};
+        en.z = min(en.z, ps);
+        sE[i] = en;
+    }
+    __syncthreads();
 
     // Q^T B operand: head n of the slot, dims 32*s + 8*grp
     bf16x8 qf[DS];
@@ -143,9 +156,10 @@ __global__ __launch_bounds__(NWD * 64) void decode_bf16_kernel(DecodeParams P) {
 
     Block<D> cur, nxt;
     int blk = wave;
-    if (blk < n_blocks) load_block<D>(P, my_lo + blk * ppb, my_hi, cur);
+    if (blk < n_blocks) load_block<D, PS>(P, sE + blk * ppb, my_lo + blk * ppb, my_hi, cur);
     for (; blk < n_blocks; blk += NWD) {
-        if (blk + NWD < n_blocks) load_block<D>(P, my_lo + (blk + NWD) * ppb, my_hi, nxt);
+        if (blk + NWD < n_blocks)
+            load_block<D, PS>(P, sE + (blk + NWD) * ppb, my_lo + (blk + NWD) * ppb, my_hi, nxt);
 
         f32x4 S[2];
 #pragma unroll
@@ -169,7 +183,7 @@ __global__ __launch_bounds__(NWD * 64) void decode_bf16_kernel(DecodeParams P) {
         mx = fmaxf(mx, xor_lane(mx, 32));
         const float m_new = fmaxf(m_run, mx);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // exponent <= 0
         float rs = 0.f;
         u32x4 pk;
 #pragma unroll
@@ -177,7 +191,7 @@ __global__ __launch_bounds__(NWD * 64) void decode_bf16_kernel(DecodeParams P) {
             float pv[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                pv[v] = exp2f(S[kt][v] - m_use);
+                pv[v] = __builtin_amdgcn_exp2f(S[kt][v] - m_use);
                 rs += pv[v];
             }
             pk[2 * kt] = pack_bf16x2(pv[0], pv[1]);
@@ -231,28 +245,31 @@ __global__ __launch_bounds__(NWD * 64) void decode_bf16_kernel(DecodeParams P) {
     }
 }
 
+// One thread per (row, head, dim) output of a split row.
 template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams P) {
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams P) {
     const int r = blockIdx.x;
     const int ns = P.nsplit[r];
     if (ns == 1) return;
     const int seq = r % P.n_seq, slot = r / P.n_seq, G = P.G;
+    const int idx = blockIdx.y * 64 + threadIdx.x;
+    if (idx >= G * D) return;
+    const int hh = idx / D, d = idx % D;
     const int64_t part0 = P.part_ptr[r];
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-        const int hh = idx / D, d = idx % D;
-        float M = -INFINITY;
-        for (int s = 0; s < ns; ++s) M = fmaxf(M, P.part_lse[(part0 + s) * G + hh]);
-        float o = 0.f, z = 0.f;
-        if (M != -INFINITY)
-            for (int s = 0; s < ns; ++s) {
-                const float w = __expf(P.part_lse[(part0 + s) * G + hh] - M);
-                o += w * P.part_o[((part0 + s) * G + hh) * D + d];
-                z += w;
-            }
-        const int64_t orow = (int64_t)seq * P.Hq + (int64_t)slot * G + hh;
-        P.out[orow * D + d] = f32_to_bf16(z > 0.f ? o / z : 0.f);
-        if (P.lse && d == 0) P.lse[orow] = z > 0.f ? M + logf(z) : -INFINITY;
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, P.part_lse[(part0 + s) * G + hh]);
+    float o = 0.f, z = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll 4
+        for (int s = 0; s < ns; ++s) {
+            const float w = __expf(P.part_lse[(part0 + s) * G + hh] - M);
+            o += w * P.part_o[((part0 + s) * G + hh) * D + d];
+            z += w;
+        }
     }
+    const int64_t orow = (int64_t)seq * P.Hq + (int64_t)slot * G + hh;
+    P.out[orow * D + d] = f32_to_bf16(z > 0.f ? o / z : 0.f);
+    if (P.lse && d == 0) P.lse[orow] = z > 0.f ? M + logf(z) : -INFINITY;
 }
 
 }  // namespace
@@ -289,13 +306,16 @@ int launch_decode(const AttnArgs &a, const Plan &p, hipStream_t stream) {
     P.Hq = a.n_slot * a.group;
     P.n_phys = a.n_phys;
     P.scale_log2 = a.scale * kLog2e;
-    if (a.head_dim == 128) {
-        hipLaunchKernelGGL(decode_bf16_kernel<128>, dim3((unsigned)p.n_items), dim3(NWD * 64), 0, stream, P);
-        if (p.n_parts) hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(p.n_rows), dim3(256), 0, stream, P);
-    } else {
-        hipLaunchKernelGGL(decode_bf16_kernel<64>, dim3((unsigned)p.n_items), dim3(NWD * 64), 0, stream, P);
-        if (p.n_parts) hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(p.n_rows), dim3(256), 0, stream, P);
+    const dim3 grid((unsigned)p.n_items);
+    const dim3 mgrid(p.n_rows, (a.group * a.head_dim + 63) / 64);
+#define SP_DECODE_CASE(DD, PSV)                                                                     \
+    if (a.head_dim == DD && a.page_size == PSV) {                                                   \
+        hipLaunchKernelGGL((decode_bf16_kernel<DD, PSV>), grid, dim3(NWD * 64), 0, stream, P);     \
+        if (p.n_parts) hipLaunchKernelGGL(decode_merge_kernel<DD>, mgrid, dim3(64), 0, stream, P); \
     }
+    SP_DECODE_CASE(128, 16) else SP_DECODE_CASE(128, 32) else SP_DECODE_CASE(64, 16) else SP_DECODE_CASE(64, 32)
+    else return fail(SP_EUNSUPPORTED, "bf16 decode head_dim %d page_size %d", a.head_dim, a.page_size);
+#undef SP_DECODE_CASE
     return check_hip(hipGetLastError(), "decode launch");
 }
 

@@ -25,9 +25,13 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __ui
 // Round-to-nearest-even fp32 -> bf16 (lowers to v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16 f32_to_bf16(float x) { return (bf16)x; }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    bf16 a = (bf16)lo, b = (bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ __forceinline__ bf16x8 u4_as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -95,6 +99,42 @@ __device__ __forceinline__ int first_greater(int a, int b, int x, Key key) {
         b = min(b, a - 1 + step);
     }
     return a;
+}
+
+// Entry range [lo, hi) of a table row [e_beg, e_end) that a query span sees:
+// hi = first entry whose first position exceeds p_hi; lo = e_beg, or for a
+// local head the first entry whose last position exceeds `bound` (= p_lo - W).
+// Entries are in ascending position, so both are prefix counts.  The common
+// case (everything of interest within the last 64 entries) takes one round of
+// loads; otherwise it falls back to the 64-ary search.
+__device__ __forceinline__ void visible_range(const int4 *__restrict__ E, int e_beg, int e_end, int p_hi,
+                                              bool is_local, int bound, int *lo_out, int *hi_out) {
+    const int lane = threadIdx.x & 63;
+    const int a = max(e_beg, e_end - 64);
+    const int idx = a + lane;
+    const bool valid = idx < e_end;
+    int first = 0, last = 0;
+    if (valid) {
+        const int4 en = E[idx];
+        first = en.y;
+        last = en.y + en.z - 1;
+    }
+    const int first_a = __shfl(first, 0, 64), last_a = __shfl(last, 0, 64);
+    int hi;
+    if (a == e_beg || first_a <= p_hi)
+        hi = a + __popcll(__ballot(valid && first <= p_hi));
+    else
+        hi = first_greater(e_beg, a, p_hi, [&](int e) { return E[e].y; });
+    int lo = e_beg;
+    if (is_local) {
+        if (hi <= a) lo = first_greater(e_beg, hi, bound, [&](int e) { return E[e].y + E[e].z - 1; });
+        else if (a == e_beg || last_a <= bound)
+            lo = min(hi, a + __popcll(__ballot(valid && last <= bound)));
+        else
+            lo = first_greater(e_beg, a + 1, bound, [&](int e) { return E[e].y + E[e].z - 1; });
+    }
+    *lo_out = __builtin_amdgcn_readfirstlane(lo);
+    *hi_out = __builtin_amdgcn_readfirstlane(hi);
 }
 
 }  // namespace sp

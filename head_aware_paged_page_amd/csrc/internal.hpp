@@ -25,9 +25,11 @@ constexpr int kDecodeWaves = 4;
 
 // Split planning targets: enough work items to fill 256 CUs a few times over,
 // while each split still streams at least kMinSplitKeys keys.
-constexpr int kTargetItems = 1024;
+constexpr int kTargetItems = 1024;         // prefill
+constexpr int kTargetDecodeItems = 384;    // decode: about one streaming split per CU
 constexpr int kMinSplitKeys = 512;
 constexpr int kMaxSplits = 1024;
+constexpr int kDecodeMaxChunk = 512;       // pages of one decode split (its entries are staged in LDS)
 
 // Number of kv splits and work items of one row; identical on host and device.
 __host__ __device__ inline void row_items(int n_entries, int n_qtiles, int chunk_pages,

@@ -45,13 +45,26 @@ struct PrefillParams {
     float scale_log2;   // softmax_scale * log2(e)
 };
 
+// Table entries of the (up to four) pages of one 64-key tile, workgroup-uniform.
+// Kept as four named values and selected with compares so that they stay in
+// registers (an array indexed by a lane-varying page would go to scratch).
+struct TileEntries {
+    int4 a, b, c, d;
+    __device__ __forceinline__ int4 pick(int pg) const {
+        const int4 lo = pg == 0 ? a : b;
+        const int4 hi = pg == 2 ? c : d;
+        return pg < 2 ? lo : hi;
+    }
+};
+
 // Output row m of a 32x32 MFMA tile <- K row sigma(m) of the 32-key block.
 // Lane (n, h) holds rows m = (v/4)*8 + 4h + v%4; sigma maps them to keys
 // 16*(v/8) + 8h + v%8, i.e. it swaps bits 2 and 3 of m.
 __device__ __forceinline__ int sigma(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillParams P) {
+template <int D, int NW, int PS>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(
+    PrefillParams P) {
     constexpr int NT = NW * 64;
     constexpr int BM = 32 * NW;
     constexpr int KS = D + 8;      // LDS row stride of K (bf16), padded against bank conflicts
@@ -63,7 +76,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillParams P) 
     __shared__ __attribute__((aligned(16))) bf16 sK[2][BN * KS];
     __shared__ __attribute__((aligned(16))) bf16 sV[2][D * VS];
     __shared__ int sPos[2][BN];
-    __shared__ int sFull[2];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, h = lane >> 5;
@@ -79,7 +91,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillParams P) 
     const int t0 = qt * P.tpt;
     const int ntok = min(P.tpt, P.tok_ptr[seq + 1] - tok_base - t0);
     const int p0 = P.q_pos0[seq] + t0, p_last = p0 + ntok - 1;
-    const int G = P.G, ps = P.ps;
+    const int G = P.G;
+    constexpr int ps = PS;
     const bool is_local = P.cls[slot] == SP_LOCAL;
     const int W = is_local ? P.window[slot] : 0;
     const int nrows = ntok * G;
@@ -87,10 +100,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillParams P) 
     // ---- the q-tile's visible entry range, then this split's share
     const int e_beg = P.row_ptr[r], e_end = P.row_ptr[r + 1];
     const int4 *E = P.entries;
-    const int hi = first_greater(e_beg, e_end, p_last, [&](int e) { return E[e].y; });
-    int lo = e_beg;
-    if (is_local) lo = first_greater(e_beg, hi, p0 - W, [&](int e) { return E[e].y + E[e].z - 1; });
-    const int ppt = BN / ps;                            // pages per tile
+    int lo, hi;
+    visible_range(E, e_beg, e_end, p_last, is_local, p0 - W, &lo, &hi);
+    constexpr int ppt = BN / ps;                        // pages per tile
     int chunk = (hi - lo + ns - 1) / ns;
     chunk = (chunk + ppt - 1) / ppt * ppt;
     const int my_lo = min(hi, lo + sp_i * chunk);
@@ -114,76 +126,92 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillParams P) 
         }
     }
 
-    // ---- tile staging: global -> registers -> LDS
-    u32x4 rk[CPT], rv[CPT];
-    auto load_tile = [&](int t) {
+    // ---- tile staging: the tile's (up to 4) table entries are workgroup-uniform;
+    // data loads take no branch on them (empty slots read page 0 and are zeroed)
+    auto fetch_entries = [&](int t, TileEntries &te) {
         const int e0 = my_lo + t * ppt;
+        auto clean = [&](int4 en) {
+            if (en.x < 0 || en.x >= P.n_phys) en = int4{0, 0, 0, 0};
+            en.z = min(en.z, ps);
+            return en;
+        };
+        if (e0 + ppt <= my_hi) {            // the usual case: one scalar burst
+            te.a = clean(E[e0]);
+            te.b = ppt > 1 ? clean(E[e0 + 1]) : int4{0, 0, 0, 0};
+            te.c = ppt > 2 ? clean(E[e0 + 2]) : int4{0, 0, 0, 0};
+            te.d = ppt > 3 ? clean(E[e0 + 3]) : int4{0, 0, 0, 0};
+        } else {                            // the item's last, partial tile
+            auto get = [&](int pg) { return e0 + pg < my_hi ? clean(E[e0 + pg]) : int4{0, 0, 0, 0}; };
+            te.a = get(0);
+            te.b = get(1);
+            te.c = get(2);
+            te.d = get(3);
+        }
+    };
+    auto tile_full = [&](const TileEntries &te) {
+        // no bounds needed if every slot holds a token visible to every query of the q-tile
+        const int4 x[4] = {te.a, te.b, te.c, te.d};
+        bool full = true;
+        int kmin = INT32_MAX, kmax = INT32_MIN;
+#pragma unroll
+        for (int pg = 0; pg < 4; ++pg)
+            if (pg < ppt) {
+                full = full && x[pg].z == ps;
+                kmin = min(kmin, x[pg].y);
+                kmax = max(kmax, x[pg].y + x[pg].z - 1);
+            }
+        return full && kmax <= p0 && (!is_local || kmin > p_last - W);
+    };
+    // Per-thread chunk geometry, fixed for the whole item.  A page spans
+    // D*ps/8 >= 64 chunks, so the page of each chunk is uniform across a wave:
+    // its base address is computed in scalar registers once per tile and the
+    // lanes only add their constant offsets.
+    static_assert(D * ps / 8 % 64 == 0, "a page must cover whole waves of 16-byte chunks");
+    constexpr int per_page = D * ps / 8;
+    int k_pg[CPT], k_tk[CPT], k_off[CPT], k_lds[CPT], v_pg[CPT], v_k8[CPT], v_off[CPT], v_lds[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = tid + i * NT;
+        const int j = c / (D / 8), col = (c % (D / 8)) * 8;
+        k_pg[i] = __builtin_amdgcn_readfirstlane(c / per_page);
+        k_tk[i] = j % ps;
+        k_off[i] = k_tk[i] * D + col;
+        k_lds[i] = j * KS + col;
+        const int rem = c % per_page;
+        const int d = rem / (ps / 8), k8 = (rem % (ps / 8)) * 8;
+        v_pg[i] = k_pg[i];
+        v_k8[i] = k8;
+        v_off[i] = d * ps + k8;
+        v_lds[i] = d * VS + v_pg[i] * ps + k8;
+    }
+    u32x4 rk[CPT], rv[CPT];
+    auto load_tile = [&](const TileEntries &te) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * NT;
-            rk[i] = u32x4{0, 0, 0, 0};
-            rv[i] = u32x4{0, 0, 0, 0};
-            if (c < KCH) {
-                // K: chunk c -> key row j, 8 dims
-                const int j = c / (D / 8), col = (c % (D / 8)) * 8;
-                const int pg = j / ps, tk = j % ps;
-                const int e = e0 + pg;
-                if (e < my_hi) {
-                    const int4 en = E[e];
-                    if (tk < en.z && en.x >= 0 && en.x < P.n_phys)
-                        rk[i] = *(const u32x4 *)(P.kp + ((int64_t)en.x * ps + tk) * D + col);
-                }
-                // V^T: chunk c -> page-major walk of the dim-major pages
-                const int per_page = D * ps / 8;
-                const int pv = c / per_page, rem = c % per_page;
-                const int d = rem / (ps / 8), k8 = (rem % (ps / 8)) * 8;
-                const int ev = e0 + pv;
-                if (ev < my_hi) {
-                    const int4 en = E[ev];
-                    if (k8 < en.z && en.x >= 0 && en.x < P.n_phys) {
-                        const u32x4 v = *(const u32x4 *)(P.vp + ((int64_t)en.x * D + d) * ps + k8);
-                        rv[i] = keep_first_bf16(v, en.z - k8);
-                    }
-                }
+            if (KCH % NT == 0 || tid + i * NT < KCH) {
+                const int4 en = te.pick(k_pg[i]);   // wave-uniform
+                const bf16 *kb = P.kp + (int64_t)en.x * (ps * D);
+                const bf16 *vb = P.vp + (int64_t)en.x * (ps * D);
+                const u32x4 kv = *(const u32x4 *)(kb + k_off[i]);
+                const u32x4 vv = *(const u32x4 *)(vb + v_off[i]);
+                rk[i] = k_tk[i] < en.z ? kv : u32x4{0, 0, 0, 0};
+                const int keep = en.z - v_k8[i];
+                rv[i] = keep >= 8 ? vv : (keep > 0 ? keep_first_bf16(vv, keep) : u32x4{0, 0, 0, 0});
             }
         }
     };
-    auto store_tile = [&](int t, int buf) {
+    auto store_tile = [&](const TileEntries &te, int buf) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * NT;
-            if (c < KCH) {
-                const int j = c / (D / 8), col = (c % (D / 8)) * 8;
-                *(u32x4 *)&sK[buf][j * KS + col] = rk[i];
-                const int per_page = D * ps / 8;
-                const int pv = c / per_page, rem = c % per_page;
-                const int d = rem / (ps / 8), k8 = (rem % (ps / 8)) * 8;
-                *(u32x4 *)&sV[buf][d * VS + pv * ps + k8] = rv[i];
+            if (KCH % NT == 0 || tid + i * NT < KCH) {
+                *(u32x4 *)&sK[buf][k_lds[i]] = rk[i];
+                *(u32x4 *)&sV[buf][v_lds[i]] = rv[i];
             }
         }
         if (tid < BN) {
-            const int e0 = my_lo + t * ppt;
-            const int pg = tid / ps, tk = tid % ps, e = e0 + pg;
-            int pos = kPosInvalid;
-            if (e < my_hi) {
-                const int4 en = E[e];
-                if (tk < en.z && en.x >= 0 && en.x < P.n_phys) pos = en.y + tk;
-            }
-            sPos[buf][tid] = pos;
-        }
-        if (tid == 0) {
-            // the tile needs no bounds if every slot holds a token visible to every query of the q-tile
-            const int e0 = my_lo + t * ppt;
-            bool full = e0 + ppt <= my_hi;
-            int kmin = INT32_MAX, kmax = INT32_MIN;
-            for (int pg = 0; full && pg < ppt; ++pg) {
-                const int4 en = E[e0 + pg];
-                full = en.z == ps && en.x >= 0 && en.x < P.n_phys;
-                kmin = min(kmin, en.y);
-                kmax = max(kmax, en.y + en.z - 1);
-            }
-            full = full && kmax <= p0 && (!is_local || kmin > p_last - W);
-            sFull[buf] = full;
+            const int pg = tid / ps, tk = tid % ps;
+            const int4 en = te.pick(pg);
+            sPos[buf][tid] = tk < en.z ? en.y + tk : kPosInvalid;
         }
     };
 
@@ -193,14 +221,22 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillParams P) 
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{0};
 
+    TileEntries te_cur, te_nxt;
+    bool full_cur = false, full_nxt = false;
     if (n_tiles > 0) {
-        load_tile(0);
-        store_tile(0, 0);
+        fetch_entries(0, te_cur);
+        full_cur = tile_full(te_cur);
+        load_tile(te_cur);
+        store_tile(te_cur, 0);
     }
     __syncthreads();
     for (int t = 0; t < n_tiles; ++t) {
         const int buf = t & 1;
-        if (t + 1 < n_tiles) load_tile(t + 1);
+        if (t + 1 < n_tiles) {
+            fetch_entries(t + 1, te_nxt);
+            full_nxt = tile_full(te_nxt);
+            load_tile(te_nxt);
+        }
 
         // S^T = K Q^T over the two 32-key halves of the tile
         f32x16 S[BN / 32];
@@ -214,39 +250,44 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillParams P) 
                 S[kt] = mfma32x32x16(a, qf[s], S[kt]);
             }
         }
-        // scale, bounds (boundary tiles only), online softmax
-        const bool full = sFull[buf];
+        // bounds (boundary tiles only) and online softmax; the running max is kept
+        // on raw scores (the scale is positive) and folded into one FMA per exp
+        if (!full_cur) {
+#pragma unroll
+            for (int kt = 0; kt < BN / 32; ++kt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int kpos = sPos[buf][32 * kt + 16 * (v >> 3) + 8 * h + (v & 7)];
+                    S[kt][v] = (kpos <= pq && kpos > lowq) ? S[kt][v] : -INFINITY;
+                }
+        }
         float mx = -INFINITY;
 #pragma unroll
-        for (int kt = 0; kt < BN / 32; ++kt) {
+        for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                float x = S[kt][v] * P.scale_log2;
-                if (!full) {
-                    const int kpos = sPos[buf][32 * kt + 16 * (v >> 3) + 8 * h + (v & 7)];
-                    if (!(kpos <= pq && kpos > lowq)) x = -INFINITY;
-                }
-                S[kt][v] = x;
-                mx = fmaxf(mx, x);
-            }
-        }
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[kt][v]);
         mx = fmaxf(mx, xor_lane(mx, 32));
         const float m_new = fmaxf(m_run, mx);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        const float c = P.scale_log2;
+        // exponents are <= 0 here; v_exp_f32 flushes results below 2^-126 to zero, which is harmless
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c);
+        const float off = -m_use * c;
         float rs = 0.f;
 #pragma unroll
         for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const float p = exp2f(S[kt][v] - m_use);
+                const float p = __builtin_amdgcn_exp2f(fmaf(S[kt][v], c, off));
                 S[kt][v] = p;
                 rs += p;
             }
         l_run = l_run * alpha + rs;
         m_run = m_new;
+        if (__any(alpha != 1.f)) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+            for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+        }
 
         // O^T += V^T P^T, 16 keys per step
 #pragma unroll
@@ -263,14 +304,17 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillParams P) 
             }
         }
 
-        if (t + 1 < n_tiles) store_tile(t + 1, buf ^ 1);
+        if (t + 1 < n_tiles) {
+            store_tile(te_nxt, buf ^ 1);
+            full_cur = full_nxt;
+        }
         __syncthreads();
     }
 
     // ---- epilogue
     const float l = l_run + xor_lane(l_run, 32);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    const float lse = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+    const float lse = l > 0.f ? (m_run * P.scale_log2 + log2f(l)) * kLn2 : -INFINITY;
     if (!row_ok) return;
     if (ns == 1) {
         bf16 *orow = P.out + ((int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g) * D;
@@ -301,43 +345,71 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillParams P) 
 }
 
 // Combines the kv splits of every split q-tile: O = sum_s e^{lse_s-M} o_s / sum_s e^{lse_s-M}.
+// Launched over the same work items: item (q-tile, split s) merges rows
+// [s * ceil(rows/ns), (s+1) * ceil(rows/ns)) of its q-tile, so all splits share
+// the work.  One wave per row: the split weights are formed once per row (in
+// LDS), then each lane accumulates its dims over the splits.
 template <int D>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, int BM) {
+    __shared__ float sw[4][kMaxSplits];
     const int b = blockIdx.x;
     const int r = find_row(P.item_ptr, P.n_rows, b);
     const int ns = P.nsplit[r];
+    if (ns == 1) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int local = b - P.item_ptr[r];
-    if (ns == 1 || local % ns != 0) return;
-    const int qt = local / ns;
+    const int qt = local / ns, sp_i = local % ns;
     const int seq = r % P.n_seq, slot = r / P.n_seq;
     const int tok_base = P.tok_ptr[seq];
     const int t0 = qt * P.tpt;
     const int ntok = min(P.tpt, P.tok_ptr[seq + 1] - tok_base - t0);
     const int nrows = ntok * P.G;
-    const int64_t part0 = (int64_t)P.part_ptr[r] + local;   // splits are part0 .. part0+ns-1
-    constexpr int TPR = D / 4;                               // threads per row (4 dims each)
-    for (int idx = threadIdx.x; idx < nrows * TPR; idx += 256) {
-        const int row = idx / TPR, d = (idx % TPR) * 4;
+    const int per = (nrows + ns - 1) / ns;
+    const int r0 = sp_i * per, r1 = min(nrows, r0 + per);
+    const int64_t part0 = (int64_t)P.part_ptr[r] + (int64_t)qt * ns;   // splits part0 .. part0+ns-1
+    constexpr int DPL = D / 64;                                      // dims per lane
+    for (int row = r0 + wave; row < r1; row += 4) {
         float M = -INFINITY;
-        for (int s = 0; s < ns; ++s) M = fmaxf(M, P.part_lse[(part0 + s) * BM + row]);
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s = lane; s < ns; s += 64) M = fmaxf(M, P.part_lse[(part0 + s) * BM + row]);
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
         float z = 0.f;
-        if (M != -INFINITY) {
-            for (int s = 0; s < ns; ++s) {
-                const float wgt = __expf(P.part_lse[(part0 + s) * BM + row] - M);
-                const float4 v = *(const float4 *)(P.part_o + ((part0 + s) * BM + row) * D + d);
-                o.x += wgt * v.x; o.y += wgt * v.y; o.z += wgt * v.z; o.w += wgt * v.w;
-                z += wgt;
+        for (int s = lane; s < ns; s += 64) {
+            const float l = P.part_lse[(part0 + s) * BM + row];
+            const float wgt = M == -INFINITY ? 0.f : __expf(l - M);
+            sw[wave][s] = wgt;
+            z += wgt;
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) z += __shfl_xor(z, m, 64);
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        float o[DPL];
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) o[i] = 0.f;
+        const float *src = P.part_o + (part0 * BM + row) * D + DPL * lane;
+#pragma unroll 8
+        for (int s = 0; s < ns; ++s) {
+            const float wgt = sw[wave][s];
+            const float *q = src + (int64_t)s * BM * D;
+            if (DPL == 2) {
+                const float2 v = *(const float2 *)q;
+                o[0] += wgt * v.x;
+                o[DPL - 1] += wgt * v.y;
+            } else {
+                o[0] += wgt * q[0];
             }
         }
         const float inv = z > 0.f ? 1.f / z : 0.f;
         const int tq = row / P.G, g = row % P.G;
         const int64_t orow = (int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * P.G + g;
-        u32x2 w;
-        w[0] = pack_bf16x2(o.x * inv, o.y * inv);
-        w[1] = pack_bf16x2(o.z * inv, o.w * inv);
-        *(u32x2 *)(P.out + orow * D + d) = w;
-        if (P.lse && d == 0) P.lse[orow] = z > 0.f ? M + logf(z) : -INFINITY;
+        if (DPL == 2) {
+            *(uint32_t *)(P.out + orow * D + 2 * lane) = pack_bf16x2(o[0] * inv, o[DPL - 1] * inv);
+        } else {
+            P.out[orow * D + lane] = f32_to_bf16(o[0] * inv);
+        }
+        if (P.lse && lane == 0) P.lse[orow] = z > 0.f ? M + logf(z) : -INFINITY;
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -431,13 +503,19 @@ int launch_prefill(const AttnArgs &a, const Plan &p, int64_t n_tok, hipStream_t 
     P.n_phys = a.n_phys;
     P.scale_log2 = a.scale * kLog2e;
     const dim3 grid((unsigned)p.n_items);
-    if (a.head_dim == 128) {
-        hipLaunchKernelGGL((prefill_bf16_kernel<128, 4>), grid, dim3(256), 0, stream, P);
-        if (p.n_parts) hipLaunchKernelGGL(prefill_merge_kernel<128>, grid, dim3(256), 0, stream, P, p.rows_per_tile);
-    } else {
-        hipLaunchKernelGGL((prefill_bf16_kernel<64, 4>), grid, dim3(256), 0, stream, P);
-        if (p.n_parts) hipLaunchKernelGGL(prefill_merge_kernel<64>, grid, dim3(256), 0, stream, P, p.rows_per_tile);
+#define SP_PREFILL_CASE(DD, PSV)                                                                        \
+    if (a.head_dim == DD && a.page_size == PSV) {                                                       \
+        if (p.waves == 8)                                                                               \
+            hipLaunchKernelGGL((prefill_bf16_kernel<DD, 8, PSV>), grid, dim3(512), 0, stream, P);      \
+        else                                                                                            \
+            hipLaunchKernelGGL((prefill_bf16_kernel<DD, 4, PSV>), grid, dim3(256), 0, stream, P);      \
+        if (p.n_parts)                                                                                  \
+            hipLaunchKernelGGL(prefill_merge_kernel<DD>, grid, dim3(256), 0, stream, P, p.rows_per_tile); \
     }
+    SP_PREFILL_CASE(128, 16) else SP_PREFILL_CASE(128, 32) else SP_PREFILL_CASE(128, 64)
+    else SP_PREFILL_CASE(64, 16) else SP_PREFILL_CASE(64, 32) else SP_PREFILL_CASE(64, 64)
+    else return fail(SP_EUNSUPPORTED, "bf16 prefill head_dim %d page_size %d", a.head_dim, a.page_size);
+#undef SP_PREFILL_CASE
     return check_hip(hipGetLastError(), "prefill launch");
 }
 

@@ -8,29 +8,33 @@
 // delta * w_i.  The angle is formed and reduced modulo 2*pi in fp64, its
 // sine/cosine taken in fp64 and the rotation applied in fp32.
 //
-// HBM-bound streaming: each thread owns 8 consecutive pairs of one key row
-// (16 B + 16 B for bf16), its 8 frequencies are fixed for the whole launch, and
-// the 8 (cos, sin) are recomputed only when the page's shift changes - the
-// workgroup walks a contiguous run of list entries, so that happens at segment
-// boundaries only.
+// HBM-bound streaming: a workgroup takes a run of 16 list items (staged in
+// LDS) and builds their (cos, sin) table in LDS once - D/2 angles per page,
+// while its first loads are in flight - then every thread rotates units of 8
+// consecutive pairs of one key row (16 B + 16 B for bf16), four units with
+// their loads in flight together.
 #include "device_common.hpp"
 
 namespace sp {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPagesPerBlock = 8;
+constexpr int kPagesPerBlock = 16;
+constexpr int kBatch = 4;             // units per thread with loads in flight together
+constexpr int kMaxHalf = 128;         // head_dim / 2
 constexpr double kTwoPiHi = 6.283185307179586232;      // 2*pi rounded to fp64
 constexpr double kTwoPiLo = 2.4492935982947064e-16;    // 2*pi - kTwoPiHi
 
+// 8 consecutive elements of a key row: raw load/store and widening to fp32.
 template <typename T>
 struct Elem;
 template <>
 struct Elem<float> {
-    typedef float4 V8[2];   // 8 fp32
-    __device__ static void load(const float *p, float *x) {
-        const float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    struct Raw { float4 lo, hi; };
+    __device__ static Raw load(const float *p) { return Raw{*(const float4 *)p, *(const float4 *)(p + 4)}; }
+    __device__ static void widen(const Raw &r, float *x) {
+        x[0] = r.lo.x; x[1] = r.lo.y; x[2] = r.lo.z; x[3] = r.lo.w;
+        x[4] = r.hi.x; x[5] = r.hi.y; x[6] = r.hi.z; x[7] = r.hi.w;
     }
     __device__ static void store(float *p, const float *x) {
         *(float4 *)p = make_float4(x[0], x[1], x[2], x[3]);
@@ -39,8 +43,9 @@ struct Elem<float> {
 };
 template <>
 struct Elem<bf16> {
-    __device__ static void load(const bf16 *p, float *x) {
-        const u32x4 v = *(const u32x4 *)p;
+    typedef u32x4 Raw;
+    __device__ static Raw load(const bf16 *p) { return *(const u32x4 *)p; }
+    __device__ static void widen(const Raw &v, float *x) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             x[2 * w] = bf16_bits_to_f32(v[w] & 0xffffu);
@@ -55,58 +60,90 @@ struct Elem<bf16> {
     }
 };
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void relocate_kernel(const T *__restrict__ k_in, T *k_out, int ps, int D,
-                                                            int64_t n_phys, int n, const int4 *__restrict__ list,
-                                                            double log2_theta) {
+// PS / DD = 0: page size / head dim taken from the arguments (any legal value);
+// otherwise compile-time, so the index arithmetic is shifts and masks.
+template <typename T, int PS, int DD>
+__global__ __launch_bounds__(kThreads) void relocate_kernel(const T *__restrict__ k_in, T *k_out, int ps_arg,
+                                                            int D_arg, int64_t n_phys, int n,
+                                                            const int4 *__restrict__ list, double log2_theta) {
+    const int ps = PS ? PS : ps_arg;
+    const int D = DD ? DD : D_arg;
+    __shared__ int4 sL[kPagesPerBlock];
+    __shared__ float2 sCS[kPagesPerBlock][kMaxHalf];   // (cos, sin) of delta * w_i per page
     const int units_per_row = D / 16;            // a unit = 8 pairs of one key row
     const int ig = threadIdx.x % units_per_row;  // fixed for the launch (kThreads % units_per_row == 0)
     const int units_per_page = ps * units_per_row;
     const int half = D / 2;
 
-    // this thread's 8 frequencies w_i = theta^(-2i/D), i = 8*ig .. 8*ig+7
-    double w[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) w[j] = exp2(-(2.0 * (8 * ig + j) / D) * log2_theta);
-
-    float c[8], s[8];
-    int cached = 0;
-    bool have = false;
-
+    // this workgroup's run of list items, sanitised (a page outside the pool holds no token)
     const int64_t first = (int64_t)blockIdx.x * kPagesPerBlock;
     const int pages = (int)min<int64_t>(kPagesPerBlock, n - first);
+    if (threadIdx.x < pages) {
+        int4 e = list[first + threadIdx.x];   // {phys, delta, n_valid, reserved}
+        if (e.x < 0 || e.x >= n_phys) e.z = 0;
+        e.z = min(e.z, ps);
+        sL[threadIdx.x] = e;
+    }
+    __syncthreads();
+
     const int total = pages * units_per_page;
-    for (int u = threadIdx.x; u < total; u += kThreads) {
-        const int pl = u / units_per_page;
-        const int row = (u % units_per_page) / units_per_row;
-        const int4 e = list[first + pl];   // {phys, delta, n_valid, reserved}
-        if (row >= min(e.z, ps) || e.x < 0 || e.x >= n_phys) continue;
-        if (!have || e.y != cached) {
+    typename Elem<T>::Raw ra[kBatch], rb[kBatch];
+    int64_t base[kBatch];
+    int pl[kBatch];
+    bool ok[kBatch];
+    auto issue = [&](int u0) {
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int u = u0 + k * kThreads;
+            ok[k] = false;
+            base[k] = 0;
+            pl[k] = 0;
+            if (u < total) {
+                pl[k] = u / units_per_page;
+                const int4 e = sL[pl[k]];
+                const int row = (u % units_per_page) / units_per_row;
+                ok[k] = row < e.z;
+                base[k] = ((int64_t)e.x * ps + row) * D + 8 * ig;
+            }
+            if (ok[k]) {
+                ra[k] = Elem<T>::load(k_in + base[k]);
+                rb[k] = Elem<T>::load(k_in + base[k] + half);
+            }
+        }
+    };
+    issue(threadIdx.x);   // the first loads fly while the angle table is built
+
+    // (cos, sin) of delta * w_i, w_i = theta^(-2i/D): angle formed and reduced mod 2*pi in fp64
+    for (int idx = threadIdx.x; idx < pages * half; idx += kThreads) {
+        const int pg = idx / half, i = idx % half;
+        const double w = exp2(-(2.0 * i / D) * log2_theta);
+        const double ang = (double)sL[pg].y * w;
+        const double q = rint(ang * (1.0 / kTwoPiHi));
+        const double r = fma(-q, kTwoPiLo, fma(-q, kTwoPiHi, ang));   // |r| <~ pi
+        double sd, cd;
+        sincos(r, &sd, &cd);
+        sCS[pg][i] = make_float2((float)cd, (float)sd);
+    }
+    __syncthreads();
+
+    for (int u0 = threadIdx.x; u0 < total; u0 += kThreads * kBatch) {
+        if (u0 != (int)threadIdx.x) issue(u0);
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            if (!ok[k]) continue;
+            const float2 *cs = &sCS[pl[k]][8 * ig];
+            float a[8], b[8], ya[8], yb[8];
+            Elem<T>::widen(ra[k], a);
+            Elem<T>::widen(rb[k], b);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const double a = (double)e.y * w[j];
-                const double q = rint(a * (1.0 / kTwoPiHi));
-                const double r = fma(-q, kTwoPiLo, fma(-q, kTwoPiHi, a));   // a mod 2*pi, |r| <~ pi
-                double sd, cd;
-                sincos(r, &sd, &cd);
-                c[j] = (float)cd;
-                s[j] = (float)sd;
+                const float2 t = cs[j];
+                ya[j] = fmaf(a[j], t.x, -(b[j] * t.y));
+                yb[j] = fmaf(b[j], t.x, a[j] * t.y);
             }
-            cached = e.y;
-            have = true;
+            Elem<T>::store(k_out + base[k], ya);
+            Elem<T>::store(k_out + base[k] + half, yb);
         }
-        const int64_t base = ((int64_t)e.x * ps + row) * D + 8 * ig;
-        float a[8], b[8];
-        Elem<T>::load(k_in + base, a);
-        Elem<T>::load(k_in + base + half, b);
-        float ya[8], yb[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            ya[j] = fmaf(a[j], c[j], -(b[j] * s[j]));
-            yb[j] = fmaf(b[j], c[j], a[j] * s[j]);
-        }
-        Elem<T>::store(k_out + base, ya);
-        Elem<T>::store(k_out + base + half, yb);
     }
 }
 
@@ -119,14 +156,24 @@ int launch_relocate(const void *k_in, void *k_out, int dtype, int page_size, int
     const int64_t blocks = (n + kPagesPerBlock - 1) / kPagesPerBlock;
     if (blocks > INT32_MAX) return fail(SP_EINVAL, "relocation list too long");
     const double l2t = log2(theta);
-    if (dtype == SP_F32)
-        hipLaunchKernelGGL(relocate_kernel<float>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                           (const float *)k_in, (float *)k_out, page_size, head_dim, n_phys, n,
-                           (const int4 *)d_list, l2t);
-    else
-        hipLaunchKernelGGL(relocate_kernel<bf16>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                           (const bf16 *)k_in, (bf16 *)k_out, page_size, head_dim, n_phys, n,
-                           (const int4 *)d_list, l2t);
+    const dim3 grid((unsigned)blocks), block(kThreads);
+#define SP_RELOC(T, PSV, DV)                                                                                \
+    hipLaunchKernelGGL((relocate_kernel<T, PSV, DV>), grid, block, 0, stream, (const T *)k_in, (T *)k_out, \
+                       page_size, head_dim, n_phys, n, (const int4 *)d_list, l2t)
+#define SP_RELOC_SHAPES(T)                                                                   \
+    if (head_dim == 128 && page_size == 16) SP_RELOC(T, 16, 128);                           \
+    else if (head_dim == 128 && page_size == 32) SP_RELOC(T, 32, 128);                      \
+    else if (head_dim == 128 && page_size == 64) SP_RELOC(T, 64, 128);                      \
+    else if (head_dim == 64 && page_size == 16) SP_RELOC(T, 16, 64);                        \
+    else if (head_dim == 64 && page_size == 32) SP_RELOC(T, 32, 64);                        \
+    else SP_RELOC(T, 0, 0);
+    if (dtype == SP_F32) {
+        SP_RELOC_SHAPES(float)
+    } else {
+        SP_RELOC_SHAPES(bf16)
+    }
+#undef SP_RELOC_SHAPES
+#undef SP_RELOC
     return check_hip(hipGetLastError(), "rope_relocate launch");
 }
 

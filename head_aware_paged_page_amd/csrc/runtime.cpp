@@ -76,7 +76,11 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
     // work units (row, q-tile) and their page counts
     int64_t units = 0, work = 0;
     if (kind == SP_WS_PREFILL) {
-        p.waves = 4;
+        // 8 waves (256 query rows) when a sequence brings that many rows, so one
+        // staged K/V tile feeds twice the queries; 4 waves otherwise
+        int max_tok = 0;
+        for (int q = 0; q < n_seq; ++q) max_tok = std::max(max_tok, h_tok_ptr[q + 1] - h_tok_ptr[q]);
+        p.waves = (int64_t)max_tok * group >= 2 * kPrefillRowsPerWave * 4 ? 8 : 4;
         p.rows_per_tile = kPrefillRowsPerWave * p.waves;
         p.tok_per_tile = p.rows_per_tile / group;
         for (int r = 0; r < n_rows; ++r) {
@@ -95,12 +99,14 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
         }
     }
     const int min_chunk = std::max(1, kMinSplitKeys / page_size);
-    if (units >= kTargetItems / 2) {
+    const int target = kind == SP_WS_PREFILL ? kTargetItems : kTargetDecodeItems;
+    if (kind == SP_WS_PREFILL && units >= target / 2) {
         p.chunk_pages = INT_MAX;
     } else {
-        const int64_t c = (work + kTargetItems - 1) / kTargetItems;
+        const int64_t c = (work + target - 1) / target;
         p.chunk_pages = (int)std::min<int64_t>(INT_MAX, std::max<int64_t>(min_chunk, c));
     }
+    if (kind == SP_WS_DECODE) p.chunk_pages = std::min(p.chunk_pages, kDecodeMaxChunk);
     int64_t items = 0, parts = 0;
     for (int r = 0; r < n_rows; ++r) {
         int nq = 1;
@@ -110,7 +116,11 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
             nq = (nt + p.tok_per_tile - 1) / p.tok_per_tile;
         }
         int ns, it;
-        row_items(h_row_ptr[r + 1] - h_row_ptr[r], nq, p.chunk_pages, &ns, &it);
+        const int64_t e_row = h_row_ptr[r + 1] - h_row_ptr[r];
+        if (kind == SP_WS_DECODE && e_row > (int64_t)kMaxSplits * p.chunk_pages)
+            return fail(SP_EUNSUPPORTED, "row %d: %lld table entries exceed one decode call's split capacity", r,
+                        (long long)e_row);
+        row_items((int)e_row, nq, p.chunk_pages, &ns, &it);
         items += it;
         if (ns > 1) parts += it;
     }

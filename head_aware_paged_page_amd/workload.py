@@ -19,7 +19,8 @@ from .kvpool import chain_token_index, place
 
 
 class Workload:
-    def __init__(self, lay, device="cuda", fill_nan: bool = True, pool_slack: int = 0, relocated_pool: bool = True):
+    def __init__(self, lay, device="cuda", fill_nan: bool = True, pool_slack: int = 0, relocated_pool: bool = True,
+                 free=None):
         import torch
         self.lay = lay
         self.device = device
@@ -33,8 +34,12 @@ class Workload:
         arr_p = lay.abi_arrays("prefill")
         arr_d = lay.abi_arrays("decode")
         cnt = sp.build_tables(**arr_p, page_size=ps, free_list=None, counts_only=True)["counts"]
-        self.n_phys = int(cnt[0]) + pool_slack
-        self.free = synth.free_list(lay, self.n_phys)
+        if free is None:
+            self.n_phys = int(cnt[0]) + pool_slack
+            self.free = synth.free_list(lay, self.n_phys)
+        else:
+            self.free = np.ascontiguousarray(free, dtype=np.int32)
+            self.n_phys = int(self.free.max()) + 1
         t0 = time.perf_counter()
         self.tp = sp.build_tables(**arr_p, page_size=ps, free_list=self.free)
         t1 = time.perf_counter()
