@@ -58,31 +58,33 @@ __device__ __forceinline__ void load_block(const DecodeParams &P, const int4 *sE
         en[i] = int4{0, 0, 0, 0};
         if (i * ps < KB && e < e_hi) en[i] = sE[i];
     }
-    // K: A operand row m of key tile kt is key 8*(m/4) + 4*kt + m%4; dims 32*s + 8*grp
+    // K: A operand row m of key tile kt is key 8*(m/4) + 4*kt + m%4; dims 32*s + 8*grp.
+    // Slots without a token are read from page 0 and never zeroed: their scores
+    // are replaced by -inf before use, so whatever they hold cannot leak.
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
         const int j = 8 * (m >> 2) + 4 * kt + (m & 3);
         const int pg = j / ps, tk = j % ps;
         const int4 e = pg ? en[1] : en[0];
-        const bool ok = tk < e.z;
-        const bf16 *src = P.kp + ((int64_t)(ok ? e.x : 0) * ps + (ok ? tk : 0)) * D + 8 * grp;
+        const bf16 *src = P.kp + ((int64_t)e.x * ps + tk) * D + 8 * grp;
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-            const u32x4 v = *(const u32x4 *)(src + 32 * s);
-            B.k[kt][s] = ok ? v : u32x4{0, 0, 0, 0};
-        }
+        for (int s = 0; s < D / 32; ++s) B.k[kt][s] = *(const u32x4 *)(src + 32 * s);
     }
-    // V^T: A operand row = dim 16*dt + m, keys 8*grp .. 8*grp+7
+    // V^T: A operand row = dim 16*dt + m, keys 8*grp .. 8*grp+7.  Values of empty
+    // slots must be zero (their weight is zero, but 0 * NaN is not); only blocks
+    // that contain such slots pay for the masking.
     {
         const int j = 8 * grp;
         const int pg = j / ps, tk = j % ps;
         const int4 e = pg ? en[1] : en[0];
         const int keep = e.z - tk;
-        const bf16 *src = P.vp + ((int64_t)(keep > 0 ? e.x : 0) * D + m) * ps + (keep > 0 ? tk : 0);
+        const bf16 *src = P.vp + ((int64_t)e.x * D + m) * ps + tk;
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-            const u32x4 v = *(const u32x4 *)(src + (int64_t)16 * dt * ps);
-            B.v[dt] = keep >= 8 ? v : (keep > 0 ? keep_first_bf16(v, keep) : u32x4{0, 0, 0, 0});
+        for (int dt = 0; dt < D / 16; ++dt) B.v[dt] = *(const u32x4 *)(src + (int64_t)16 * dt * ps);
+        if (__any(keep < 8)) {
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+                B.v[dt] = keep >= 8 ? B.v[dt] : (keep > 0 ? keep_first_bf16(B.v[dt], keep) : u32x4{0, 0, 0, 0});
         }
     }
     // positions of this lane's score keys: 8*grp + 4*kt + v

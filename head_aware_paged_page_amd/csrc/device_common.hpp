@@ -137,4 +137,39 @@ __device__ __forceinline__ void visible_range(const int4 *__restrict__ E, int e_
     *hi_out = __builtin_amdgcn_readfirstlane(hi);
 }
 
+// One 16-byte global->LDS load per lane (gfx950 global_load_lds_dwordx4): lane l
+// of the wave writes LDS bytes [dst + 16 l, dst + 16 l + 16); dst must be
+// wave-uniform.  The builtin exists only for the device target, so the host
+// pass (which must still emit the kernel's launch stub) sees a no-op.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define SP_LDS_DMA16(src, dst) __builtin_amdgcn_global_load_lds((src), (dst), 16, 0, 0)
+#else
+#define SP_LDS_DMA16(src, dst) ((void)(src), (void)(dst))
+#endif
+
+// Scalar (constant-cache) loads of workgroup-uniform table entries.  Kernels
+// that stream tiles with global->LDS loads keep every other vector load out of
+// their main loop (one in-order counter tracks both), so the page entries go
+// through the scalar path; each block waits for its own result.
+__device__ __forceinline__ int4 sload_int4(const int4 *p) {
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    v4i r = {0, 0, 0, 0};
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass must not see amdgcn register constraints
+    asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
+#endif
+    return int4{r.x, r.y, r.z, r.w};
+}
+
+__device__ __forceinline__ void sload_int4x4(const int4 *p, int4 &a, int4 &b, int4 &c, int4 &d) {
+    typedef int v16i __attribute__((ext_vector_type(16)));
+    v16i r = {0};
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_load_dwordx16 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
+#endif
+    a = int4{r[0], r[1], r[2], r[3]};
+    b = int4{r[4], r[5], r[6], r[7]};
+    c = int4{r[8], r[9], r[10], r[11]};
+    d = int4{r[12], r[13], r[14], r[15]};
+}
+
 }  // namespace sp

@@ -52,7 +52,7 @@ struct Plan {
     int chunk_pages = 0;     // pages per kv split (INT32_MAX = no split)
     int64_t n_items = 0;     // work items (= workgroups of the attention kernel)
     int64_t n_parts = 0;     // work items whose result is a partial to merge
-    size_t off_item_ptr = 0, off_part_ptr = 0, off_nsplit = 0, off_part_o = 0, off_part_lse = 0;
+    size_t off_item_ptr = 0, off_part_ptr = 0, off_nsplit = 0, off_zero = 0, off_part_o = 0, off_part_lse = 0;
     size_t bytes = 0;        // workspace bytes
 };
 

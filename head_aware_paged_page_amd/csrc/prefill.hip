@@ -43,6 +43,7 @@ struct PrefillParams {
     int n_seq, n_rows, G, ps, tpt, Hq;
     int64_t n_phys;
     float scale_log2;   // softmax_scale * log2(e)
+    const bf16 *zero16;  // 16 zero bytes in the workspace (source for empty V slots)
 };
 
 // Table entries of the (up to four) pages of one 64-key tile, workgroup-uniform.
@@ -62,23 +63,49 @@ struct TileEntries {
 // 16*(v/8) + 8h + v%8, i.e. it swaps bits 2 and 3 of m.
 __device__ __forceinline__ int sigma(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-template <int D, int NW, int PS>
+// s_waitcnt immediate that waits until at most n vector-memory loads are
+// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14, the other counters
+// left at their "no wait" maximum).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding global->LDS load); callers wait explicitly.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
+    asm volatile("s_barrier" ::: "memory");
+}
+
+template <int D, int NW, int PS, int NBUF>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(
     PrefillParams P) {
-    constexpr int NT = NW * 64;
     constexpr int BM = 32 * NW;
-    constexpr int KS = D + 8;      // LDS row stride of K (bf16), padded against bank conflicts
-    constexpr int VS = BN + 8;     // LDS row stride of V^T
     constexpr int DK = D / 16;     // k-steps of the QK^T product
     constexpr int DT = D / 32;     // 32-dim tiles of the output
-    constexpr int KCH = BN * D / 8;                 // 16-byte chunks per K (or V) tile
-    constexpr int CPT = (KCH + NT - 1) / NT;        // chunks per thread
-    __shared__ __attribute__((aligned(16))) bf16 sK[2][BN * KS];
-    __shared__ __attribute__((aligned(16))) bf16 sV[2][D * VS];
-    __shared__ int sPos[2][BN];
+    // Tiles arrive by global->LDS loads of 1 KB per wave instruction (lane l
+    // writes bytes [16 l, 16 l + 16)).  K rows (2D bytes) and V^T rows (2*BN
+    // bytes) are stored with their 16-byte chunks XOR-swizzled by row so that
+    // the MFMA operand reads of 32 rows spread over all LDS banks.
+    constexpr int KI = BN * D * 2 / 1024, VI = D * BN * 2 / 1024;   // 1 KB blocks per tile
+    static_assert(KI % NW == 0 && VI % NW == 0, "tile blocks must split evenly over the waves");
+    constexpr int KIW = KI / NW, VIW = VI / NW;                       // per wave and tile
+    constexpr int IPW = KIW + VIW;
+    constexpr int ppt = BN / PS;                                      // pages per tile
+    static_assert(1024 / (2 * D) <= PS, "a 1 KB block of K rows must stay inside one page");
+    __shared__ __attribute__((aligned(1024))) bf16 sK[NBUF][BN * D];
+    __shared__ __attribute__((aligned(1024))) bf16 sV[NBUF][D * BN];
+    __shared__ int sPos[NBUF][BN];
+    __shared__ __attribute__((aligned(16))) int4 sEnt[2][64];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, h = lane >> 5;
+    auto swz_k = [](int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
+    auto swz_v = [](int d) { return (d >> 1) & 7; };
 
     // ---- work item
     const int b = blockIdx.x;
@@ -92,7 +119,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int ntok = min(P.tpt, P.tok_ptr[seq + 1] - tok_base - t0);
     const int p0 = P.q_pos0[seq] + t0, p_last = p0 + ntok - 1;
     const int G = P.G;
-    constexpr int ps = PS;
     const bool is_local = P.cls[slot] == SP_LOCAL;
     const int W = is_local ? P.window[slot] : 0;
     const int nrows = ntok * G;
@@ -102,7 +128,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int4 *E = P.entries;
     int lo, hi;
     visible_range(E, e_beg, e_end, p_last, is_local, p0 - W, &lo, &hi);
-    constexpr int ppt = BN / ps;                        // pages per tile
     int chunk = (hi - lo + ns - 1) / ns;
     chunk = (chunk + ppt - 1) / ppt * ppt;
     const int my_lo = min(hi, lo + sp_i * chunk);
@@ -125,93 +150,103 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             qf[s] = u4_as_bf16x8(v);
         }
     }
+    wait_vmcnt<0>();   // queries in registers before the tile loads start
 
-    // ---- tile staging: the tile's (up to 4) table entries are workgroup-uniform;
-    // data loads take no branch on them (empty slots read page 0 and are zeroed)
-    auto fetch_entries = [&](int t, TileEntries &te) {
-        const int e0 = my_lo + t * ppt;
-        auto clean = [&](int4 en) {
-            if (en.x < 0 || en.x >= P.n_phys) en = int4{0, 0, 0, 0};
-            en.z = min(en.z, ps);
-            return en;
-        };
-        if (e0 + ppt <= my_hi) {            // the usual case: one scalar burst
-            te.a = clean(E[e0]);
-            te.b = ppt > 1 ? clean(E[e0 + 1]) : int4{0, 0, 0, 0};
-            te.c = ppt > 2 ? clean(E[e0 + 2]) : int4{0, 0, 0, 0};
-            te.d = ppt > 3 ? clean(E[e0 + 3]) : int4{0, 0, 0, 0};
-        } else {                            // the item's last, partial tile
-            auto get = [&](int pg) { return e0 + pg < my_hi ? clean(E[e0 + pg]) : int4{0, 0, 0, 0}; };
-            te.a = get(0);
-            te.b = get(1);
-            te.c = get(2);
-            te.d = get(3);
+    // ---- tile issue: entries (workgroup-uniform, scalar loads), bounds flags,
+    // key positions, and the global->LDS loads of K and V^T
+    // Page entries stream through LDS too: 64 entries (one 1 KB load by wave 0)
+    // per block, block b+1 requested when block b is first used, so the entry
+    // loads ride in the same in-order stream as the tiles and are covered by
+    // the same waits.  Lanes past the row's end re-read its last entry.
+    auto load_entry_block = [&](int k) {
+        if (wave == 0 && 64 * k < my_hi - my_lo) {
+            const int idx = min(my_lo + 64 * k + lane, e_end - 1);
+            SP_LDS_DMA16(E + idx, &sEnt[k & 1][0]);
         }
     };
-    auto tile_full = [&](const TileEntries &te) {
-        // no bounds needed if every slot holds a token visible to every query of the q-tile
+    auto fetch_entries = [&](int t, TileEntries &te) {
+        const int i0 = t * ppt;                              // entry index within the split
+        const int4 *blk = &sEnt[(i0 >> 6) & 1][i0 & 63];
+        auto get = [&](int pg) {
+            int4 en = int4{0, 0, 0, 0};
+            if (pg < ppt && my_lo + i0 + pg < my_hi) {
+                const int4 v = blk[pg];
+                en = int4{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                          __builtin_amdgcn_readfirstlane(v.z), 0};
+                if (en.x < 0 || en.x >= P.n_phys) en = int4{0, 0, 0, 0};
+                en.z = min(en.z, PS);
+            }
+            return en;
+        };
+        te.a = get(0);
+        te.b = get(1);
+        te.c = get(2);
+        te.d = get(3);
+    };
+    unsigned full_mask = 0, fix_mask = 0;     // per ring stage: no bounds needed / V chunks to trim
+    auto issue = [&](int t, int st) {
+        const int i0 = t * ppt;
+        if (i0 > 0 && (i0 & 63) == 0) load_entry_block((i0 >> 6) + 1);   // before this tile's loads
+        TileEntries te;
+        fetch_entries(t, te);
         const int4 x[4] = {te.a, te.b, te.c, te.d};
-        bool full = true;
+        bool full = true, fix = false;
         int kmin = INT32_MAX, kmax = INT32_MIN;
 #pragma unroll
         for (int pg = 0; pg < 4; ++pg)
             if (pg < ppt) {
-                full = full && x[pg].z == ps;
+                full = full && x[pg].z == PS;
+                fix = fix || (x[pg].z & 7) != 0;
                 kmin = min(kmin, x[pg].y);
                 kmax = max(kmax, x[pg].y + x[pg].z - 1);
             }
-        return full && kmax <= p0 && (!is_local || kmin > p_last - W);
-    };
-    // Per-thread chunk geometry, fixed for the whole item.  A page spans
-    // D*ps/8 >= 64 chunks, so the page of each chunk is uniform across a wave:
-    // its base address is computed in scalar registers once per tile and the
-    // lanes only add their constant offsets.
-    static_assert(D * ps / 8 % 64 == 0, "a page must cover whole waves of 16-byte chunks");
-    constexpr int per_page = D * ps / 8;
-    int k_pg[CPT], k_tk[CPT], k_off[CPT], k_lds[CPT], v_pg[CPT], v_k8[CPT], v_off[CPT], v_lds[CPT];
+        full = full && kmax <= p0 && (!is_local || kmin > p_last - W);
+        const unsigned bit = 1u << st;
+        full_mask = full ? (full_mask | bit) : (full_mask & ~bit);
+        fix_mask = fix ? (fix_mask | bit) : (fix_mask & ~bit);
+        // K: block q of this wave covers rows [4*blk, 4*blk+4) (D = 128) of one page
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-        const int c = tid + i * NT;
-        const int j = c / (D / 8), col = (c % (D / 8)) * 8;
-        k_pg[i] = __builtin_amdgcn_readfirstlane(c / per_page);
-        k_tk[i] = j % ps;
-        k_off[i] = k_tk[i] * D + col;
-        k_lds[i] = j * KS + col;
-        const int rem = c % per_page;
-        const int d = rem / (ps / 8), k8 = (rem % (ps / 8)) * 8;
-        v_pg[i] = k_pg[i];
-        v_k8[i] = k8;
-        v_off[i] = d * ps + k8;
-        v_lds[i] = d * VS + v_pg[i] * ps + k8;
-    }
-    u32x4 rk[CPT], rv[CPT];
-    auto load_tile = [&](const TileEntries &te) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            if (KCH % NT == 0 || tid + i * NT < KCH) {
-                const int4 en = te.pick(k_pg[i]);   // wave-uniform
-                const bf16 *kb = P.kp + (int64_t)en.x * (ps * D);
-                const bf16 *vb = P.vp + (int64_t)en.x * (ps * D);
-                const u32x4 kv = *(const u32x4 *)(kb + k_off[i]);
-                const u32x4 vv = *(const u32x4 *)(vb + v_off[i]);
-                rk[i] = k_tk[i] < en.z ? kv : u32x4{0, 0, 0, 0};
-                const int keep = en.z - v_k8[i];
-                rv[i] = keep >= 8 ? vv : (keep > 0 ? keep_first_bf16(vv, keep) : u32x4{0, 0, 0, 0});
-            }
+        for (int q = 0; q < KIW; ++q) {
+            const int blk = wave * KIW + q;
+            const int byte = blk * 1024 + lane * 16;
+            const int kr = byte / (2 * D), pc = (byte % (2 * D)) / 16;
+            const int c = pc ^ swz_k(kr);
+            const int4 en = te.pick(__builtin_amdgcn_readfirstlane(kr / PS));
+            const int tk = kr % PS;
+            const bf16 *src = P.kp + (int64_t)en.x * (PS * D) + tk * D + 8 * c;
+            SP_LDS_DMA16(src, &sK[st][blk * 512]);
         }
-    };
-    auto store_tile = [&](const TileEntries &te, int buf) {
+        // V^T: block q covers dims [8*blk, 8*blk+8); lane -> (dim, 8 consecutive keys)
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            if (KCH % NT == 0 || tid + i * NT < KCH) {
-                *(u32x4 *)&sK[buf][k_lds[i]] = rk[i];
-                *(u32x4 *)&sV[buf][v_lds[i]] = rv[i];
-            }
+        for (int q = 0; q < VIW; ++q) {
+            const int blk = wave * VIW + q;
+            const int d = blk * 8 + (lane >> 3), pc = lane & 7;
+            const int c = pc ^ swz_v(d);
+            const int key = 8 * c;
+            const int4 en = te.pick(key / PS);
+            const int k8 = key % PS;
+            const bf16 *src = en.z - k8 > 0 ? P.vp + ((int64_t)en.x * D + d) * PS + k8 : P.zero16;
+            SP_LDS_DMA16(src, &sV[st][blk * 512]);
         }
         if (tid < BN) {
-            const int pg = tid / ps, tk = tid % ps;
-            const int4 en = te.pick(pg);
-            sPos[buf][tid] = tk < en.z ? en.y + tk : kPosInvalid;
+            const int4 en = te.pick(tid / PS);
+            const int tk = tid % PS;
+            sPos[st][tid] = tk < en.z ? en.y + tk : kPosInvalid;
+        }
+    };
+    // zero the keys past n_valid inside partially filled 8-key chunks of V^T
+    auto fixup = [&](int st) {
+        for (int idx = tid; idx < D * 8; idx += NW * 64) {
+            const int d = idx >> 3, pc = idx & 7;
+            const int key = 8 * (pc ^ swz_v(d));
+            const int kp = sPos[st][key];                 // position of the chunk's first key
+            int keep = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) keep += sPos[st][key + i] != kPosInvalid;
+            if (kp != kPosInvalid && keep < 8) {
+                u32x4 *cell = (u32x4 *)&sV[st][d * BN + pc * 8];
+                *cell = keep_first_bf16(*cell, keep);
+            }
         }
     };
 
@@ -221,100 +256,156 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{0};
 
-    TileEntries te_cur, te_nxt;
-    bool full_cur = false, full_nxt = false;
-    if (n_tiles > 0) {
-        fetch_entries(0, te_cur);
-        full_cur = tile_full(te_cur);
-        load_tile(te_cur);
-        store_tile(te_cur, 0);
-    }
-    __syncthreads();
-    for (int t = 0; t < n_tiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < n_tiles) {
-            fetch_entries(t + 1, te_nxt);
-            full_nxt = tile_full(te_nxt);
-            load_tile(te_nxt);
-        }
+    // per-lane LDS read offsets (bf16 elements); the swizzle of an operand row
+    // does not depend on which 32-row tile it sits in
+    const int krow0 = sigma(n) * D, kx = swz_k(sigma(n));
+    const int vrow0 = n * BN, vx = swz_v(n);
 
-        // S^T = K Q^T over the two 32-key halves of the tile
-        f32x16 S[BN / 32];
+    auto qk = [&](int st, f32x16 (&S)[BN / 32]) {       // S^T = K Q^T of one tile
 #pragma unroll
         for (int kt = 0; kt < BN / 32; ++kt) {
             S[kt] = f32x16{0};
-            const bf16 *krow = &sK[buf][(32 * kt + sigma(n)) * KS + 8 * h];
+            const bf16 *kbase = &sK[st][krow0 + 32 * kt * D];
 #pragma unroll
             for (int s = 0; s < DK; ++s) {
-                const bf16x8 a = *(const bf16x8 *)(krow + 16 * s);
+                const bf16x8 a = *(const bf16x8 *)(kbase + ((2 * s + h) ^ kx) * 8);
                 S[kt] = mfma32x32x16(a, qf[s], S[kt]);
             }
         }
-        // bounds (boundary tiles only) and online softmax; the running max is kept
-        // on raw scores (the scale is positive) and folded into one FMA per exp
-        if (!full_cur) {
+    };
+    auto mask = [&](int st, f32x16 (&S)[BN / 32]) {     // bounds of a boundary tile
 #pragma unroll
-            for (int kt = 0; kt < BN / 32; ++kt)
+        for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int kpos = sPos[buf][32 * kt + 16 * (v >> 3) + 8 * h + (v & 7)];
-                    S[kt][v] = (kpos <= pq && kpos > lowq) ? S[kt][v] : -INFINITY;
-                }
-        }
+            for (int v = 0; v < 16; ++v) {
+                const int kpos = sPos[st][32 * kt + 16 * (v >> 3) + 8 * h + (v & 7)];
+                S[kt][v] = (kpos <= pq && kpos > lowq) ? S[kt][v] : -INFINITY;
+            }
+    };
+    // Online softmax with a lazily moved reference max (log2 domain, raw scores
+    // times c = scale*log2 e): the reference only moves when a row's max exceeds
+    // it by more than kLazy, so weights stay <= 2^kLazy (harmless in fp32 and
+    // bf16) and the rescale of the accumulators becomes rare.  The final
+    // normalisation by l makes the result independent of the reference.
+    constexpr float kLazy = 8.f;
+    const float cl = P.scale_log2;
+    auto update_max = [&](f32x16 (&S)[BN / 32]) {
         float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
             for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[kt][v]);
-        mx = fmaxf(mx, xor_lane(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float c = P.scale_log2;
-        // exponents are <= 0 here; v_exp_f32 flushes results below 2^-126 to zero, which is harmless
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c);
-        const float off = -m_use * c;
-        float rs = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < BN / 32; ++kt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(S[kt][v], c, off));
-                S[kt][v] = p;
-                rs += p;
-            }
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
-        if (__any(alpha != 1.f)) {
+        mx = fmaxf(mx, xor_lane(mx, 32)) * cl;
+        if (__any(mx > m_run + kLazy)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+            m_run = m_new;
         }
-
-        // O^T += V^T P^T, 16 keys per step
+    };
+    // weights of one tile -> packed bf16 P^T operands (exponents <= kLazy;
+    // v_exp_f32 flushes results below 2^-126 to zero, which is harmless)
+    auto softmax = [&](f32x16 (&S)[BN / 32], u32x4 (&Pk)[BN / 16]) {
+        const float off = m_run == -INFINITY ? 0.f : -m_run;
+        float rs = 0.f;
 #pragma unroll
         for (int s2 = 0; s2 < BN / 16; ++s2) {
             const int kt = s2 >> 1, u = s2 & 1;
-            u32x4 pk;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) pk[w] = pack_bf16x2(S[kt][8 * u + 2 * w], S[kt][8 * u + 2 * w + 1]);
-            const bf16x8 pb = u4_as_bf16x8(pk);
+            for (int w = 0; w < 4; ++w) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(S[kt][8 * u + 2 * w], cl, off));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(S[kt][8 * u + 2 * w + 1], cl, off));
+                rs += p0 + p1;
+                Pk[s2][w] = pack_bf16x2(p0, p1);
+            }
+        }
+        l_run += rs;
+    };
+    auto pv = [&](int st, const u32x4 (&Pk)[BN / 16]) {   // O^T += V^T P^T, 16 keys per step
+#pragma unroll
+        for (int s2 = 0; s2 < BN / 16; ++s2) {
+            const bf16x8 pb = u4_as_bf16x8(Pk[s2]);
+            const int vc = ((2 * s2 + h) ^ vx) * 8;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const bf16x8 a = *(const bf16x8 *)&sV[buf][(32 * dt + n) * VS + 16 * s2 + 8 * h];
+                const bf16x8 a = *(const bf16x8 *)&sV[st][vrow0 + 32 * dt * BN + vc];
                 acc[dt] = mfma32x32x16(a, pb, acc[dt]);
             }
         }
+    };
+    auto wait_first_tile = [&]() {        // the prologue issued tiles 0 .. min(2, n_tiles-1)
+        const int after = min(NBUF - 2, n_tiles - 1);
+        if (after >= 2) wait_vmcnt<2 * IPW>();
+        else if (after == 1) wait_vmcnt<IPW>();
+        else wait_vmcnt<0>();
+    };
 
-        if (t + 1 < n_tiles) {
-            store_tile(te_nxt, buf ^ 1);
-            full_cur = full_nxt;
+    // ---- ring pipeline.  Tiles t and t+1 are resident, t+2 is in flight.
+    // Iteration t: the QK^T of tile t+1 runs on the matrix cores interleaved
+    // with the softmax of tile t on the vector ALUs, then P.V of tile t.
+    static_assert(NBUF == 4, "the pipeline keeps two tiles resident and two in flight");
+    if (n_tiles > 0) {
+        load_entry_block(0);
+        wait_vmcnt<0>();
+        lds_barrier();
+        load_entry_block(1);
+    }
+#pragma unroll
+    for (int j = 0; j < NBUF - 1; ++j)
+        if (j < n_tiles) issue(j, j);
+    f32x16 Sc[BN / 32];
+    if (n_tiles > 0) {
+        wait_first_tile();
+        lds_barrier();
+        if (fix_mask & 1) {
+            fixup(0);
+            lds_barrier();
         }
-        __syncthreads();
+        qk(0, Sc);
+    }
+    for (int t = 0; t < n_tiles; ++t) {
+        const int st = t % NBUF, st1 = (t + 1) % NBUF;
+        const bool has1 = t + 1 < n_tiles;
+        if (has1) {                          // tiles issued after t+1: at most one
+            if (t + 2 < n_tiles) wait_vmcnt<IPW>();
+            else wait_vmcnt<0>();
+        }
+        lds_barrier();                       // tile t+1 visible; stage of tile t-1 free
+        if (has1 && ((fix_mask >> st1) & 1)) fixup(st1);   // visible after the next barrier
+        if (t + NBUF - 1 < n_tiles) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF);
+        if (!((full_mask >> st) & 1)) mask(st, Sc);
+        update_max(Sc);
+        f32x16 Sn[BN / 32];
+        u32x4 Pk[BN / 16];
+        qk(st1, Sn);                         // past the last tile this reads a stale stage; unused
+        softmax(Sc, Pk);
+        pv(st, Pk);
+        // Schedule of this block: the MFMAs of QK^T(t+1) interleaved with the
+        // exponentials and packing of tile t (vector ALU, incl. transcendental),
+        // then the MFMAs of P.V(t); operand reads run two MFMAs ahead.
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                 // LDS read
+#pragma unroll
+        for (int i = 0; i < 2 * DK; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);             // VALU + transcendental
+        }
+#pragma unroll
+        for (int i = 0; i < (BN / 16) * DT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);
+        }
+#pragma unroll
+        for (int kt = 0; kt < BN / 32; ++kt) Sc[kt] = Sn[kt];
     }
 
     // ---- epilogue
     const float l = l_run + xor_lane(l_run, 32);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    const float lse = l > 0.f ? (m_run * P.scale_log2 + log2f(l)) * kLn2 : -INFINITY;
+    const float lse = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
     if (!row_ok) return;
     if (ns == 1) {
         bf16 *orow = P.out + ((int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g) * D;
@@ -418,9 +509,10 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, int
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ row_ptr,
                                                    const int32_t *__restrict__ tok_ptr, int n_seq, int n_rows,
                                                    int tpt, int chunk, int32_t *item_ptr, int32_t *part_ptr,
-                                                   int32_t *nsplit) {
+                                                   int32_t *nsplit, int32_t *zero) {
     __shared__ int s_items[256], s_parts[256];
     __shared__ int carry_i, carry_p;
+    if (threadIdx.x < 64) zero[threadIdx.x] = 0;
     if (threadIdx.x == 0) { carry_i = 0; carry_p = 0; }
     __syncthreads();
     for (int base = 0; base < n_rows; base += 256) {
@@ -466,7 +558,7 @@ int launch_plan(const Plan &p, const int32_t *d_row_ptr, const int32_t *d_tok_pt
     char *w = (char *)ws;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, d_row_ptr, d_tok_ptr, n_seq, p.n_rows,
                        p.tok_per_tile, p.chunk_pages, (int32_t *)(w + p.off_item_ptr),
-                       (int32_t *)(w + p.off_part_ptr), (int32_t *)(w + p.off_nsplit));
+                       (int32_t *)(w + p.off_part_ptr), (int32_t *)(w + p.off_nsplit), (int32_t *)(w + p.off_zero));
     return check_hip(hipGetLastError(), "plan launch");
 }
 
@@ -502,13 +594,11 @@ int launch_prefill(const AttnArgs &a, const Plan &p, int64_t n_tok, hipStream_t 
     P.Hq = a.n_slot * a.group;
     P.n_phys = a.n_phys;
     P.scale_log2 = a.scale * kLog2e;
+    P.zero16 = (const bf16 *)(w + p.off_zero);
     const dim3 grid((unsigned)p.n_items);
 #define SP_PREFILL_CASE(DD, PSV)                                                                        \
     if (a.head_dim == DD && a.page_size == PSV) {                                                       \
-        if (p.waves == 8)                                                                               \
-            hipLaunchKernelGGL((prefill_bf16_kernel<DD, 8, PSV>), grid, dim3(512), 0, stream, P);      \
-        else                                                                                            \
-            hipLaunchKernelGGL((prefill_bf16_kernel<DD, 4, PSV>), grid, dim3(256), 0, stream, P);      \
+        hipLaunchKernelGGL((prefill_bf16_kernel<DD, 8, PSV, 4>), grid, dim3(512), 0, stream, P);       \
         if (p.n_parts)                                                                                  \
             hipLaunchKernelGGL(prefill_merge_kernel<DD>, grid, dim3(256), 0, stream, P, p.rows_per_tile); \
     }

@@ -60,6 +60,7 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
     p.off_part_ptr = off; off += sizeof(int32_t) * (n_rows + 1);
     p.off_nsplit = off;   off += sizeof(int32_t) * n_rows;
     off = align_up(off, 256);
+    p.off_zero = off;     off += 256;          // zero-filled by the plan kernel
 
     if (dtype == SP_F32) {
         // The fp32 kernels take one query token per workgroup and never split.
@@ -76,11 +77,8 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
     // work units (row, q-tile) and their page counts
     int64_t units = 0, work = 0;
     if (kind == SP_WS_PREFILL) {
-        // 8 waves (256 query rows) when a sequence brings that many rows, so one
-        // staged K/V tile feeds twice the queries; 4 waves otherwise
-        int max_tok = 0;
-        for (int q = 0; q < n_seq; ++q) max_tok = std::max(max_tok, h_tok_ptr[q + 1] - h_tok_ptr[q]);
-        p.waves = (int64_t)max_tok * group >= 2 * kPrefillRowsPerWave * 4 ? 8 : 4;
+        // 8 waves of 32 query rows: one staged K/V tile feeds 256 rows
+        p.waves = 8;
         p.rows_per_tile = kPrefillRowsPerWave * p.waves;
         p.tok_per_tile = p.rows_per_tile / group;
         for (int r = 0; r < n_rows; ++r) {

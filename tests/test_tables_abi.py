@@ -29,6 +29,15 @@ def test_library_exports_every_declared_symbol():
     assert sp.version() == 100
 
 
+def test_library_has_no_unresolved_internal_symbols():
+    """Every kernel's host launch stub must be defined (a device-only builtin in a
+    kernel body can make the host pass drop it silently)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", sp._LIB_PATH], capture_output=True, text=True).stdout
+    bad = [l for l in out.splitlines() if "_ZN2sp" in l]
+    assert not bad, bad[:5]
+
+
 def _lib_tables(lay, call, free):
     return sp.build_tables(**lay.abi_arrays(call), page_size=lay.page_size, free_list=free)
 
