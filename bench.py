@@ -12,6 +12,8 @@ host; its time is reported separately (build_tables_ms).
 
 Work counted is algorithmic only:
   prefill FLOPs = 4 * head_dim per (query row, visible key) pair;
+  prefill bytes = K and V of every page in each head's table, read once
+                  (the chunk's queries share them) + q/out;
   relocate bytes = 2 * (valid segment-key elements) * elem + 16 B per list item;
   decode bytes  = per slot, visible keys * 2 * head_dim * elem (K and V read
                   once, shared by the group's heads) + q/out + table entries.
@@ -19,7 +21,11 @@ Visible counts are read back from the HIP path itself with zero queries
 (every weight is then exactly 1, so exp(LSE) is the count).
 
 The reported value is the whole step's share of the MI355X roofline:
-100 * (prefill FLOPs / 2.5 PFLOP/s + (relocate + decode bytes) / 8 TB/s) / step time.
+100 * (max(prefill FLOPs / 2.5 PFLOP/s, prefill bytes / 8 TB/s)
+       + (relocate + decode bytes) / 8 TB/s) / step time.
+(A 64-token chunk over a shared KV page does 4 * 256 rows FLOPs per 4 bytes
+of K and V: about 256 FLOP/B, below the chip's 312 FLOP/B ridge, so the
+prefill of such a chunk is bound by HBM, not by the matrix cores.)
 """
 from __future__ import annotations
 
@@ -94,9 +100,13 @@ def algorithmic_work(w, torch):
     prefill_flops = int(cnt_p.sum()) * 4 * D
     per_slot = cnt_d[:, ::lay.group]                       # one head per slot: K/V read once per slot
     decode_bytes = int(per_slot.sum()) * 2 * D * esz + 2 * w.q_decode.numel() * esz + 16 * len(w.td["entries"])
+    ent_p, rp = w.tp["entries"], w.tp["row_ptr"]
+    table_keys = int(ent_p[:, 2].sum())
+    prefill_bytes = table_keys * 2 * D * esz + 2 * w.q_prefill.numel() * esz + 16 * len(ent_p)
     reloc = w.tp["reloc"]
     reloc_bytes = 2 * int(reloc[:, 2].sum()) * D * esz + 16 * len(reloc)
-    return dict(prefill_flops=prefill_flops, decode_bytes=decode_bytes, relocate_bytes=reloc_bytes,
+    return dict(prefill_flops=prefill_flops, prefill_bytes=prefill_bytes, decode_bytes=decode_bytes,
+                relocate_bytes=reloc_bytes,
                 prefill_pairs=int(cnt_p.sum()), decode_keys=int(per_slot.sum()))
 
 
@@ -113,9 +123,11 @@ def cpu_baseline(w, work_budget_s: float):
     rows_l = [s * lay.n_seq for s in range(lay.n_slot) if lay.cls[s] == 1]
     order = [r for pair in zip(rows_g, rows_l) for r in pair] + rows_g[len(rows_l):] + rows_l[len(rows_g):]
     flops = 0
+    pbytes = 0
     rbytes = 0
     dbytes = 0
     t_used = 0.0
+    ent_p, rp = w.tp["entries"], w.tp["row_ptr"]
     n_rows = 0
     esz = 4 if lay.dtype == "f32" else 2
     with threadpool_limits(1):
@@ -136,11 +148,12 @@ def cpu_baseline(w, work_budget_s: float):
             t_used += time.perf_counter() - t0
             n_rows += 1
             flops += int(cnt.sum()) * G * 4 * D
+            pbytes += int(ent_p[rp[r]:rp[r + 1], 2].sum()) * 2 * D * esz
             rbytes += 2 * ctx * D * esz
             dbytes += int(cd.sum()) * 2 * D * esz
             if t_used >= work_budget_s:
                 break
-    t_roof = flops / PEAK_BF16_FLOPS + (rbytes + dbytes) / PEAK_HBM
+    t_roof = max(flops / PEAK_BF16_FLOPS, pbytes / PEAK_HBM) + (rbytes + dbytes) / PEAK_HBM
     return {"value": 100.0 * t_roof / t_used, "unit": "% of roofline", "cores": 1, "kind": "oracle",
             "sample": f"{n_rows} of {lay.n_slot * lay.n_seq} (slot, seq) rows of the same workload, alternating "
                       f"global/local: fp64 relocation of their segment keys, prefill of all {lay.n_prefill} "
@@ -209,29 +222,35 @@ def main():
     ms_per_step = wall / args.steps * 1e3
 
     peak_flops = PEAK_FP32_FLOPS if lay.dtype == "f32" else PEAK_BF16_FLOPS
+    t_pref_roof = max(work["prefill_flops"] / peak_flops, work["prefill_bytes"] / PEAK_HBM)
+    pref_bound = "mfma" if work["prefill_flops"] / peak_flops >= work["prefill_bytes"] / PEAK_HBM else "hbm"
     calls = {
         "rope_relocate": {"ms": round(t_reloc, 4), "GB/s": round(work["relocate_bytes"] / t_reloc / 1e6, 1),
                           "frac_hbm": round(work["relocate_bytes"] / t_reloc / 1e-3 / PEAK_HBM, 4),
                           "bytes": work["relocate_bytes"]},
         "segpaged_prefill": {"ms": round(t_pref, 4), "TFLOP/s": round(work["prefill_flops"] / t_pref / 1e9, 2),
                              "frac_mfma": round(work["prefill_flops"] / t_pref / 1e-3 / peak_flops, 4),
-                             "flops": work["prefill_flops"]},
+                             "GB/s": round(work["prefill_bytes"] / t_pref / 1e6, 1),
+                             "frac_hbm": round(work["prefill_bytes"] / t_pref / 1e-3 / PEAK_HBM, 4),
+                             "flops": work["prefill_flops"], "bytes": work["prefill_bytes"],
+                             "bound": pref_bound},
         "segpaged_decode": {"ms": round(t_dec, 4), "GB/s": round(work["decode_bytes"] / t_dec / 1e6, 1),
                             "frac_hbm": round(work["decode_bytes"] / t_dec / 1e-3 / PEAK_HBM, 4),
                             "bytes": work["decode_bytes"]},
         "segpaged_build_tables": {"host_ms": round(build_ms, 3), "outside_timed_step": True},
     }
-    t_roof = work["prefill_flops"] / peak_flops + (work["relocate_bytes"] + work["decode_bytes"]) / PEAK_HBM
+    t_roof = t_pref_roof + (work["relocate_bytes"] + work["decode_bytes"]) / PEAK_HBM
     value = 100.0 * t_roof / (ms_per_step * 1e-3)
 
     times = {"rope_relocate": t_reloc, "segpaged_prefill": t_pref, "segpaged_decode": t_dec}
     dom = max(times, key=times.get)
-    if dom == "segpaged_prefill":
+    if dom == "segpaged_prefill" and pref_bound == "mfma":
         ach = work["prefill_flops"] / (t_pref * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_flops / 1e12, "unit": "TFLOP/s",
                 "frac": round(ach * 1e12 / peak_flops, 4)}
     else:
-        b = work["relocate_bytes"] if dom == "rope_relocate" else work["decode_bytes"]
+        b = {"rope_relocate": work["relocate_bytes"], "segpaged_decode": work["decode_bytes"],
+             "segpaged_prefill": work["prefill_bytes"]}[dom]
         ach = b / (times[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                 "frac": round(ach * 1e9 / PEAK_HBM, 4)}

@@ -30,7 +30,7 @@ struct DecodeParams {
     float *lse;
     const int32_t *q_pos, *cls, *window, *row_ptr;
     const int4 *entries;
-    const int32_t *item_ptr, *part_ptr, *nsplit;
+    const int32_t *item_ptr, *item_ptr2, *part_ptr, *nsplit;
     float *part_o, *part_lse;
     int n_seq, n_rows, G, ps, Hq;
     int64_t n_phys;
@@ -111,10 +111,9 @@ __global__ __launch_bounds__(NWD * 64) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, grp = lane >> 4;
 
-    const int b = blockIdx.x;
-    const int r = find_row(P.item_ptr, P.n_rows, b);
+    int r, sp_i;
+    item_of(P.item_ptr, P.item_ptr2, P.n_rows, blockIdx.x, &r, &sp_i);
     const int ns = P.nsplit[r];
-    const int sp_i = b - P.item_ptr[r];
     const int seq = r % P.n_seq, slot = r / P.n_seq;
     const int G = P.G;
     constexpr int ps = PS;
@@ -297,6 +296,7 @@ int launch_decode(const AttnArgs &a, const Plan &p, hipStream_t stream) {
     P.row_ptr = a.d_row_ptr;
     P.entries = (const int4 *)a.d_entries;
     P.item_ptr = (const int32_t *)(w + p.off_item_ptr);
+    P.item_ptr2 = (const int32_t *)(w + p.off_item_ptr2);
     P.part_ptr = (const int32_t *)(w + p.off_part_ptr);
     P.nsplit = (const int32_t *)(w + p.off_nsplit);
     P.part_o = (float *)(w + p.off_part_o);

@@ -83,6 +83,19 @@ __device__ __forceinline__ int find_row(const int32_t *item_ptr, int n_rows, int
     return lo;
 }
 
+// Row and index within the row of work item b.  Items are numbered long-first:
+// [0, item_ptr[n_rows]) are the items of split rows (first item of row r at
+// item_ptr[r]), the rest those of unsplit rows (at item_ptr[n_rows] + item_ptr2[r]).
+__device__ __forceinline__ void item_of(const int32_t *item_ptr, const int32_t *item_ptr2, int n_rows, int b,
+                                        int *row, int *local) {
+    const int n_long = item_ptr[n_rows];
+    const int32_t *ip = b < n_long ? item_ptr : item_ptr2;
+    const int bb = b < n_long ? b : b - n_long;
+    const int r = find_row(ip, n_rows, bb);
+    *row = r;
+    *local = bb - ip[r];
+}
+
 // First index e in [a, b) whose key(e) > x, keys ascending in e; b if none.
 template <class Key>
 __device__ __forceinline__ int first_greater(int a, int b, int x, Key key) {

@@ -23,10 +23,12 @@ constexpr int kPrefillKeysPerTile = 64;   // keys staged in LDS per iteration
 constexpr int kDecodeKeysPerBlock = 32;   // keys one wave consumes per step
 constexpr int kDecodeWaves = 4;
 
-// Split planning targets: enough work items to fill 256 CUs a few times over,
-// while each split still streams at least kMinSplitKeys keys.
-constexpr int kTargetItems = 1024;         // prefill
-constexpr int kTargetDecodeItems = 384;    // decode: about one streaming split per CU
+// Split planning: the prefill splits long rows so that their pieces fill the
+// 256 CUs of the chip once; decode aims at about one streaming split per CU.
+// Every split still streams at least kMinSplitKeys keys.
+constexpr int kPlanCUs = 256;
+constexpr int kPrefillSetupTiles = 3;      // fixed cost of a prefill item, in 64-key tiles
+constexpr int kTargetDecodeItems = 384;
 constexpr int kMinSplitKeys = 512;
 constexpr int kMaxSplits = 1024;
 constexpr int kDecodeMaxChunk = 512;       // pages of one decode split (its entries are staged in LDS)
@@ -52,7 +54,10 @@ struct Plan {
     int chunk_pages = 0;     // pages per kv split (INT32_MAX = no split)
     int64_t n_items = 0;     // work items (= workgroups of the attention kernel)
     int64_t n_parts = 0;     // work items whose result is a partial to merge
-    size_t off_item_ptr = 0, off_part_ptr = 0, off_nsplit = 0, off_zero = 0, off_part_o = 0, off_part_lse = 0;
+    // Work items are numbered long-first: the items of split rows (row order),
+    // then those of unsplit rows.  item_ptr[r] / item_ptr2[r] = first item of
+    // row r in the first / second range (zero-length for rows of the other).
+    size_t off_item_ptr = 0, off_item_ptr2 = 0, off_part_ptr = 0, off_nsplit = 0, off_zero = 0, off_part_o = 0, off_part_lse = 0;
     size_t bytes = 0;        // workspace bytes
 };
 

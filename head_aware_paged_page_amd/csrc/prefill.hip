@@ -38,12 +38,14 @@ struct PrefillParams {
     float *lse;
     const int32_t *tok_ptr, *q_pos0, *cls, *window, *row_ptr;
     const int4 *entries;
-    const int32_t *item_ptr, *part_ptr, *nsplit;
+    const int32_t *item_ptr, *item_ptr2, *part_ptr, *nsplit;
     float *part_o, *part_lse;
     int n_seq, n_rows, G, ps, tpt, Hq;
     int64_t n_phys;
     float scale_log2;   // softmax_scale * log2(e)
     const bf16 *zero16;  // 16 zero bytes in the workspace (source for empty V slots)
+    int *work_ctr;       // next work item to take; zeroed by the plan kernel
+    int n_items;
 };
 
 // Table entries of the (up to four) pages of one 64-key tile, workgroup-uniform.
@@ -102,337 +104,349 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     __shared__ int sPos[NBUF][BN];
     __shared__ __attribute__((aligned(16))) int4 sEnt[2][64];
 
+    __shared__ int s_item;
+
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, h = lane >> 5;
     auto swz_k = [](int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
     auto swz_v = [](int d) { return (d >> 1) & 7; };
 
-    // ---- work item
-    const int b = blockIdx.x;
-    const int r = find_row(P.item_ptr, P.n_rows, b);
-    const int ns = P.nsplit[r];
-    const int local = b - P.item_ptr[r];
-    const int qt = local / ns, sp_i = local % ns;
-    const int seq = r % P.n_seq, slot = r / P.n_seq;
-    const int tok_base = P.tok_ptr[seq];
-    const int t0 = qt * P.tpt;
-    const int ntok = min(P.tpt, P.tok_ptr[seq + 1] - tok_base - t0);
-    const int p0 = P.q_pos0[seq] + t0, p_last = p0 + ntok - 1;
-    const int G = P.G;
-    const bool is_local = P.cls[slot] == SP_LOCAL;
-    const int W = is_local ? P.window[slot] : 0;
-    const int nrows = ntok * G;
+    // Persistent workgroups (one per CU) take the work items in their long-first
+    // order from a counter: the hardware dispatcher places workgroups in order
+    // and would hold short items back until a long one ends.
+    for (;;) {
+        if (tid == 0) s_item = atomicAdd(P.work_ctr, 1);
+        __syncthreads();                     // also: every wave is done with the previous item
+        const int b = s_item;
+        __syncthreads();
+        if (b >= P.n_items) break;
 
-    // ---- the q-tile's visible entry range, then this split's share
-    const int e_beg = P.row_ptr[r], e_end = P.row_ptr[r + 1];
-    const int4 *E = P.entries;
-    int lo, hi;
-    visible_range(E, e_beg, e_end, p_last, is_local, p0 - W, &lo, &hi);
-    int chunk = (hi - lo + ns - 1) / ns;
-    chunk = (chunk + ppt - 1) / ppt * ppt;
-    const int my_lo = min(hi, lo + sp_i * chunk);
-    const int my_hi = min(hi, my_lo + chunk);
-    const int n_tiles = (my_hi - my_lo + ppt - 1) / ppt;
+        // ---- work item
+        int r, local;
+        item_of(P.item_ptr, P.item_ptr2, P.n_rows, b, &r, &local);
+        const int ns = P.nsplit[r];
+        const int qt = local / ns, sp_i = local % ns;
+        const int seq = r % P.n_seq, slot = r / P.n_seq;
+        const int tok_base = P.tok_ptr[seq];
+        const int t0 = qt * P.tpt;
+        const int ntok = min(P.tpt, P.tok_ptr[seq + 1] - tok_base - t0);
+        const int p0 = P.q_pos0[seq] + t0, p_last = p0 + ntok - 1;
+        const int G = P.G;
+        const bool is_local = P.cls[slot] == SP_LOCAL;
+        const int W = is_local ? P.window[slot] : 0;
+        const int nrows = ntok * G;
 
-    // ---- queries of this wave: row = 32*wave + n -> (token, head)
-    const int row = 32 * wave + n;
-    const bool row_ok = row < nrows;
-    const int tq = row / G, g = row % G;
-    const int pq = p0 + tq;                    // this lane's query position
-    const int lowq = is_local ? pq - W : INT32_MIN;   // visible iff lowq < pos <= pq
-    bf16x8 qf[DK];
-    {
-        const bf16 *qrow = P.q + ((int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g) * D;
-#pragma unroll
-        for (int s = 0; s < DK; ++s) {
-            u32x4 v = {0, 0, 0, 0};
-            if (row_ok) v = *(const u32x4 *)(qrow + 16 * s + 8 * h);
-            qf[s] = u4_as_bf16x8(v);
-        }
-    }
-    wait_vmcnt<0>();   // queries in registers before the tile loads start
+        // ---- the q-tile's visible entry range, then this split's share
+        const int e_beg = P.row_ptr[r], e_end = P.row_ptr[r + 1];
+        const int4 *E = P.entries;
+        int lo, hi;
+        visible_range(E, e_beg, e_end, p_last, is_local, p0 - W, &lo, &hi);
+        int chunk = (hi - lo + ns - 1) / ns;
+        chunk = (chunk + ppt - 1) / ppt * ppt;
+        const int my_lo = min(hi, lo + sp_i * chunk);
+        const int my_hi = min(hi, my_lo + chunk);
+        const int n_tiles = (my_hi - my_lo + ppt - 1) / ppt;
 
-    // ---- tile issue: entries (workgroup-uniform, scalar loads), bounds flags,
-    // key positions, and the global->LDS loads of K and V^T
-    // Page entries stream through LDS too: 64 entries (one 1 KB load by wave 0)
-    // per block, block b+1 requested when block b is first used, so the entry
-    // loads ride in the same in-order stream as the tiles and are covered by
-    // the same waits.  Lanes past the row's end re-read its last entry.
-    auto load_entry_block = [&](int k) {
-        if (wave == 0 && 64 * k < my_hi - my_lo) {
-            const int idx = min(my_lo + 64 * k + lane, e_end - 1);
-            SP_LDS_DMA16(E + idx, &sEnt[k & 1][0]);
-        }
-    };
-    auto fetch_entries = [&](int t, TileEntries &te) {
-        const int i0 = t * ppt;                              // entry index within the split
-        const int4 *blk = &sEnt[(i0 >> 6) & 1][i0 & 63];
-        auto get = [&](int pg) {
-            int4 en = int4{0, 0, 0, 0};
-            if (pg < ppt && my_lo + i0 + pg < my_hi) {
-                const int4 v = blk[pg];
-                en = int4{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
-                          __builtin_amdgcn_readfirstlane(v.z), 0};
-                if (en.x < 0 || en.x >= P.n_phys) en = int4{0, 0, 0, 0};
-                en.z = min(en.z, PS);
-            }
-            return en;
-        };
-        te.a = get(0);
-        te.b = get(1);
-        te.c = get(2);
-        te.d = get(3);
-    };
-    unsigned full_mask = 0, fix_mask = 0;     // per ring stage: no bounds needed / V chunks to trim
-    auto issue = [&](int t, int st) {
-        const int i0 = t * ppt;
-        if (i0 > 0 && (i0 & 63) == 0) load_entry_block((i0 >> 6) + 1);   // before this tile's loads
-        TileEntries te;
-        fetch_entries(t, te);
-        const int4 x[4] = {te.a, te.b, te.c, te.d};
-        bool full = true, fix = false;
-        int kmin = INT32_MAX, kmax = INT32_MIN;
-#pragma unroll
-        for (int pg = 0; pg < 4; ++pg)
-            if (pg < ppt) {
-                full = full && x[pg].z == PS;
-                fix = fix || (x[pg].z & 7) != 0;
-                kmin = min(kmin, x[pg].y);
-                kmax = max(kmax, x[pg].y + x[pg].z - 1);
-            }
-        full = full && kmax <= p0 && (!is_local || kmin > p_last - W);
-        const unsigned bit = 1u << st;
-        full_mask = full ? (full_mask | bit) : (full_mask & ~bit);
-        fix_mask = fix ? (fix_mask | bit) : (fix_mask & ~bit);
-        // K: block q of this wave covers rows [4*blk, 4*blk+4) (D = 128) of one page
-#pragma unroll
-        for (int q = 0; q < KIW; ++q) {
-            const int blk = wave * KIW + q;
-            const int byte = blk * 1024 + lane * 16;
-            const int kr = byte / (2 * D), pc = (byte % (2 * D)) / 16;
-            const int c = pc ^ swz_k(kr);
-            const int4 en = te.pick(__builtin_amdgcn_readfirstlane(kr / PS));
-            const int tk = kr % PS;
-            const bf16 *src = P.kp + (int64_t)en.x * (PS * D) + tk * D + 8 * c;
-            SP_LDS_DMA16(src, &sK[st][blk * 512]);
-        }
-        // V^T: block q covers dims [8*blk, 8*blk+8); lane -> (dim, 8 consecutive keys)
-#pragma unroll
-        for (int q = 0; q < VIW; ++q) {
-            const int blk = wave * VIW + q;
-            const int d = blk * 8 + (lane >> 3), pc = lane & 7;
-            const int c = pc ^ swz_v(d);
-            const int key = 8 * c;
-            const int4 en = te.pick(key / PS);
-            const int k8 = key % PS;
-            const bf16 *src = en.z - k8 > 0 ? P.vp + ((int64_t)en.x * D + d) * PS + k8 : P.zero16;
-            SP_LDS_DMA16(src, &sV[st][blk * 512]);
-        }
-        if (tid < BN) {
-            const int4 en = te.pick(tid / PS);
-            const int tk = tid % PS;
-            sPos[st][tid] = tk < en.z ? en.y + tk : kPosInvalid;
-        }
-    };
-    // zero the keys past n_valid inside partially filled 8-key chunks of V^T
-    auto fixup = [&](int st) {
-        for (int idx = tid; idx < D * 8; idx += NW * 64) {
-            const int d = idx >> 3, pc = idx & 7;
-            const int key = 8 * (pc ^ swz_v(d));
-            const int kp = sPos[st][key];                 // position of the chunk's first key
-            int keep = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) keep += sPos[st][key + i] != kPosInvalid;
-            if (kp != kPosInvalid && keep < 8) {
-                u32x4 *cell = (u32x4 *)&sV[st][d * BN + pc * 8];
-                *cell = keep_first_bf16(*cell, keep);
-            }
-        }
-    };
-
-    // ---- running softmax state (log2 domain) and O^T accumulators
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x16 acc[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{0};
-
-    // per-lane LDS read offsets (bf16 elements); the swizzle of an operand row
-    // does not depend on which 32-row tile it sits in
-    const int krow0 = sigma(n) * D, kx = swz_k(sigma(n));
-    const int vrow0 = n * BN, vx = swz_v(n);
-
-    auto qk = [&](int st, f32x16 (&S)[BN / 32]) {       // S^T = K Q^T of one tile
-#pragma unroll
-        for (int kt = 0; kt < BN / 32; ++kt) {
-            S[kt] = f32x16{0};
-            const bf16 *kbase = &sK[st][krow0 + 32 * kt * D];
-#pragma unroll
+        // ---- queries of this wave: row = 32*wave + n -> (token, head)
+        const int row = 32 * wave + n;
+        const bool row_ok = row < nrows;
+        const int tq = row / G, g = row % G;
+        const int pq = p0 + tq;                    // this lane's query position
+        const int lowq = is_local ? pq - W : INT32_MIN;   // visible iff lowq < pos <= pq
+        bf16x8 qf[DK];
+        {
+            const bf16 *qrow = P.q + ((int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g) * D;
+    #pragma unroll
             for (int s = 0; s < DK; ++s) {
-                const bf16x8 a = *(const bf16x8 *)(kbase + ((2 * s + h) ^ kx) * 8);
-                S[kt] = mfma32x32x16(a, qf[s], S[kt]);
+                u32x4 v = {0, 0, 0, 0};
+                if (row_ok) v = *(const u32x4 *)(qrow + 16 * s + 8 * h);
+                qf[s] = u4_as_bf16x8(v);
             }
         }
-    };
-    auto mask = [&](int st, f32x16 (&S)[BN / 32]) {     // bounds of a boundary tile
-#pragma unroll
-        for (int kt = 0; kt < BN / 32; ++kt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int kpos = sPos[st][32 * kt + 16 * (v >> 3) + 8 * h + (v & 7)];
-                S[kt][v] = (kpos <= pq && kpos > lowq) ? S[kt][v] : -INFINITY;
-            }
-    };
-    // Online softmax with a lazily moved reference max (log2 domain, raw scores
-    // times c = scale*log2 e): the reference only moves when a row's max exceeds
-    // it by more than kLazy, so weights stay <= 2^kLazy (harmless in fp32 and
-    // bf16) and the rescale of the accumulators becomes rare.  The final
-    // normalisation by l makes the result independent of the reference.
-    constexpr float kLazy = 8.f;
-    const float cl = P.scale_log2;
-    auto update_max = [&](f32x16 (&S)[BN / 32]) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < BN / 32; ++kt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[kt][v]);
-        mx = fmaxf(mx, xor_lane(mx, 32)) * cl;
-        if (__any(mx > m_run + kLazy)) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-            m_run = m_new;
-        }
-    };
-    // weights of one tile -> packed bf16 P^T operands (exponents <= kLazy;
-    // v_exp_f32 flushes results below 2^-126 to zero, which is harmless)
-    auto softmax = [&](f32x16 (&S)[BN / 32], u32x4 (&Pk)[BN / 16]) {
-        const float off = m_run == -INFINITY ? 0.f : -m_run;
-        float rs = 0.f;
-#pragma unroll
-        for (int s2 = 0; s2 < BN / 16; ++s2) {
-            const int kt = s2 >> 1, u = s2 & 1;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(S[kt][8 * u + 2 * w], cl, off));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(S[kt][8 * u + 2 * w + 1], cl, off));
-                rs += p0 + p1;
-                Pk[s2][w] = pack_bf16x2(p0, p1);
-            }
-        }
-        l_run += rs;
-    };
-    auto pv = [&](int st, const u32x4 (&Pk)[BN / 16]) {   // O^T += V^T P^T, 16 keys per step
-#pragma unroll
-        for (int s2 = 0; s2 < BN / 16; ++s2) {
-            const bf16x8 pb = u4_as_bf16x8(Pk[s2]);
-            const int vc = ((2 * s2 + h) ^ vx) * 8;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const bf16x8 a = *(const bf16x8 *)&sV[st][vrow0 + 32 * dt * BN + vc];
-                acc[dt] = mfma32x32x16(a, pb, acc[dt]);
-            }
-        }
-    };
-    auto wait_first_tile = [&]() {        // the prologue issued tiles 0 .. min(2, n_tiles-1)
-        const int after = min(NBUF - 2, n_tiles - 1);
-        if (after >= 2) wait_vmcnt<2 * IPW>();
-        else if (after == 1) wait_vmcnt<IPW>();
-        else wait_vmcnt<0>();
-    };
+        wait_vmcnt<0>();   // queries in registers before the tile loads start
 
-    // ---- ring pipeline.  Tiles t and t+1 are resident, t+2 is in flight.
-    // Iteration t: the QK^T of tile t+1 runs on the matrix cores interleaved
-    // with the softmax of tile t on the vector ALUs, then P.V of tile t.
-    static_assert(NBUF == 4, "the pipeline keeps two tiles resident and two in flight");
-    if (n_tiles > 0) {
-        load_entry_block(0);
-        wait_vmcnt<0>();
-        lds_barrier();
-        load_entry_block(1);
-    }
-#pragma unroll
-    for (int j = 0; j < NBUF - 1; ++j)
-        if (j < n_tiles) issue(j, j);
-    f32x16 Sc[BN / 32];
-    if (n_tiles > 0) {
-        wait_first_tile();
-        lds_barrier();
-        if (fix_mask & 1) {
-            fixup(0);
-            lds_barrier();
-        }
-        qk(0, Sc);
-    }
-    for (int t = 0; t < n_tiles; ++t) {
-        const int st = t % NBUF, st1 = (t + 1) % NBUF;
-        const bool has1 = t + 1 < n_tiles;
-        if (has1) {                          // tiles issued after t+1: at most one
-            if (t + 2 < n_tiles) wait_vmcnt<IPW>();
+        // ---- tile issue: entries (workgroup-uniform, scalar loads), bounds flags,
+        // key positions, and the global->LDS loads of K and V^T
+        // Page entries stream through LDS too: 64 entries (one 1 KB load by wave 0)
+        // per block, block b+1 requested when block b is first used, so the entry
+        // loads ride in the same in-order stream as the tiles and are covered by
+        // the same waits.  Lanes past the row's end re-read its last entry.
+        auto load_entry_block = [&](int k) {
+            if (wave == 0 && 64 * k < my_hi - my_lo) {
+                const int idx = min(my_lo + 64 * k + lane, e_end - 1);
+                SP_LDS_DMA16(E + idx, &sEnt[k & 1][0]);
+            }
+        };
+        auto fetch_entries = [&](int t, TileEntries &te) {
+            const int i0 = t * ppt;                              // entry index within the split
+            const int4 *blk = &sEnt[(i0 >> 6) & 1][i0 & 63];
+            auto get = [&](int pg) {
+                int4 en = int4{0, 0, 0, 0};
+                if (pg < ppt && my_lo + i0 + pg < my_hi) {
+                    const int4 v = blk[pg];
+                    en = int4{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                              __builtin_amdgcn_readfirstlane(v.z), 0};
+                    if (en.x < 0 || en.x >= P.n_phys) en = int4{0, 0, 0, 0};
+                    en.z = min(en.z, PS);
+                }
+                return en;
+            };
+            te.a = get(0);
+            te.b = get(1);
+            te.c = get(2);
+            te.d = get(3);
+        };
+        unsigned full_mask = 0, fix_mask = 0;     // per ring stage: no bounds needed / V chunks to trim
+        auto issue = [&](int t, int st) {
+            const int i0 = t * ppt;
+            if (i0 > 0 && (i0 & 63) == 0) load_entry_block((i0 >> 6) + 1);   // before this tile's loads
+            TileEntries te;
+            fetch_entries(t, te);
+            const int4 x[4] = {te.a, te.b, te.c, te.d};
+            bool full = true, fix = false;
+            int kmin = INT32_MAX, kmax = INT32_MIN;
+    #pragma unroll
+            for (int pg = 0; pg < 4; ++pg)
+                if (pg < ppt) {
+                    full = full && x[pg].z == PS;
+                    fix = fix || (x[pg].z & 7) != 0;
+                    kmin = min(kmin, x[pg].y);
+                    kmax = max(kmax, x[pg].y + x[pg].z - 1);
+                }
+            full = full && kmax <= p0 && (!is_local || kmin > p_last - W);
+            const unsigned bit = 1u << st;
+            full_mask = full ? (full_mask | bit) : (full_mask & ~bit);
+            fix_mask = fix ? (fix_mask | bit) : (fix_mask & ~bit);
+            // K: block q of this wave covers rows [4*blk, 4*blk+4) (D = 128) of one page
+    #pragma unroll
+            for (int q = 0; q < KIW; ++q) {
+                const int blk = wave * KIW + q;
+                const int byte = blk * 1024 + lane * 16;
+                const int kr = byte / (2 * D), pc = (byte % (2 * D)) / 16;
+                const int c = pc ^ swz_k(kr);
+                const int4 en = te.pick(__builtin_amdgcn_readfirstlane(kr / PS));
+                const int tk = kr % PS;
+                const bf16 *src = P.kp + (int64_t)en.x * (PS * D) + tk * D + 8 * c;
+                SP_LDS_DMA16(src, &sK[st][blk * 512]);
+            }
+            // V^T: block q covers dims [8*blk, 8*blk+8); lane -> (dim, 8 consecutive keys)
+    #pragma unroll
+            for (int q = 0; q < VIW; ++q) {
+                const int blk = wave * VIW + q;
+                const int d = blk * 8 + (lane >> 3), pc = lane & 7;
+                const int c = pc ^ swz_v(d);
+                const int key = 8 * c;
+                const int4 en = te.pick(key / PS);
+                const int k8 = key % PS;
+                const bf16 *src = en.z - k8 > 0 ? P.vp + ((int64_t)en.x * D + d) * PS + k8 : P.zero16;
+                SP_LDS_DMA16(src, &sV[st][blk * 512]);
+            }
+            if (tid < BN) {
+                const int4 en = te.pick(tid / PS);
+                const int tk = tid % PS;
+                sPos[st][tid] = tk < en.z ? en.y + tk : kPosInvalid;
+            }
+        };
+        // zero the keys past n_valid inside partially filled 8-key chunks of V^T
+        auto fixup = [&](int st) {
+            for (int idx = tid; idx < D * 8; idx += NW * 64) {
+                const int d = idx >> 3, pc = idx & 7;
+                const int key = 8 * (pc ^ swz_v(d));
+                const int kp = sPos[st][key];                 // position of the chunk's first key
+                int keep = 0;
+    #pragma unroll
+                for (int i = 0; i < 8; ++i) keep += sPos[st][key + i] != kPosInvalid;
+                if (kp != kPosInvalid && keep < 8) {
+                    u32x4 *cell = (u32x4 *)&sV[st][d * BN + pc * 8];
+                    *cell = keep_first_bf16(*cell, keep);
+                }
+            }
+        };
+
+        // ---- running softmax state (log2 domain) and O^T accumulators
+        float m_run = -INFINITY, l_run = 0.f;
+        f32x16 acc[DT];
+    #pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{0};
+
+        // per-lane LDS read offsets (bf16 elements); the swizzle of an operand row
+        // does not depend on which 32-row tile it sits in
+        const int krow0 = sigma(n) * D, kx = swz_k(sigma(n));
+        const int vrow0 = n * BN, vx = swz_v(n);
+
+        auto qk = [&](int st, f32x16 (&S)[BN / 32]) {       // S^T = K Q^T of one tile
+    #pragma unroll
+            for (int kt = 0; kt < BN / 32; ++kt) {
+                S[kt] = f32x16{0};
+                const bf16 *kbase = &sK[st][krow0 + 32 * kt * D];
+    #pragma unroll
+                for (int s = 0; s < DK; ++s) {
+                    const bf16x8 a = *(const bf16x8 *)(kbase + ((2 * s + h) ^ kx) * 8);
+                    S[kt] = mfma32x32x16(a, qf[s], S[kt]);
+                }
+            }
+        };
+        auto mask = [&](int st, f32x16 (&S)[BN / 32]) {     // bounds of a boundary tile
+    #pragma unroll
+            for (int kt = 0; kt < BN / 32; ++kt)
+    #pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int kpos = sPos[st][32 * kt + 16 * (v >> 3) + 8 * h + (v & 7)];
+                    S[kt][v] = (kpos <= pq && kpos > lowq) ? S[kt][v] : -INFINITY;
+                }
+        };
+        // Online softmax with a lazily moved reference max (log2 domain, raw scores
+        // times c = scale*log2 e): the reference only moves when a row's max exceeds
+        // it by more than kLazy, so weights stay <= 2^kLazy (harmless in fp32 and
+        // bf16) and the rescale of the accumulators becomes rare.  The final
+        // normalisation by l makes the result independent of the reference.
+        constexpr float kLazy = 8.f;
+        const float cl = P.scale_log2;
+        auto update_max = [&](f32x16 (&S)[BN / 32]) {
+            float mx = -INFINITY;
+    #pragma unroll
+            for (int kt = 0; kt < BN / 32; ++kt)
+    #pragma unroll
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[kt][v]);
+            mx = fmaxf(mx, xor_lane(mx, 32)) * cl;
+            if (__any(mx > m_run + kLazy)) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+    #pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+                m_run = m_new;
+            }
+        };
+        // weights of one tile -> packed bf16 P^T operands (exponents <= kLazy;
+        // v_exp_f32 flushes results below 2^-126 to zero, which is harmless)
+        auto softmax = [&](f32x16 (&S)[BN / 32], u32x4 (&Pk)[BN / 16]) {
+            const float off = m_run == -INFINITY ? 0.f : -m_run;
+            float rs = 0.f;
+    #pragma unroll
+            for (int s2 = 0; s2 < BN / 16; ++s2) {
+                const int kt = s2 >> 1, u = s2 & 1;
+    #pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(S[kt][8 * u + 2 * w], cl, off));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(S[kt][8 * u + 2 * w + 1], cl, off));
+                    rs += p0 + p1;
+                    Pk[s2][w] = pack_bf16x2(p0, p1);
+                }
+            }
+            l_run += rs;
+        };
+        auto pv = [&](int st, const u32x4 (&Pk)[BN / 16]) {   // O^T += V^T P^T, 16 keys per step
+    #pragma unroll
+            for (int s2 = 0; s2 < BN / 16; ++s2) {
+                const bf16x8 pb = u4_as_bf16x8(Pk[s2]);
+                const int vc = ((2 * s2 + h) ^ vx) * 8;
+    #pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const bf16x8 a = *(const bf16x8 *)&sV[st][vrow0 + 32 * dt * BN + vc];
+                    acc[dt] = mfma32x32x16(a, pb, acc[dt]);
+                }
+            }
+        };
+        auto wait_first_tile = [&]() {        // the prologue issued tiles 0 .. min(2, n_tiles-1)
+            const int after = min(NBUF - 2, n_tiles - 1);
+            if (after >= 2) wait_vmcnt<2 * IPW>();
+            else if (after == 1) wait_vmcnt<IPW>();
             else wait_vmcnt<0>();
-        }
-        lds_barrier();                       // tile t+1 visible; stage of tile t-1 free
-        if (has1 && ((fix_mask >> st1) & 1)) fixup(st1);   // visible after the next barrier
-        if (t + NBUF - 1 < n_tiles) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF);
-        if (!((full_mask >> st) & 1)) mask(st, Sc);
-        update_max(Sc);
-        f32x16 Sn[BN / 32];
-        u32x4 Pk[BN / 16];
-        qk(st1, Sn);                         // past the last tile this reads a stale stage; unused
-        softmax(Sc, Pk);
-        pv(st, Pk);
-        // Schedule of this block: the MFMAs of QK^T(t+1) interleaved with the
-        // exponentials and packing of tile t (vector ALU, incl. transcendental),
-        // then the MFMAs of P.V(t); operand reads run two MFMAs ahead.
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                 // LDS read
-#pragma unroll
-        for (int i = 0; i < 2 * DK; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);             // VALU + transcendental
-        }
-#pragma unroll
-        for (int i = 0; i < (BN / 16) * DT; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);
-        }
-#pragma unroll
-        for (int kt = 0; kt < BN / 32; ++kt) Sc[kt] = Sn[kt];
-    }
+        };
 
-    // ---- epilogue
-    const float l = l_run + xor_lane(l_run, 32);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const float lse = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
-    if (!row_ok) return;
-    if (ns == 1) {
-        bf16 *orow = P.out + ((int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g) * D;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = 32 * dt + 8 * q4 + 4 * h;
-                u32x2 w;
-                w[0] = pack_bf16x2(acc[dt][4 * q4 + 0] * inv, acc[dt][4 * q4 + 1] * inv);
-                w[1] = pack_bf16x2(acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv);
-                *(u32x2 *)(orow + d) = w;
+        // ---- ring pipeline.  Tiles t and t+1 are resident, t+2 is in flight.
+        // Iteration t: the QK^T of tile t+1 runs on the matrix cores interleaved
+        // with the softmax of tile t on the vector ALUs, then P.V of tile t.
+        static_assert(NBUF == 4, "the pipeline keeps two tiles resident and two in flight");
+        if (n_tiles > 0) {
+            load_entry_block(0);
+            wait_vmcnt<0>();
+            lds_barrier();
+            load_entry_block(1);
+        }
+    #pragma unroll
+        for (int j = 0; j < NBUF - 1; ++j)
+            if (j < n_tiles) issue(j, j);
+        f32x16 Sc[BN / 32];
+        if (n_tiles > 0) {
+            wait_first_tile();
+            lds_barrier();
+            if (fix_mask & 1) {
+                fixup(0);
+                lds_barrier();
             }
-        if (P.lse && h == 0) P.lse[(int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g] = lse;
-    } else {
-        const int64_t part = (int64_t)P.part_ptr[r] + local;
-        float *po = P.part_o + (part * BM + row) * D;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = 32 * dt + 8 * q4 + 4 * h;
-                *(float4 *)(po + d) = make_float4(acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv,
-                                                  acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv);
+            qk(0, Sc);
+        }
+        for (int t = 0; t < n_tiles; ++t) {
+            const int st = t % NBUF, st1 = (t + 1) % NBUF;
+            const bool has1 = t + 1 < n_tiles;
+            if (has1) {                          // tiles issued after t+1: at most one
+                if (t + 2 < n_tiles) wait_vmcnt<IPW>();
+                else wait_vmcnt<0>();
             }
-        if (h == 0) P.part_lse[part * BM + row] = lse;
-    }
+            lds_barrier();                       // tile t+1 visible; stage of tile t-1 free
+            if (has1 && ((fix_mask >> st1) & 1)) fixup(st1);   // visible after the next barrier
+            if (t + NBUF - 1 < n_tiles) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF);
+            if (!((full_mask >> st) & 1)) mask(st, Sc);
+            update_max(Sc);
+            f32x16 Sn[BN / 32];
+            u32x4 Pk[BN / 16];
+            qk(st1, Sn);                         // past the last tile this reads a stale stage; unused
+            softmax(Sc, Pk);
+            pv(st, Pk);
+            // Schedule of this block: the MFMAs of QK^T(t+1) interleaved with the
+            // exponentials and packing of tile t (vector ALU, incl. transcendental),
+            // then the MFMAs of P.V(t); operand reads run two MFMAs ahead.
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                 // LDS read
+    #pragma unroll
+            for (int i = 0; i < 2 * DK; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);             // VALU + transcendental
+            }
+    #pragma unroll
+            for (int i = 0; i < (BN / 16) * DT; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);
+            }
+    #pragma unroll
+            for (int kt = 0; kt < BN / 32; ++kt) Sc[kt] = Sn[kt];
+        }
+
+        // ---- epilogue
+        const float l = l_run + xor_lane(l_run, 32);
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const float lse = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+        if (!row_ok) continue;
+        if (ns == 1) {
+            bf16 *orow = P.out + ((int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g) * D;
+    #pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+    #pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int d = 32 * dt + 8 * q4 + 4 * h;
+                    u32x2 w;
+                    w[0] = pack_bf16x2(acc[dt][4 * q4 + 0] * inv, acc[dt][4 * q4 + 1] * inv);
+                    w[1] = pack_bf16x2(acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv);
+                    *(u32x2 *)(orow + d) = w;
+                }
+            if (P.lse && h == 0) P.lse[(int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g] = lse;
+        } else {
+            const int64_t part = (int64_t)P.part_ptr[r] + local;
+            float *po = P.part_o + (part * BM + row) * D;
+    #pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+    #pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int d = 32 * dt + 8 * q4 + 4 * h;
+                    *(float4 *)(po + d) = make_float4(acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv,
+                                                      acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv);
+                }
+            if (h == 0) P.part_lse[part * BM + row] = lse;
+        }
+    }   // work items
 }
 
 // Combines the kv splits of every split q-tile: O = sum_s e^{lse_s-M} o_s / sum_s e^{lse_s-M}.
@@ -443,12 +457,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 template <int D>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, int BM) {
     __shared__ float sw[4][kMaxSplits];
-    const int b = blockIdx.x;
-    const int r = find_row(P.item_ptr, P.n_rows, b);
+    int r, local;
+    item_of(P.item_ptr, P.item_ptr2, P.n_rows, blockIdx.x, &r, &local);
     const int ns = P.nsplit[r];
     if (ns == 1) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int local = b - P.item_ptr[r];
     const int qt = local / ns, sp_i = local % ns;
     const int seq = r % P.n_seq, slot = r / P.n_seq;
     const int tok_base = P.tok_ptr[seq];
@@ -505,50 +518,61 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, int
 }
 
 // Writes the work-item prefix sums of the launch plan into the workspace; one
-// workgroup, the same integer formulas as the host plan (row_items).
+// workgroup, the same integer formulas as the host plan (row_items).  Items of
+// split rows are numbered first (item_ptr), those of unsplit rows after them
+// (item_ptr2, counted from zero; see item_of).
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ row_ptr,
                                                    const int32_t *__restrict__ tok_ptr, int n_seq, int n_rows,
-                                                   int tpt, int chunk, int32_t *item_ptr, int32_t *part_ptr,
-                                                   int32_t *nsplit, int32_t *zero) {
-    __shared__ int s_items[256], s_parts[256];
-    __shared__ int carry_i, carry_p;
+                                                   int tpt, int chunk, int32_t *item_ptr, int32_t *item_ptr2,
+                                                   int32_t *part_ptr, int32_t *nsplit, int32_t *zero) {
+    __shared__ int s_l[256], s_s[256], s_p[256];
+    __shared__ int carry_l, carry_s, carry_p;
     if (threadIdx.x < 64) zero[threadIdx.x] = 0;
-    if (threadIdx.x == 0) { carry_i = 0; carry_p = 0; }
+    if (threadIdx.x == 0) { carry_l = 0; carry_s = 0; carry_p = 0; }
     __syncthreads();
     for (int base = 0; base < n_rows; base += 256) {
         const int r = base + threadIdx.x;
-        int it = 0, pt = 0;
+        int il = 0, is = 0, pt = 0;
         if (r < n_rows) {
             int nq = 1;
             if (tok_ptr) {
                 const int q = r % n_seq;
                 nq = (tok_ptr[q + 1] - tok_ptr[q] + tpt - 1) / tpt;
             }
-            int ns;
+            int ns, it;
             row_items(row_ptr[r + 1] - row_ptr[r], nq, chunk, &ns, &it);
             nsplit[r] = ns;
-            pt = ns > 1 ? it : 0;
+            if (ns > 1) { il = it; pt = it; }
+            else is = it;
         }
-        s_items[threadIdx.x] = it;
-        s_parts[threadIdx.x] = pt;
+        s_l[threadIdx.x] = il;
+        s_s[threadIdx.x] = is;
+        s_p[threadIdx.x] = pt;
         __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {   // inclusive scan
-            const int a = threadIdx.x >= off ? s_items[threadIdx.x - off] : 0;
-            const int c = threadIdx.x >= off ? s_parts[threadIdx.x - off] : 0;
+        for (int off = 1; off < 256; off <<= 1) {   // inclusive scans
+            const int x = threadIdx.x >= off ? s_l[threadIdx.x - off] : 0;
+            const int y = threadIdx.x >= off ? s_s[threadIdx.x - off] : 0;
+            const int z = threadIdx.x >= off ? s_p[threadIdx.x - off] : 0;
             __syncthreads();
-            s_items[threadIdx.x] += a;
-            s_parts[threadIdx.x] += c;
+            s_l[threadIdx.x] += x;
+            s_s[threadIdx.x] += y;
+            s_p[threadIdx.x] += z;
             __syncthreads();
         }
         if (r < n_rows) {
-            item_ptr[r] = carry_i + s_items[threadIdx.x] - it;
-            part_ptr[r] = carry_p + s_parts[threadIdx.x] - pt;
+            item_ptr[r] = carry_l + s_l[threadIdx.x] - il;
+            item_ptr2[r] = carry_s + s_s[threadIdx.x] - is;
+            part_ptr[r] = carry_p + s_p[threadIdx.x] - pt;
         }
         __syncthreads();
-        if (threadIdx.x == 255) { carry_i += s_items[255]; carry_p += s_parts[255]; }
+        if (threadIdx.x == 255) { carry_l += s_l[255]; carry_s += s_s[255]; carry_p += s_p[255]; }
         __syncthreads();
     }
-    if (threadIdx.x == 0) { item_ptr[n_rows] = carry_i; part_ptr[n_rows] = carry_p; }
+    if (threadIdx.x == 0) {
+        item_ptr[n_rows] = carry_l;
+        item_ptr2[n_rows] = carry_s;
+        part_ptr[n_rows] = carry_p;
+    }
 }
 
 }  // namespace
@@ -558,7 +582,7 @@ int launch_plan(const Plan &p, const int32_t *d_row_ptr, const int32_t *d_tok_pt
     char *w = (char *)ws;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, d_row_ptr, d_tok_ptr, n_seq, p.n_rows,
                        p.tok_per_tile, p.chunk_pages, (int32_t *)(w + p.off_item_ptr),
-                       (int32_t *)(w + p.off_part_ptr), (int32_t *)(w + p.off_nsplit), (int32_t *)(w + p.off_zero));
+                       (int32_t *)(w + p.off_item_ptr2), (int32_t *)(w + p.off_part_ptr), (int32_t *)(w + p.off_nsplit), (int32_t *)(w + p.off_zero));
     return check_hip(hipGetLastError(), "plan launch");
 }
 
@@ -582,6 +606,7 @@ int launch_prefill(const AttnArgs &a, const Plan &p, int64_t n_tok, hipStream_t 
     P.row_ptr = a.d_row_ptr;
     P.entries = (const int4 *)a.d_entries;
     P.item_ptr = (const int32_t *)(w + p.off_item_ptr);
+    P.item_ptr2 = (const int32_t *)(w + p.off_item_ptr2);
     P.part_ptr = (const int32_t *)(w + p.off_part_ptr);
     P.nsplit = (const int32_t *)(w + p.off_nsplit);
     P.part_o = (float *)(w + p.off_part_o);
@@ -595,10 +620,13 @@ int launch_prefill(const AttnArgs &a, const Plan &p, int64_t n_tok, hipStream_t 
     P.n_phys = a.n_phys;
     P.scale_log2 = a.scale * kLog2e;
     P.zero16 = (const bf16 *)(w + p.off_zero);
+    P.work_ctr = (int *)(w + p.off_zero + 128);
+    P.n_items = (int)p.n_items;
     const dim3 grid((unsigned)p.n_items);
+    const dim3 grid_persist((unsigned)std::min<int64_t>(p.n_items, kPlanCUs));
 #define SP_PREFILL_CASE(DD, PSV)                                                                        \
     if (a.head_dim == DD && a.page_size == PSV) {                                                       \
-        hipLaunchKernelGGL((prefill_bf16_kernel<DD, 8, PSV, 4>), grid, dim3(512), 0, stream, P);       \
+        hipLaunchKernelGGL((prefill_bf16_kernel<DD, 8, PSV, 4>), grid_persist, dim3(512), 0, stream, P); \
         if (p.n_parts)                                                                                  \
             hipLaunchKernelGGL(prefill_merge_kernel<DD>, grid, dim3(256), 0, stream, P, p.rows_per_tile); \
     }

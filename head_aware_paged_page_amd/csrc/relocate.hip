@@ -8,18 +8,20 @@
 // delta * w_i.  The angle is formed and reduced modulo 2*pi in fp64, its
 // sine/cosine taken in fp64 and the rotation applied in fp32.
 //
-// HBM-bound streaming: a workgroup takes a run of 16 list items (staged in
-// LDS) and builds their (cos, sin) table in LDS once - D/2 angles per page,
-// while its first loads are in flight - then every thread rotates units of 8
-// consecutive pairs of one key row (16 B + 16 B for bf16), four units with
-// their loads in flight together.
+// HBM-bound streaming: a workgroup takes a run of 8 list items (staged in LDS)
+// and issues all their loads at once (streaming, non-temporal loads and stores:
+// every byte is touched once; the table builder lists pages in address order,
+// so a run is mostly one contiguous stretch of the pool).  While the loads are
+// in flight it builds one (cos, sin) table of D/2 angles per distinct delta of
+// the run (a sequence has one delta per segment); then every thread rotates
+// units of 8 consecutive pairs of one key row (16 B + 16 B for bf16).
 #include "device_common.hpp"
 
 namespace sp {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPagesPerBlock = 16;
+constexpr int kPagesPerBlock = 8;
 constexpr int kBatch = 4;             // units per thread with loads in flight together
 constexpr int kMaxHalf = 128;         // head_dim / 2
 constexpr double kTwoPiHi = 6.283185307179586232;      // 2*pi rounded to fp64
@@ -30,21 +32,26 @@ template <typename T>
 struct Elem;
 template <>
 struct Elem<float> {
-    struct Raw { float4 lo, hi; };
-    __device__ static Raw load(const float *p) { return Raw{*(const float4 *)p, *(const float4 *)(p + 4)}; }
+    struct Raw { f32x4 lo, hi; };
+    __device__ static Raw load(const float *p) {
+        return Raw{__builtin_nontemporal_load((const f32x4 *)p), __builtin_nontemporal_load((const f32x4 *)(p + 4))};
+    }
     __device__ static void widen(const Raw &r, float *x) {
-        x[0] = r.lo.x; x[1] = r.lo.y; x[2] = r.lo.z; x[3] = r.lo.w;
-        x[4] = r.hi.x; x[5] = r.hi.y; x[6] = r.hi.z; x[7] = r.hi.w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[j] = r.lo[j];
+            x[4 + j] = r.hi[j];
+        }
     }
     __device__ static void store(float *p, const float *x) {
-        *(float4 *)p = make_float4(x[0], x[1], x[2], x[3]);
-        *(float4 *)(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+        __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, (f32x4 *)p);
+        __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, (f32x4 *)(p + 4));
     }
 };
 template <>
 struct Elem<bf16> {
     typedef u32x4 Raw;
-    __device__ static Raw load(const bf16 *p) { return *(const u32x4 *)p; }
+    __device__ static Raw load(const bf16 *p) { return __builtin_nontemporal_load((const u32x4 *)p); }
     __device__ static void widen(const Raw &v, float *x) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -56,7 +63,7 @@ struct Elem<bf16> {
         u32x4 v;
 #pragma unroll
         for (int w = 0; w < 4; ++w) v[w] = pack_bf16x2(x[2 * w], x[2 * w + 1]);
-        *(u32x4 *)p = v;
+        __builtin_nontemporal_store(v, (u32x4 *)p);
     }
 };
 
@@ -69,7 +76,10 @@ __global__ __launch_bounds__(kThreads) void relocate_kernel(const T *__restrict_
     const int ps = PS ? PS : ps_arg;
     const int D = DD ? DD : D_arg;
     __shared__ int4 sL[kPagesPerBlock];
-    __shared__ float2 sCS[kPagesPerBlock][kMaxHalf];   // (cos, sin) of delta * w_i per page
+    __shared__ int sSlot[kPagesPerBlock];               // page -> its delta's table
+    __shared__ int sDelta[kPagesPerBlock];
+    __shared__ int sNd;
+    __shared__ float2 sCS[kPagesPerBlock][kMaxHalf];   // (cos, sin) of delta * w_i per distinct delta
     const int units_per_row = D / 16;            // a unit = 8 pairs of one key row
     const int ig = threadIdx.x % units_per_row;  // fixed for the launch (kThreads % units_per_row == 0)
     const int units_per_page = ps * units_per_row;
@@ -111,18 +121,29 @@ __global__ __launch_bounds__(kThreads) void relocate_kernel(const T *__restrict_
             }
         }
     };
-    issue(threadIdx.x);   // the first loads fly while the angle table is built
+    issue(threadIdx.x);   // the first loads fly while the angle tables are built
 
+    if (threadIdx.x == 0) {   // distinct deltas of the run
+        int nd = 0;
+        for (int pg = 0; pg < pages; ++pg) {
+            int j = 0;
+            while (j < nd && sDelta[j] != sL[pg].y) ++j;
+            if (j == nd) sDelta[nd++] = sL[pg].y;
+            sSlot[pg] = j;
+        }
+        sNd = nd;
+    }
+    __syncthreads();
     // (cos, sin) of delta * w_i, w_i = theta^(-2i/D): angle formed and reduced mod 2*pi in fp64
-    for (int idx = threadIdx.x; idx < pages * half; idx += kThreads) {
-        const int pg = idx / half, i = idx % half;
+    for (int idx = threadIdx.x; idx < sNd * half; idx += kThreads) {
+        const int sl = idx / half, i = idx % half;
         const double w = exp2(-(2.0 * i / D) * log2_theta);
-        const double ang = (double)sL[pg].y * w;
+        const double ang = (double)sDelta[sl] * w;
         const double q = rint(ang * (1.0 / kTwoPiHi));
         const double r = fma(-q, kTwoPiLo, fma(-q, kTwoPiHi, ang));   // |r| <~ pi
         double sd, cd;
         sincos(r, &sd, &cd);
-        sCS[pg][i] = make_float2((float)cd, (float)sd);
+        sCS[sl][i] = make_float2((float)cd, (float)sd);
     }
     __syncthreads();
 
@@ -131,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void relocate_kernel(const T *__restrict_
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             if (!ok[k]) continue;
-            const float2 *cs = &sCS[pl[k]][8 * ig];
+            const float2 *cs = &sCS[sSlot[pl[k]]][8 * ig];
             float a[8], b[8], ya[8], yb[8];
             Elem<T>::widen(ra[k], a);
             Elem<T>::widen(rb[k], b);

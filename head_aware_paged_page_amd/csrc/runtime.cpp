@@ -57,6 +57,7 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
     p.n_rows = n_rows;
     size_t off = 0;
     p.off_item_ptr = off; off += sizeof(int32_t) * (n_rows + 1);
+    p.off_item_ptr2 = off; off += sizeof(int32_t) * (n_rows + 1);
     p.off_part_ptr = off; off += sizeof(int32_t) * (n_rows + 1);
     p.off_nsplit = off;   off += sizeof(int32_t) * n_rows;
     off = align_up(off, 256);
@@ -97,14 +98,64 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
         }
     }
     const int min_chunk = std::max(1, kMinSplitKeys / page_size);
-    const int target = kind == SP_WS_PREFILL ? kTargetItems : kTargetDecodeItems;
-    if (kind == SP_WS_PREFILL && units >= target / 2) {
-        p.chunk_pages = INT_MAX;
+    if (kind == SP_WS_PREFILL) {
+        // One persistent workgroup per CU takes the items long-first.  If the
+        // unsplit work already fills the CUs, nothing is split.  Otherwise the
+        // chunk minimises an estimate of the makespan (in 64-key tiles, each
+        // item paying a fixed setup): the long items (of split rows) run side
+        // by side, and the short ones share the CUs that the long ones leave
+        // free (list-scheduling bound: total / CUs + largest), spilling onto
+        // all CUs once the long items end.
+        if (units >= kPlanCUs) {
+            p.chunk_pages = INT_MAX;
+        } else {
+            const int ppt = std::max(1, kPrefillKeysPerTile / page_size);
+            auto cost = [&](int64_t pages) { return (double)((pages + ppt - 1) / ppt + kPrefillSetupTiles); };
+            int e_max = 1;
+            for (int r = 0; r < n_rows; ++r) e_max = std::max(e_max, h_row_ptr[r + 1] - h_row_ptr[r]);
+            double best = 0;
+            int best_c = INT_MAX;
+            for (int k = 1; k <= kMaxSplits; ++k) {
+                const int c = (e_max + k - 1) / k;
+                if (c < min_chunk) break;
+                if (k > 1 && c == (e_max + k - 2) / (k - 1)) continue;   // same chunk as k-1
+                int64_t n_long = 0;
+                double L = 0, s_tot = 0, s_max = 0;
+                for (int r = 0; r < n_rows; ++r) {
+                    const int q = r % n_seq;
+                    const int nq = (h_tok_ptr[q + 1] - h_tok_ptr[q] + p.tok_per_tile - 1) / p.tok_per_tile;
+                    int ns, it;
+                    const int e = h_row_ptr[r + 1] - h_row_ptr[r];
+                    row_items(e, nq, c, &ns, &it);
+                    if (ns > 1) {
+                        n_long += it;
+                        L = std::max(L, cost((e + ns - 1) / ns));
+                    } else if (nq > 0) {
+                        s_tot += nq * cost(e);
+                        s_max = std::max(s_max, cost(e));
+                    }
+                }
+                double est;
+                if (n_long >= kPlanCUs) {
+                    est = (double)((n_long + kPlanCUs - 1) / kPlanCUs) * L + s_tot / kPlanCUs;
+                } else {
+                    const double free_cus = (double)(kPlanCUs - n_long);
+                    double sh = s_tot > 0 ? s_tot / free_cus + s_max : 0;
+                    if (sh > L && L > 0) sh = L + (s_tot - free_cus * L) / kPlanCUs + s_max;
+                    est = std::max(L, sh);
+                }
+                if (best_c == INT_MAX || est < best) {
+                    best = est;
+                    best_c = c;
+                }
+                if (n_long > 2 * kPlanCUs) break;                    // finer chunks only add rounds
+            }
+            p.chunk_pages = best_c;
+        }
     } else {
-        const int64_t c = (work + target - 1) / target;
-        p.chunk_pages = (int)std::min<int64_t>(INT_MAX, std::max<int64_t>(min_chunk, c));
+        const int64_t c = (work + kTargetDecodeItems - 1) / kTargetDecodeItems;
+        p.chunk_pages = (int)std::min<int64_t>(kDecodeMaxChunk, std::max<int64_t>(min_chunk, c));
     }
-    if (kind == SP_WS_DECODE) p.chunk_pages = std::min(p.chunk_pages, kDecodeMaxChunk);
     int64_t items = 0, parts = 0;
     for (int r = 0; r < n_rows; ++r) {
         int nq = 1;

@@ -76,6 +76,25 @@ void walk_row(int cls, int window, const sp_segment *segs, int n_segs, const Seq
 
 }  // namespace
 
+// Sorts relocation items by physical page (ids are distinct).  Dense pools
+// (ids below 8x the item count) take one bucket pass, others a comparison sort.
+static void sort_by_phys(sp_reloc *rl, int64_t n) {
+    if (n < 2) return;
+    int32_t mx = 0;
+    for (int64_t i = 0; i < n; ++i) mx = std::max(mx, rl[i].phys);
+    if ((int64_t)mx < 8 * n + 1024) {
+        std::vector<int64_t> at((size_t)mx + 1, -1);
+        for (int64_t i = 0; i < n; ++i) at[rl[i].phys] = i;
+        std::vector<sp_reloc> out;
+        out.reserve((size_t)n);
+        for (int32_t p = 0; p <= mx; ++p)
+            if (at[p] >= 0) out.push_back(rl[at[p]]);
+        std::copy(out.begin(), out.end(), rl);
+    } else {
+        std::sort(rl, rl + n, [](const sp_reloc &a, const sp_reloc &b) { return a.phys < b.phys; });
+    }
+}
+
 extern "C" int segpaged_build_tables(int n_seq, const int32_t *seg_ptr, const sp_segment *segs,
                                      const int32_t *n_new, const int32_t *q_lo, const int32_t *q_hi,
                                      int n_slot, const int32_t *cls, const int32_t *window,
@@ -213,7 +232,9 @@ extern "C" int segpaged_build_tables(int n_seq, const int32_t *seg_ptr, const sp
     }
     std::memcpy(storage, free_list, sizeof(int32_t) * (size_t)total_pages);
 
-    // ---- relocation list
+    // ---- relocation list, ascending physical page: the relocation then sweeps
+    // the pool in address order instead of gathering pages scattered by the
+    // free list (items are independent, so their order is free)
     int64_t k = 0;
     for (int r = 0; r < n_rows; ++r) {
         const int q = r % n_seq;
@@ -225,6 +246,7 @@ extern "C" int segpaged_build_tables(int n_seq, const int32_t *seg_ptr, const sp
                 reloc[k++] = sp_reloc{storage[ci++], delta, (int32_t)std::min<int64_t>(ps, g.len - j * ps), 0};
         }
     }
+    sort_by_phys(reloc, k);
 
     // ---- tables
     row_ptr[0] = 0;

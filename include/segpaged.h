@@ -137,7 +137,7 @@ typedef struct { int32_t phys, delta, n_valid, reserved; } sp_reloc;
  *   row_ptr[n_rows+1], entries[counts[1]]   the call's table per row: the pages
  *                            holding >= 1 token visible to >= 1 of the call's
  *                            queries, ascending position
- *   reloc[counts[2]]         every stored segment page, allocation order
+ *   reloc[counts[2]]         every stored segment page, ascending phys
  *   counts[3]                (always written) pages, entries, reloc items
  * Errors: SP_EINVAL (bad layout, class, window, list, position overflow,
  * duplicate or negative page id), SP_ENOMEM (n_free < pages needed; a count
