@@ -57,19 +57,7 @@ WORKLOAD_TEXT = {
              "decode per sequence; 55 local (256) / 6 global / 3 retrieval (32 pages)",
     "tiny": "tiny fp32 layer: 4 slots (MHA), head_dim 64, page 16, 2 x 256 segments + 32-token suffix + 1 decode",
 }
-KERNEL_SOURCES = {
-    "rope_relocate": ["relocate.hip"],
-    "segpaged_prefill": ["prefill.hip", "device_common.hpp"],
-    "segpaged_decode": ["decode.hip", "device_common.hpp"],
-}
-
-
-def source_hash(call: str) -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES[call]:
-        with open(os.path.join(ROOT, "head_aware_paged_page_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+from head_aware_paged_page_amd.profiling import source_hash  # noqa: E402
 
 
 def committed_traffic(call: str, workload: str):
