@@ -41,7 +41,7 @@ template <int D>
 struct Block {
     u32x4 k[2][D / 32];   // S^T A operands: [key tile][k-step]
     u32x4 v[D / 16];      // O^T A operands: [dim tile]
-    int pos[2][4];        // position of each of this lane's 8 keys (kPosInvalid if none)
+    int y[2], z[2];       // pos_start / n_valid of the block's (one or two) pages, wave-uniform
 };
 
 // Loads one 32-key block whose table entries sit in LDS at sE[e0 - base ..]
@@ -50,13 +50,19 @@ template <int D, int ps>
 __device__ __forceinline__ void load_block(const DecodeParams &P, const int4 *sE, int e0, int e_hi, Block<D> &B) {
     const int lane = threadIdx.x & 63;
     const int m = lane & 15, grp = lane >> 4;
-    // entries of the block's pages (one or two)
+    // entries of the block's pages (one or two), wave-uniform
     int4 en[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int e = e0 + i;
         en[i] = int4{0, 0, 0, 0};
-        if (i * ps < KB && e < e_hi) en[i] = sE[i];
+        if (i * ps < KB && e < e_hi) {
+            const int4 v = sE[i];
+            en[i] = int4{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                         __builtin_amdgcn_readfirstlane(v.z), 0};
+        }
+        B.y[i] = en[i].y;
+        B.z[i] = en[i].z;
     }
     // K: A operand row m of key tile kt is key 8*(m/4) + 4*kt + m%4; dims 32*s + 8*grp.
     // Slots without a token are read from page 0 and never zeroed: their scores
@@ -71,36 +77,28 @@ __device__ __forceinline__ void load_block(const DecodeParams &P, const int4 *sE
         for (int s = 0; s < D / 32; ++s) B.k[kt][s] = *(const u32x4 *)(src + 32 * s);
     }
     // V^T: A operand row = dim 16*dt + m, keys 8*grp .. 8*grp+7.  Values of empty
-    // slots must be zero (their weight is zero, but 0 * NaN is not); only blocks
-    // that contain such slots pay for the masking.
+    // slots are zeroed when the block is used, not here: the loads must stay in
+    // flight while the previous block computes.
     {
         const int j = 8 * grp;
         const int pg = j / ps, tk = j % ps;
         const int4 e = pg ? en[1] : en[0];
-        const int keep = e.z - tk;
         const bf16 *src = P.vp + ((int64_t)e.x * D + m) * ps + tk;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) B.v[dt] = *(const u32x4 *)(src + (int64_t)16 * dt * ps);
-        if (__any(keep < 8)) {
-#pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt)
-                B.v[dt] = keep >= 8 ? B.v[dt] : (keep > 0 ? keep_first_bf16(B.v[dt], keep) : u32x4{0, 0, 0, 0});
-        }
     }
-    // positions of this lane's score keys: 8*grp + 4*kt + v
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int j = 8 * grp + 4 * kt + v;
-            const int pg = j / ps, tk = j % ps;
-            const int4 e = pg ? en[1] : en[0];
-            B.pos[kt][v] = tk < e.z ? e.y + tk : kPosInvalid;
-        }
+}
+
+// Position of key j (0..31) of a block, kPosInvalid if its slot holds no token.
+template <int ps, int D>
+__device__ __forceinline__ int block_pos(const Block<D> &B, int j) {
+    const int pg = j / ps, tk = j % ps;
+    const int y = pg ? B.y[1] : B.y[0], z = pg ? B.z[1] : B.z[0];
+    return tk < z ? y + tk : kPosInvalid;
 }
 
 template <int D, int PS>
-__global__ __launch_bounds__(NWD * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_bf16_kernel(
+__global__ __launch_bounds__(NWD * 64) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_bf16_kernel(
     DecodeParams P) {
     constexpr int DS = D / 32;   // k-steps of S^T
     constexpr int DT = D / 16;   // dim tiles of O^T
@@ -155,13 +153,9 @@ __global__ __launch_bounds__(NWD * 64) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    Block<D> cur, nxt;
-    int blk = wave;
-    if (blk < n_blocks) load_block<D, PS>(P, sE + blk * ppb, my_lo + blk * ppb, my_hi, cur);
-    for (; blk < n_blocks; blk += NWD) {
-        if (blk + NWD < n_blocks)
-            load_block<D, PS>(P, sE + (blk + NWD) * ppb, my_lo + (blk + NWD) * ppb, my_hi, nxt);
-
+    // One block in registers per wave; latency is hidden across the waves (three
+    // per SIMD) rather than by a second register buffer, which would halve them.
+    auto use = [&](Block<D> &cur) {
         f32x4 S[2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
@@ -174,7 +168,7 @@ __global__ __launch_bounds__(NWD * 64) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int kpos = cur.pos[kt][v];
+                const int kpos = block_pos<PS, D>(cur, 8 * grp + 4 * kt + v);
                 float x = S[kt][v] * P.scale_log2;
                 if (!(kpos <= p && kpos > low)) x = -INFINITY;
                 S[kt][v] = x;
@@ -200,10 +194,23 @@ __global__ __launch_bounds__(NWD * 64) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         l_run = l_run * alpha + rs;
         m_run = m_new;
+        // values of empty slots must be zero (their weight is zero, but 0 * NaN
+        // is not); only blocks that hold such slots pay for it
+        const int keep = (8 * grp / PS ? cur.z[1] : cur.z[0]) - (8 * grp) % PS;
+        if (__any(keep < 8)) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                cur.v[dt] = keep >= 8 ? cur.v[dt] : (keep > 0 ? keep_first_bf16(cur.v[dt], keep) : u32x4{0, 0, 0, 0});
+        }
         const bf16x8 pb = u4_as_bf16x8(pk);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma16x16x32(u4_as_bf16x8(cur.v[dt]), pb, acc[dt] * alpha);
-        cur = nxt;
+    };
+    auto load = [&](int bk, Block<D> &B) { load_block<D, PS>(P, sE + bk * ppb, my_lo + bk * ppb, my_hi, B); };
+    Block<D> blk_regs;
+    for (int blk = wave; blk < n_blocks; blk += NWD) {
+        load(blk, blk_regs);
+        use(blk_regs);
     }
 
     // ---- combine the four waves

@@ -14,8 +14,8 @@
 // K/V tile feeds every head of the slot.  Each wave owns 32 query rows.
 //
 // Per 64-key tile (one to four pages):
-//   K  [64 keys][D]  -> LDS, token-major as stored;
-//   V^T[D][64 keys]  -> LDS, copied straight from the dim-major V pages;
+//   K  [64 keys][D]        -> LDS, token-major as stored;
+//   V^T[page][D][PS keys]  -> LDS, each dim-major V page copied as it is stored;
 //   S^T = K Q^T      (v_mfma_f32_32x32x16_bf16: keys x queries), so every lane
 //                    holds one query's scores and the row softmax needs a single
 //                    cross-lane step;
@@ -43,7 +43,6 @@ struct PrefillParams {
     int n_seq, n_rows, G, ps, tpt, Hq;
     int64_t n_phys;
     float scale_log2;   // softmax_scale * log2(e)
-    const bf16 *zero16;  // 16 zero bytes in the workspace (source for empty V slots)
     int *work_ctr;       // next work item to take; zeroed by the plan kernel
     int n_items;
 };
@@ -90,15 +89,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     constexpr int DK = D / 16;     // k-steps of the QK^T product
     constexpr int DT = D / 32;     // 32-dim tiles of the output
     // Tiles arrive by global->LDS loads of 1 KB per wave instruction (lane l
-    // writes bytes [16 l, 16 l + 16)).  K rows (2D bytes) and V^T rows (2*BN
-    // bytes) are stored with their 16-byte chunks XOR-swizzled by row so that
-    // the MFMA operand reads of 32 rows spread over all LDS banks.
+    // writes bytes [16 l, 16 l + 16)), each block inside one page, so a load's
+    // source is a wave-uniform page base plus a per-lane offset that is the same
+    // for every tile.  K rows (2D bytes) and V^T rows (2*PS bytes, one page's
+    // keys of one dim) hold their 16-byte chunks XOR-swizzled by row so that the
+    // MFMA operand reads of 32 rows spread over all LDS banks; the swizzle is
+    // applied on the source side (lane l fetches the chunk that belongs at l).
     constexpr int KI = BN * D * 2 / 1024, VI = D * BN * 2 / 1024;   // 1 KB blocks per tile
     static_assert(KI % NW == 0 && VI % NW == 0, "tile blocks must split evenly over the waves");
     constexpr int KIW = KI / NW, VIW = VI / NW;                       // per wave and tile
     constexpr int IPW = KIW + VIW;
     constexpr int ppt = BN / PS;                                      // pages per tile
-    static_assert(1024 / (2 * D) <= PS, "a 1 KB block of K rows must stay inside one page");
+    constexpr int CPK = D / 8, RK = 1024 / (2 * D);                   // K: chunks per row, rows per block
+    constexpr int CPV = PS / 8, RV = 1024 / (2 * PS);                 // V^T: chunks per row, rows per block
+    constexpr int BPP = D / RV;                                       // V^T blocks per page
+    static_assert(RK <= PS && PS % RK == 0, "a 1 KB block of K rows must stay inside one page");
+    static_assert(RV <= D && D % RV == 0, "a 1 KB block of V^T rows must stay inside one page");
     __shared__ __attribute__((aligned(1024))) bf16 sK[NBUF][BN * D];
     __shared__ __attribute__((aligned(1024))) bf16 sV[NBUF][D * BN];
     __shared__ int sPos[NBUF][BN];
@@ -109,7 +115,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, h = lane >> 5;
     auto swz_k = [](int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
-    auto swz_v = [](int d) { return (d >> 1) & 7; };
+    auto swz_v = [](int d) { return PS == 16 ? 0 : PS == 32 ? ((d >> 2) & 3) : ((d >> 1) & 7); };
+
+    // Per-lane source offsets (bytes within a page) and page slots of this
+    // wave's K and V^T blocks: fixed for the launch.
+    uint32_t koff[KIW], voff[VIW];
+    int kpg[KIW], vpg[VIW];
+#pragma unroll
+    for (int q = 0; q < KIW; ++q) {
+        const int blk = wave * KIW + q;
+        const int row = blk * RK + lane / CPK;                    // key row of the tile
+        const int c = (lane % CPK) ^ swz_k(row);
+        koff[q] = (uint32_t)(((row % PS) * D + 8 * c) * 2);
+        kpg[q] = __builtin_amdgcn_readfirstlane(blk * RK / PS);
+    }
+#pragma unroll
+    for (int q = 0; q < VIW; ++q) {
+        const int blk = wave * VIW + q;
+        const int d = (blk % BPP) * RV + lane / CPV;              // dim row within the page
+        const int c = (lane % CPV) ^ swz_v(d);
+        voff[q] = (uint32_t)((d * PS + 8 * c) * 2);
+        vpg[q] = __builtin_amdgcn_readfirstlane(blk / BPP);
+    }
 
     // Persistent workgroups (one per CU) take the work items in their long-first
     // order from a counter: the hardware dispatcher places workgroups in order
@@ -179,16 +206,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         };
         auto fetch_entries = [&](int t, TileEntries &te) {
             const int i0 = t * ppt;                              // entry index within the split
-            const int4 *blk = &sEnt[(i0 >> 6) & 1][i0 & 63];
+            const int4 *blk = &sEnt[(i0 >> 6) & 1][i0 & 63];    // ppt divides 64: all inside the block
+            int4 v[4];
+    #pragma unroll
+            for (int pg = 0; pg < 4; ++pg) v[pg] = pg < ppt ? blk[pg] : int4{0, 0, 0, 0};   // one LDS wait
             auto get = [&](int pg) {
-                int4 en = int4{0, 0, 0, 0};
-                if (pg < ppt && my_lo + i0 + pg < my_hi) {
-                    const int4 v = blk[pg];
-                    en = int4{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
-                              __builtin_amdgcn_readfirstlane(v.z), 0};
-                    if (en.x < 0 || en.x >= P.n_phys) en = int4{0, 0, 0, 0};
-                    en.z = min(en.z, PS);
-                }
+                int4 en = int4{__builtin_amdgcn_readfirstlane(v[pg].x), __builtin_amdgcn_readfirstlane(v[pg].y),
+                               __builtin_amdgcn_readfirstlane(v[pg].z), 0};
+                const bool ok = pg < ppt && my_lo + i0 + pg < my_hi && en.x >= 0 && en.x < P.n_phys;
+                en.x = ok ? en.x : 0;
+                en.y = ok ? en.y : 0;
+                en.z = ok ? min(en.z, PS) : 0;
                 return en;
             };
             te.a = get(0);
@@ -209,7 +237,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             for (int pg = 0; pg < 4; ++pg)
                 if (pg < ppt) {
                     full = full && x[pg].z == PS;
-                    fix = fix || (x[pg].z & 7) != 0;
+                    fix = fix || x[pg].z != PS;
                     kmin = min(kmin, x[pg].y);
                     kmax = max(kmax, x[pg].y + x[pg].z - 1);
                 }
@@ -217,29 +245,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             const unsigned bit = 1u << st;
             full_mask = full ? (full_mask | bit) : (full_mask & ~bit);
             fix_mask = fix ? (fix_mask | bit) : (fix_mask & ~bit);
-            // K: block q of this wave covers rows [4*blk, 4*blk+4) (D = 128) of one page
+            // K and V^T blocks of this wave: page base (uniform) + per-lane offset
     #pragma unroll
             for (int q = 0; q < KIW; ++q) {
-                const int blk = wave * KIW + q;
-                const int byte = blk * 1024 + lane * 16;
-                const int kr = byte / (2 * D), pc = (byte % (2 * D)) / 16;
-                const int c = pc ^ swz_k(kr);
-                const int4 en = te.pick(__builtin_amdgcn_readfirstlane(kr / PS));
-                const int tk = kr % PS;
-                const bf16 *src = P.kp + (int64_t)en.x * (PS * D) + tk * D + 8 * c;
-                SP_LDS_DMA16(src, &sK[st][blk * 512]);
+                const int4 en = te.pick(kpg[q]);
+                const char *base = (const char *)(P.kp + (int64_t)en.x * (PS * D));
+                SP_LDS_DMA16((const bf16 *)(base + koff[q]), &sK[st][(wave * KIW + q) * 512]);
             }
-            // V^T: block q covers dims [8*blk, 8*blk+8); lane -> (dim, 8 consecutive keys)
     #pragma unroll
             for (int q = 0; q < VIW; ++q) {
-                const int blk = wave * VIW + q;
-                const int d = blk * 8 + (lane >> 3), pc = lane & 7;
-                const int c = pc ^ swz_v(d);
-                const int key = 8 * c;
-                const int4 en = te.pick(key / PS);
-                const int k8 = key % PS;
-                const bf16 *src = en.z - k8 > 0 ? P.vp + ((int64_t)en.x * D + d) * PS + k8 : P.zero16;
-                SP_LDS_DMA16(src, &sV[st][blk * 512]);
+                const int4 en = te.pick(vpg[q]);
+                const char *base = (const char *)(P.vp + (int64_t)en.x * (D * PS));
+                SP_LDS_DMA16((const bf16 *)(base + voff[q]), &sV[st][(wave * VIW + q) * 512]);
             }
             if (tid < BN) {
                 const int4 en = te.pick(tid / PS);
@@ -247,18 +264,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 sPos[st][tid] = tk < en.z ? en.y + tk : kPosInvalid;
             }
         };
-        // zero the keys past n_valid inside partially filled 8-key chunks of V^T
+        // Zero the V^T slots of keys that hold no token (past a page's n_valid, or
+        // pages past the split): their weight is zero, but 0 * NaN is not.
         auto fixup = [&](int st) {
-            for (int idx = tid; idx < D * 8; idx += NW * 64) {
-                const int d = idx >> 3, pc = idx & 7;
-                const int key = 8 * (pc ^ swz_v(d));
-                const int kp = sPos[st][key];                 // position of the chunk's first key
+            for (int idx = tid; idx < ppt * D * CPV; idx += NW * 64) {
+                const int pg = idx / (D * CPV), rem = idx % (D * CPV);
+                const int d = rem / CPV, cp = rem % CPV;
+                const int key0 = pg * PS + 8 * (cp ^ swz_v(d));     // first key of the cell
                 int keep = 0;
     #pragma unroll
-                for (int i = 0; i < 8; ++i) keep += sPos[st][key + i] != kPosInvalid;
-                if (kp != kPosInvalid && keep < 8) {
-                    u32x4 *cell = (u32x4 *)&sV[st][d * BN + pc * 8];
-                    *cell = keep_first_bf16(*cell, keep);
+                for (int i = 0; i < 8; ++i) keep += sPos[st][key0 + i] != kPosInvalid;
+                if (keep < 8) {
+                    u32x4 *cell = (u32x4 *)&sV[st][pg * D * PS + d * PS + 8 * cp];
+                    *cell = keep > 0 ? keep_first_bf16(*cell, keep) : u32x4{0, 0, 0, 0};
                 }
             }
         };
@@ -272,28 +290,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         // per-lane LDS read offsets (bf16 elements); the swizzle of an operand row
         // does not depend on which 32-row tile it sits in
         const int krow0 = sigma(n) * D, kx = swz_k(sigma(n));
-        const int vrow0 = n * BN, vx = swz_v(n);
+        const int vx = swz_v(n);
 
-        auto qk = [&](int st, f32x16 (&S)[BN / 32]) {       // S^T = K Q^T of one tile
+        // The compute runs in halves of a tile (32 keys): S^T of one half is one
+        // 32x32 MFMA tile per lane group, so the pipeline below keeps just two
+        // of them (the half being exponentiated, the half being scored) and the
+        // operand reads of a whole half in registers ahead of their MFMAs.
+        auto qk = [&](int st, int kt, f32x16 &S) {          // S^T = K Q^T of keys [32 kt, 32 kt + 32)
+            const bf16 *kbase = &sK[st][krow0 + 32 * kt * D];
+            bf16x8 a[DK];
     #pragma unroll
-            for (int kt = 0; kt < BN / 32; ++kt) {
-                S[kt] = f32x16{0};
-                const bf16 *kbase = &sK[st][krow0 + 32 * kt * D];
+            for (int s = 0; s < DK; ++s) a[s] = *(const bf16x8 *)(kbase + ((2 * s + h) ^ kx) * 8);
+            S = f32x16{0};
     #pragma unroll
-                for (int s = 0; s < DK; ++s) {
-                    const bf16x8 a = *(const bf16x8 *)(kbase + ((2 * s + h) ^ kx) * 8);
-                    S[kt] = mfma32x32x16(a, qf[s], S[kt]);
-                }
-            }
+            for (int s = 0; s < DK; ++s) S = mfma32x32x16(a[s], qf[s], S);
         };
-        auto mask = [&](int st, f32x16 (&S)[BN / 32]) {     // bounds of a boundary tile
+        auto mask = [&](int st, int kt, f32x16 &S) {         // bounds of a boundary tile
     #pragma unroll
-            for (int kt = 0; kt < BN / 32; ++kt)
-    #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int kpos = sPos[st][32 * kt + 16 * (v >> 3) + 8 * h + (v & 7)];
-                    S[kt][v] = (kpos <= pq && kpos > lowq) ? S[kt][v] : -INFINITY;
-                }
+            for (int v = 0; v < 16; ++v) {
+                const int kpos = sPos[st][32 * kt + 16 * (v >> 3) + 8 * h + (v & 7)];
+                S[v] = (kpos <= pq && kpos > lowq) ? S[v] : -INFINITY;
+            }
         };
         // Online softmax with a lazily moved reference max (log2 domain, raw scores
         // times c = scale*log2 e): the reference only moves when a row's max exceeds
@@ -302,12 +319,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         // normalisation by l makes the result independent of the reference.
         constexpr float kLazy = 8.f;
         const float cl = P.scale_log2;
-        auto update_max = [&](f32x16 (&S)[BN / 32]) {
+        auto update_max = [&](const f32x16 &S) {
             float mx = -INFINITY;
     #pragma unroll
-            for (int kt = 0; kt < BN / 32; ++kt)
-    #pragma unroll
-                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[kt][v]);
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[v]);
             mx = fmaxf(mx, xor_lane(mx, 32)) * cl;
             if (__any(mx > m_run + kLazy)) {
                 const float m_new = fmaxf(m_run, mx);
@@ -318,35 +333,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 m_run = m_new;
             }
         };
-        // weights of one tile -> packed bf16 P^T operands (exponents <= kLazy;
-        // v_exp_f32 flushes results below 2^-126 to zero, which is harmless)
-        auto softmax = [&](f32x16 (&S)[BN / 32], u32x4 (&Pk)[BN / 16]) {
+        // weights of one half -> packed bf16 P^T operands of its two 16-key steps
+        // (exponents <= kLazy; v_exp_f32 flushes results below 2^-126 to zero)
+        auto softmax = [&](const f32x16 &S, u32x4 (&Pk)[2]) {
             const float off = m_run == -INFINITY ? 0.f : -m_run;
             float rs = 0.f;
     #pragma unroll
-            for (int s2 = 0; s2 < BN / 16; ++s2) {
-                const int kt = s2 >> 1, u = s2 & 1;
+            for (int u = 0; u < 2; ++u)
     #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(S[kt][8 * u + 2 * w], cl, off));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(S[kt][8 * u + 2 * w + 1], cl, off));
-                    rs += p0 + p1;
-                    Pk[s2][w] = pack_bf16x2(p0, p1);
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(S[8 * u + 2 * w], cl, off));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(S[8 * u + 2 * w + 1], cl, off));
+                    Pk[u][w] = pack_bf16x2(p0, p1);
+                    rs = sum_bf16x2(Pk[u][w], rs);   // the row sum of the weights P.V uses
                 }
-            }
             l_run += rs;
         };
-        auto pv = [&](int st, const u32x4 (&Pk)[BN / 16]) {   // O^T += V^T P^T, 16 keys per step
+        auto pv = [&](int st, int kt, const u32x4 (&Pk)[2]) {   // O^T += V^T P^T over keys [32 kt, 32 kt + 32)
+            bf16x8 a[2][DT];
     #pragma unroll
-            for (int s2 = 0; s2 < BN / 16; ++s2) {
-                const bf16x8 pb = u4_as_bf16x8(Pk[s2]);
-                const int vc = ((2 * s2 + h) ^ vx) * 8;
+            for (int u = 0; u < 2; ++u) {
+                const int s2 = 2 * kt + u;
+                const int pg = 16 * s2 / PS, c = (16 * s2 % PS) / 8 + h;
+                const bf16 *vb = &sV[st][pg * D * PS + n * PS + 8 * (c ^ vx)];
     #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const bf16x8 a = *(const bf16x8 *)&sV[st][vrow0 + 32 * dt * BN + vc];
-                    acc[dt] = mfma32x32x16(a, pb, acc[dt]);
-                }
+                for (int dt = 0; dt < DT; ++dt) a[u][dt] = *(const bf16x8 *)(vb + 32 * dt * PS);
             }
+    #pragma unroll
+            for (int u = 0; u < 2; ++u)
+    #pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32x32x16(a[u][dt], u4_as_bf16x8(Pk[u]), acc[dt]);
         };
         auto wait_first_tile = [&]() {        // the prologue issued tiles 0 .. min(2, n_tiles-1)
             const int after = min(NBUF - 2, n_tiles - 1);
@@ -354,10 +370,37 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             else if (after == 1) wait_vmcnt<IPW>();
             else wait_vmcnt<0>();
         };
+        // One half-step: the scores Sc of the current half are masked (boundary
+        // tiles only), exponentiated and multiplied into O while the next half's
+        // scores Sn are formed on the matrix cores.
+        auto half = [&](int st, int kt, bool full, f32x16 &Sc, int st_n, int kt_n, f32x16 &Sn) {
+            if (!full) mask(st, kt, Sc);
+            update_max(Sc);
+            u32x4 Pk[2];
+            qk(st_n, kt_n, Sn);                  // past the last tile this reads a stale stage; unused
+            softmax(Sc, Pk);
+            pv(st, kt, Pk);
+            // Schedule: all operand reads of the next half's QK^T first, then its
+            // MFMAs each followed by a share of the exponentials and packing of
+            // this half, then P.V with its operand reads issued up front.
+            __builtin_amdgcn_sched_group_barrier(0x100, DK, 0);            // LDS reads (K)
+    #pragma unroll
+            for (int i = 0; i < DK; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);         // VALU incl. transcendental
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * DT, 0);        // LDS reads (V^T)
+    #pragma unroll
+            for (int i = 0; i < 2 * DT; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
+            }
+        };
 
-        // ---- ring pipeline.  Tiles t and t+1 are resident, t+2 is in flight.
-        // Iteration t: the QK^T of tile t+1 runs on the matrix cores interleaved
-        // with the softmax of tile t on the vector ALUs, then P.V of tile t.
+        // ---- ring pipeline.  Tiles t and t+1 are resident, t+2 and t+3 in flight.
+        // Iteration t: half 0 of tile t (scoring half 1), then the wait for tile
+        // t+1, the barrier and the issue of tile t+3, then half 1 of tile t
+        // (scoring half 0 of tile t+1).
         static_assert(NBUF == 4, "the pipeline keeps two tiles resident and two in flight");
         if (n_tiles > 0) {
             load_entry_block(0);
@@ -368,7 +411,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     #pragma unroll
         for (int j = 0; j < NBUF - 1; ++j)
             if (j < n_tiles) issue(j, j);
-        f32x16 Sc[BN / 32];
+        f32x16 Sa, Sb;
         if (n_tiles > 0) {
             wait_first_tile();
             lds_barrier();
@@ -376,43 +419,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 fixup(0);
                 lds_barrier();
             }
-            qk(0, Sc);
+            qk(0, 0, Sa);
         }
         for (int t = 0; t < n_tiles; ++t) {
             const int st = t % NBUF, st1 = (t + 1) % NBUF;
             const bool has1 = t + 1 < n_tiles;
+            const bool full = (full_mask >> st) & 1;
+            half(st, 0, full, Sa, st, 1, Sb);
             if (has1) {                          // tiles issued after t+1: at most one
                 if (t + 2 < n_tiles) wait_vmcnt<IPW>();
                 else wait_vmcnt<0>();
             }
             lds_barrier();                       // tile t+1 visible; stage of tile t-1 free
-            if (has1 && ((fix_mask >> st1) & 1)) fixup(st1);   // visible after the next barrier
+            if (has1 && ((fix_mask >> st1) & 1)) {
+                fixup(st1);
+                lds_barrier();
+            }
             if (t + NBUF - 1 < n_tiles) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF);
-            if (!((full_mask >> st) & 1)) mask(st, Sc);
-            update_max(Sc);
-            f32x16 Sn[BN / 32];
-            u32x4 Pk[BN / 16];
-            qk(st1, Sn);                         // past the last tile this reads a stale stage; unused
-            softmax(Sc, Pk);
-            pv(st, Pk);
-            // Schedule of this block: the MFMAs of QK^T(t+1) interleaved with the
-            // exponentials and packing of tile t (vector ALU, incl. transcendental),
-            // then the MFMAs of P.V(t); operand reads run two MFMAs ahead.
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                 // LDS read
-    #pragma unroll
-            for (int i = 0; i < 2 * DK; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);             // VALU + transcendental
-            }
-    #pragma unroll
-            for (int i = 0; i < (BN / 16) * DT; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);
-            }
-    #pragma unroll
-            for (int kt = 0; kt < BN / 32; ++kt) Sc[kt] = Sn[kt];
+            half(st, 1, full, Sb, st1, 0, Sa);
         }
 
         // ---- epilogue
@@ -619,7 +643,6 @@ int launch_prefill(const AttnArgs &a, const Plan &p, int64_t n_tok, hipStream_t 
     P.Hq = a.n_slot * a.group;
     P.n_phys = a.n_phys;
     P.scale_log2 = a.scale * kLog2e;
-    P.zero16 = (const bf16 *)(w + p.off_zero);
     P.work_ctr = (int *)(w + p.off_zero + 128);
     P.n_items = (int)p.n_items;
     const dim3 grid((unsigned)p.n_items);
