@@ -47,18 +47,6 @@ struct PrefillParams {
     int n_items;
 };
 
-// Table entries of the (up to four) pages of one 64-key tile, workgroup-uniform.
-// Kept as four named values and selected with compares so that they stay in
-// registers (an array indexed by a lane-varying page would go to scratch).
-struct TileEntries {
-    int4 a, b, c, d;
-    __device__ __forceinline__ int4 pick(int pg) const {
-        const int4 lo = pg == 0 ? a : b;
-        const int4 hi = pg == 2 ? c : d;
-        return pg < 2 ? lo : hi;
-    }
-};
-
 // Output row m of a 32x32 MFMA tile <- K row sigma(m) of the 32-key block.
 // Lane (n, h) holds rows m = (v/4)*8 + 4h + v%4; sigma maps them to keys
 // 16*(v/8) + 8h + v%8, i.e. it swaps bits 2 and 3 of m.
@@ -108,6 +96,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     __shared__ __attribute__((aligned(1024))) bf16 sK[NBUF][BN * D];
     __shared__ __attribute__((aligned(1024))) bf16 sV[NBUF][D * BN];
     __shared__ int sPos[NBUF][BN];
+    __shared__ int sFlags[NBUF];    // bit 0: no bounds needed; bits 1..ppt: pages with empty key slots
+    __shared__ int sNv[NBUF][4];    // tokens held by each page of the tile
     __shared__ __attribute__((aligned(16))) int4 sEnt[2][64];
 
     __shared__ int s_item;
@@ -204,79 +194,78 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 SP_LDS_DMA16(E + idx, &sEnt[k & 1][0]);
             }
         };
-        auto fetch_entries = [&](int t, TileEntries &te) {
+        // Entry of page pg (0..ppt-1) of tile t, sanitised: pages past the split
+        // or outside the pool read as {phys 0, no tokens}.  `uniform` reads it
+        // into scalar registers (every lane asks for the same page).
+        auto entry = [&](int t, int pg, bool uniform) {
             const int i0 = t * ppt;                              // entry index within the split
-            const int4 *blk = &sEnt[(i0 >> 6) & 1][i0 & 63];    // ppt divides 64: all inside the block
-            int4 v[4];
-    #pragma unroll
-            for (int pg = 0; pg < 4; ++pg) v[pg] = pg < ppt ? blk[pg] : int4{0, 0, 0, 0};   // one LDS wait
-            auto get = [&](int pg) {
-                int4 en = int4{__builtin_amdgcn_readfirstlane(v[pg].x), __builtin_amdgcn_readfirstlane(v[pg].y),
-                               __builtin_amdgcn_readfirstlane(v[pg].z), 0};
-                const bool ok = pg < ppt && my_lo + i0 + pg < my_hi && en.x >= 0 && en.x < P.n_phys;
-                en.x = ok ? en.x : 0;
-                en.y = ok ? en.y : 0;
-                en.z = ok ? min(en.z, PS) : 0;
-                return en;
-            };
-            te.a = get(0);
-            te.b = get(1);
-            te.c = get(2);
-            te.d = get(3);
+            int4 en = sEnt[(i0 >> 6) & 1][(i0 & 63) + pg];       // ppt divides 64: inside the block
+            if (uniform)
+                en = int4{__builtin_amdgcn_readfirstlane(en.x), __builtin_amdgcn_readfirstlane(en.y),
+                          __builtin_amdgcn_readfirstlane(en.z), 0};
+            const bool ok = my_lo + i0 + pg < my_hi && en.x >= 0 && en.x < P.n_phys;
+            return ok ? int4{en.x, en.y, min(en.z, PS), 0} : int4{0, 0, 0, 0};
         };
-        unsigned full_mask = 0, fix_mask = 0;     // per ring stage: no bounds needed / V chunks to trim
+        // Tile issue.  Every wave loads its own 1 KB blocks of K and V^T (each
+        // inside one page, so it needs that page's entry only).  One wave per
+        // tile (rotating) writes the key positions, each page's token count and
+        // the tile's flags: bit 0 = every key exists and is visible to every
+        // query of the q-tile (no bounds needed), bit 1 + pg = page pg has key
+        // slots without a token (their V^T cells must be zeroed).
         auto issue = [&](int t, int st) {
             const int i0 = t * ppt;
-            if (i0 > 0 && (i0 & 63) == 0) load_entry_block((i0 >> 6) + 1);   // before this tile's loads
-            TileEntries te;
-            fetch_entries(t, te);
-            const int4 x[4] = {te.a, te.b, te.c, te.d};
-            bool full = true, fix = false;
-            int kmin = INT32_MAX, kmax = INT32_MIN;
+            // Entries first: the block they come from arrived long ago (the
+            // per-phase waits cover it); reading after the next block's load
+            // would make the compiler wait for every load in flight.
+            int kph[KIW], vph[VIW];
     #pragma unroll
-            for (int pg = 0; pg < 4; ++pg)
-                if (pg < ppt) {
-                    full = full && x[pg].z == PS;
-                    fix = fix || x[pg].z != PS;
-                    kmin = min(kmin, x[pg].y);
-                    kmax = max(kmax, x[pg].y + x[pg].z - 1);
-                }
-            full = full && kmax <= p0 && (!is_local || kmin > p_last - W);
-            const unsigned bit = 1u << st;
-            full_mask = full ? (full_mask | bit) : (full_mask & ~bit);
-            fix_mask = fix ? (fix_mask | bit) : (fix_mask & ~bit);
-            // K and V^T blocks of this wave: page base (uniform) + per-lane offset
+            for (int q = 0; q < KIW; ++q) kph[q] = entry(t, kpg[q], true).x;
+    #pragma unroll
+            for (int q = 0; q < VIW; ++q) vph[q] = entry(t, vpg[q], true).x;
+            if (wave == t % NW) {
+                const int4 en = entry(t, lane / PS, false);
+                const int tk = lane % PS;
+                const int pos = tk < en.z ? en.y + tk : kPosInvalid;
+                sPos[st][lane] = pos;
+                if (tk == 0) sNv[st][lane / PS] = en.z;
+                const bool valid = pos != kPosInvalid;
+                const bool full = __all(valid && pos <= p0 && (!is_local || pos > p_last - W));
+                // pages with an empty key slot: their first lane's bit of the ballot
+                const uint64_t part = __ballot(tk == 0 && en.z < PS);
+                uint32_t pmask = 0;
+    #pragma unroll
+                for (int pg = 0; pg < ppt; ++pg) pmask |= ((part >> (pg * PS)) & 1) << pg;
+                if (lane == 0) sFlags[st] = (full ? 1 : 0) | (int)(pmask << 1);
+            }
+            if (i0 > 0 && (i0 & 63) == 0) load_entry_block((i0 >> 6) + 1);   // before this tile's loads
     #pragma unroll
             for (int q = 0; q < KIW; ++q) {
-                const int4 en = te.pick(kpg[q]);
-                const char *base = (const char *)(P.kp + (int64_t)en.x * (PS * D));
+                const char *base = (const char *)(P.kp + (int64_t)kph[q] * (PS * D));
                 SP_LDS_DMA16((const bf16 *)(base + koff[q]), &sK[st][(wave * KIW + q) * 512]);
             }
     #pragma unroll
             for (int q = 0; q < VIW; ++q) {
-                const int4 en = te.pick(vpg[q]);
-                const char *base = (const char *)(P.vp + (int64_t)en.x * (D * PS));
+                const char *base = (const char *)(P.vp + (int64_t)vph[q] * (D * PS));
                 SP_LDS_DMA16((const bf16 *)(base + voff[q]), &sV[st][(wave * VIW + q) * 512]);
-            }
-            if (tid < BN) {
-                const int4 en = te.pick(tid / PS);
-                const int tk = tid % PS;
-                sPos[st][tid] = tk < en.z ? en.y + tk : kPosInvalid;
             }
         };
         // Zero the V^T slots of keys that hold no token (past a page's n_valid, or
-        // pages past the split): their weight is zero, but 0 * NaN is not.
-        auto fixup = [&](int st) {
-            for (int idx = tid; idx < ppt * D * CPV; idx += NW * 64) {
-                const int pg = idx / (D * CPV), rem = idx % (D * CPV);
-                const int d = rem / CPV, cp = rem % CPV;
-                const int key0 = pg * PS + 8 * (cp ^ swz_v(d));     // first key of the cell
-                int keep = 0;
+        // pages past the split): their weight is zero, but 0 * NaN is not.  The
+        // tokens of a page are a prefix of its slots, so a 16-byte cell of 8
+        // keys keeps its first clamp(n_valid - 8c, 0, 8) values.
+        auto fixup = [&](int st, int t0, int nt) {     // threads t0 .. t0+nt-1 of the workgroup
+            const int pmask = sFlags[st] >> 1;
     #pragma unroll
-                for (int i = 0; i < 8; ++i) keep += sPos[st][key0 + i] != kPosInvalid;
-                if (keep < 8) {
-                    u32x4 *cell = (u32x4 *)&sV[st][pg * D * PS + d * PS + 8 * cp];
-                    *cell = keep > 0 ? keep_first_bf16(*cell, keep) : u32x4{0, 0, 0, 0};
+            for (int pg = 0; pg < ppt; ++pg) {
+                if (!((pmask >> pg) & 1)) continue;
+                const int nv = sNv[st][pg];
+                for (int idx = tid - t0; idx < D * CPV; idx += nt) {
+                    const int d = idx / CPV, cp = idx % CPV;
+                    const int keep = min(max(nv - 8 * (cp ^ swz_v(d)), 0), 8);
+                    if (keep < 8) {
+                        u32x4 *cell = (u32x4 *)&sV[st][pg * D * PS + d * PS + 8 * cp];
+                        *cell = keep > 0 ? keep_first_bf16(*cell, keep) : u32x4{0, 0, 0, 0};
+                    }
                 }
             }
         };
@@ -292,25 +281,65 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int krow0 = sigma(n) * D, kx = swz_k(sigma(n));
         const int vx = swz_v(n);
 
-        // The compute runs in halves of a tile (32 keys): S^T of one half is one
-        // 32x32 MFMA tile per lane group, so the pipeline below keeps just two
-        // of them (the half being exponentiated, the half being scored) and the
-        // operand reads of a whole half in registers ahead of their MFMAs.
-        auto qk = [&](int st, int kt, f32x16 &S) {          // S^T = K Q^T of keys [32 kt, 32 kt + 32)
-            const bf16 *kbase = &sK[st][krow0 + 32 * kt * D];
-            bf16x8 a[DK];
+        // ---- ping-pong schedule.  The waves form two groups of one wave per
+        // SIMD (waves 0-3 and 4-7 share SIMDs pairwise).  Phases are separated by
+        // workgroup barriers; in each phase one group runs its matrix products
+        // (P.V of the previous tile, then S = K Q^T of the next) while the other
+        // group runs the softmax of its current tile on the vector ALUs, and the
+        // roles swap every phase.  Each SIMD thus has one wave feeding its
+        // matrix cores and one keeping its vector ALUs busy at all times.
+        //   group 0: phase 2j   = MFMA(j): PV(j-1), QK(j);  phase 2j+1 = softmax(j)
+        //   group 1: phase 2j+1 = MFMA(j);                  phase 2j+2 = softmax(j)
+        // Tile m is issued in phase 2m-4 (0..2 before phase 0), waited for at
+        // the end of phase 2m-1, and its stage is free after phase 2m+3.
+        const int grp = wave >> 2;
+        static_assert(NW == 8, "the ping-pong schedule pairs two groups of four waves");
+        // Operand reads run one k-group ahead of the MFMAs that use them: the
+        // first group's reads are issued together, then each MFMA is followed
+        // by one read of the next group (explicit schedule groups), so the LDS
+        // latency is paid once per product and the live operands stay few.
+        auto qk = [&](int st, f32x16 (&S)[2]) {              // S^T = K Q^T of one tile
+            bf16x8 a[2][DK];
     #pragma unroll
-            for (int s = 0; s < DK; ++s) a[s] = *(const bf16x8 *)(kbase + ((2 * s + h) ^ kx) * 8);
-            S = f32x16{0};
+            for (int kt = 0; kt < 2; ++kt) {
+                const bf16 *kbase = &sK[st][krow0 + 32 * kt * D];
     #pragma unroll
-            for (int s = 0; s < DK; ++s) S = mfma32x32x16(a[s], qf[s], S);
-        };
-        auto mask = [&](int st, int kt, f32x16 &S) {         // bounds of a boundary tile
-    #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int kpos = sPos[st][32 * kt + 16 * (v >> 3) + 8 * h + (v & 7)];
-                S[v] = (kpos <= pq && kpos > lowq) ? S[v] : -INFINITY;
+                for (int s = 0; s < DK; ++s) a[kt][s] = *(const bf16x8 *)(kbase + ((2 * s + h) ^ kx) * 8);
             }
+    #pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                S[kt] = f32x16{0};
+    #pragma unroll
+                for (int s = 0; s < DK; ++s) S[kt] = mfma32x32x16(a[kt][s], qf[s], S[kt]);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, DK, 0);           // reads of key tile 0
+    #pragma unroll
+            for (int i = 0; i < DK; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA of key tile 0
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // read of key tile 1
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, DK, 0);           // MFMAs of key tile 1
+        };
+        auto pv = [&](int st, const u32x4 (&Pk)[4]) {       // O^T += V^T P^T over one tile
+            bf16x8 a[4][DT];
+    #pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const int pg = 16 * s2 / PS, c = (16 * s2 % PS) / 8 + h;
+                const bf16 *vb = &sV[st][pg * D * PS + n * PS + 8 * (c ^ vx)];
+    #pragma unroll
+                for (int dt = 0; dt < DT; ++dt) a[s2][dt] = *(const bf16x8 *)(vb + 32 * dt * PS);
+            }
+    #pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2)
+    #pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32x32x16(a[s2][dt], u4_as_bf16x8(Pk[s2]), acc[dt]);
+            __builtin_amdgcn_sched_group_barrier(0x100, DT, 0);           // reads of k-step 0
+    #pragma unroll
+            for (int i = 0; i < 3 * DT; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA of k-step i / DT
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // read of k-step i / DT + 1
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, DT, 0);           // MFMAs of k-step 3
         };
         // Online softmax with a lazily moved reference max (log2 domain, raw scores
         // times c = scale*log2 e): the reference only moves when a row's max exceeds
@@ -319,10 +348,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         // normalisation by l makes the result independent of the reference.
         constexpr float kLazy = 8.f;
         const float cl = P.scale_log2;
-        auto update_max = [&](const f32x16 &S) {
-            float mx = -INFINITY;
+        auto softmax = [&](int st, bool full, f32x16 (&S)[2], u32x4 (&Pk)[4]) {
+            if (!full) {                                     // bounds of a boundary tile
     #pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[v]);
+                for (int kt = 0; kt < 2; ++kt)
+    #pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int kpos = sPos[st][32 * kt + 16 * (v >> 3) + 8 * h + (v & 7)];
+                        S[kt][v] = (kpos <= pq && kpos > lowq) ? S[kt][v] : -INFINITY;
+                    }
+            }
+            // row max: four independent chains, then one cross-lane step
+            float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    #pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+    #pragma unroll
+                for (int v = 0; v < 16; ++v) m4[(kt * 16 + v) & 3] = fmaxf(m4[(kt * 16 + v) & 3], S[kt][v]);
+            float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
             mx = fmaxf(mx, xor_lane(mx, 32)) * cl;
             if (__any(mx > m_run + kLazy)) {
                 const float m_new = fmaxf(m_run, mx);
@@ -332,76 +374,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
                 m_run = m_new;
             }
-        };
-        // weights of one half -> packed bf16 P^T operands of its two 16-key steps
-        // (exponents <= kLazy; v_exp_f32 flushes results below 2^-126 to zero)
-        auto softmax = [&](const f32x16 &S, u32x4 (&Pk)[2]) {
+            // weights -> packed bf16 P^T operands (exponents <= kLazy; v_exp_f32
+            // flushes results below 2^-126 to zero, which is harmless).  Each
+            // stage runs over all 32 scores in place, so the vector ALU sees 32
+            // independent operations at a time instead of one short chain.
             const float off = m_run == -INFINITY ? 0.f : -m_run;
-            float rs = 0.f;
     #pragma unroll
-            for (int u = 0; u < 2; ++u)
+            for (int kt = 0; kt < 2; ++kt)
     #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(S[8 * u + 2 * w], cl, off));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(S[8 * u + 2 * w + 1], cl, off));
-                    Pk[u][w] = pack_bf16x2(p0, p1);
-                    rs = sum_bf16x2(Pk[u][w], rs);   // the row sum of the weights P.V uses
-                }
+                for (int v = 0; v < 16; ++v) S[kt][v] = fmaf(S[kt][v], cl, off);
+    #pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+    #pragma unroll
+                for (int v = 0; v < 16; ++v) S[kt][v] = __builtin_amdgcn_exp2f(S[kt][v]);
+    #pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2)
+    #pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    Pk[s2][w] = pack_bf16x2(S[s2 >> 1][8 * (s2 & 1) + 2 * w], S[s2 >> 1][8 * (s2 & 1) + 2 * w + 1]);
+            float r4[4] = {0.f, 0.f, 0.f, 0.f};              // the row sum of the weights P.V uses
+    #pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2)
+    #pragma unroll
+                for (int w = 0; w < 4; ++w) r4[w] = sum_bf16x2(Pk[s2][w], r4[w]);
+            const float rs = (r4[0] + r4[1]) + (r4[2] + r4[3]);
             l_run += rs;
         };
-        auto pv = [&](int st, int kt, const u32x4 (&Pk)[2]) {   // O^T += V^T P^T over keys [32 kt, 32 kt + 32)
-            bf16x8 a[2][DT];
-    #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int s2 = 2 * kt + u;
-                const int pg = 16 * s2 / PS, c = (16 * s2 % PS) / 8 + h;
-                const bf16 *vb = &sV[st][pg * D * PS + n * PS + 8 * (c ^ vx)];
-    #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) a[u][dt] = *(const bf16x8 *)(vb + 32 * dt * PS);
-            }
-    #pragma unroll
-            for (int u = 0; u < 2; ++u)
-    #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32x32x16(a[u][dt], u4_as_bf16x8(Pk[u]), acc[dt]);
-        };
-        auto wait_first_tile = [&]() {        // the prologue issued tiles 0 .. min(2, n_tiles-1)
-            const int after = min(NBUF - 2, n_tiles - 1);
-            if (after >= 2) wait_vmcnt<2 * IPW>();
-            else if (after == 1) wait_vmcnt<IPW>();
-            else wait_vmcnt<0>();
-        };
-        // One half-step: the scores Sc of the current half are masked (boundary
-        // tiles only), exponentiated and multiplied into O while the next half's
-        // scores Sn are formed on the matrix cores.
-        auto half = [&](int st, int kt, bool full, f32x16 &Sc, int st_n, int kt_n, f32x16 &Sn) {
-            if (!full) mask(st, kt, Sc);
-            update_max(Sc);
-            u32x4 Pk[2];
-            qk(st_n, kt_n, Sn);                  // past the last tile this reads a stale stage; unused
-            softmax(Sc, Pk);
-            pv(st, kt, Pk);
-            // Schedule: all operand reads of the next half's QK^T first, then its
-            // MFMAs each followed by a share of the exponentials and packing of
-            // this half, then P.V with its operand reads issued up front.
-            __builtin_amdgcn_sched_group_barrier(0x100, DK, 0);            // LDS reads (K)
-    #pragma unroll
-            for (int i = 0; i < DK; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);         // VALU incl. transcendental
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * DT, 0);        // LDS reads (V^T)
-    #pragma unroll
-            for (int i = 0; i < 2 * DT; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
-            }
-        };
 
-        // ---- ring pipeline.  Tiles t and t+1 are resident, t+2 and t+3 in flight.
-        // Iteration t: half 0 of tile t (scoring half 1), then the wait for tile
-        // t+1, the barrier and the issue of tile t+3, then half 1 of tile t
-        // (scoring half 0 of tile t+1).
-        static_assert(NBUF == 4, "the pipeline keeps two tiles resident and two in flight");
+        static_assert(NBUF == 4, "tiles m-1 .. m+2 occupy the four stages around phase 2m");
         if (n_tiles > 0) {
             load_entry_block(0);
             wait_vmcnt<0>();
@@ -411,32 +411,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     #pragma unroll
         for (int j = 0; j < NBUF - 1; ++j)
             if (j < n_tiles) issue(j, j);
-        f32x16 Sa, Sb;
         if (n_tiles > 0) {
-            wait_first_tile();
+            if (n_tiles > 2) wait_vmcnt<2 * IPW>();
+            else if (n_tiles > 1) wait_vmcnt<IPW>();
+            else wait_vmcnt<0>();
             lds_barrier();
-            if (fix_mask & 1) {
-                fixup(0);
-                lds_barrier();
-            }
-            qk(0, 0, Sa);
         }
-        for (int t = 0; t < n_tiles; ++t) {
-            const int st = t % NBUF, st1 = (t + 1) % NBUF;
-            const bool has1 = t + 1 < n_tiles;
-            const bool full = (full_mask >> st) & 1;
-            half(st, 0, full, Sa, st, 1, Sb);
-            if (has1) {                          // tiles issued after t+1: at most one
-                if (t + 2 < n_tiles) wait_vmcnt<IPW>();
-                else wait_vmcnt<0>();
+        f32x16 S[2];
+        u32x4 Pk[4];
+        const int n_phases = n_tiles > 0 ? 2 * n_tiles + 2 : 0;
+        for (int k = 0; k < n_phases; ++k) {
+            const int p2 = k >> 1;
+            if (!(k & 1) && p2 >= 1 && p2 + 2 < n_tiles) issue(p2 + 2, (p2 + 2) % NBUF);
+            if (!(k & 1) && grp == 1 && p2 < n_tiles && (sFlags[p2 % NBUF] >> 1))
+                fixup(p2 % NBUF, 4 * 64, 4 * 64);            // group 1 is in its vector-ALU phase
+
+            const int j = (k - grp) >> 1;                    // this group's tile in this phase
+            if (((k + grp) & 1) == 0) {                      // matrix-core phase
+                if (j >= 1) pv((j - 1) % NBUF, Pk);
+                if (j < n_tiles) qk(j % NBUF, S);
+            } else if (j >= 0 && j < n_tiles) {              // vector-ALU phase
+                softmax(j % NBUF, sFlags[j % NBUF] & 1, S, Pk);
             }
-            lds_barrier();                       // tile t+1 visible; stage of tile t-1 free
-            if (has1 && ((fix_mask >> st1) & 1)) {
-                fixup(st1);
-                lds_barrier();
+            if (k & 1) {                                     // tile (k+1)/2 is used from the next phase on
+                const int m = (k + 1) >> 1;
+                if (m < n_tiles) {
+                    if (m + 1 < n_tiles) wait_vmcnt<IPW>();
+                    else wait_vmcnt<0>();
+                }
             }
-            if (t + NBUF - 1 < n_tiles) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF);
-            half(st, 1, full, Sb, st1, 0, Sa);
+            lds_barrier();
         }
 
         // ---- epilogue
