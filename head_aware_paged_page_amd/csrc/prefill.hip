@@ -31,6 +31,13 @@ namespace sp {
 namespace {
 
 constexpr int BN = kPrefillKeysPerTile;   // 64 keys per tile
+// Ping-pong (the two wave groups of a SIMD in opposite phases) measured well
+// ahead of running both groups' phases in step on gfx950, where two waves
+// issuing MFMAs together on one SIMD stall each other's operand reads.
+#ifndef SP_PINGPONG
+#define SP_PINGPONG 1
+#endif
+constexpr bool kPingPong = SP_PINGPONG;
 
 struct PrefillParams {
     const bf16 *q, *kp, *vp;
@@ -282,8 +289,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int vx = swz_v(n);
 
         // ---- ping-pong schedule.  The waves form two groups of one wave per
-        // SIMD (waves 0-3 and 4-7 share SIMDs pairwise).  Phases are separated by
-        // workgroup barriers; in each phase one group runs its matrix products
+        // SIMD (waves 0-3 and 4-7 share SIMDs pairwise).  In each phase one
+        // group runs its matrix products
         // (P.V of the previous tile, then S = K Q^T of the next) while the other
         // group runs the softmax of its current tile on the vector ALUs, and the
         // roles swap every phase.  Each SIMD thus has one wave feeding its
@@ -292,8 +299,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         //   group 1: phase 2j+1 = MFMA(j);                  phase 2j+2 = softmax(j)
         // Tile m is issued in phase 2m-4 (0..2 before phase 0), waited for at
         // the end of phase 2m-1, and its stage is free after phase 2m+3.
-        const int grp = wave >> 2;
         static_assert(NW == 8, "the ping-pong schedule pairs two groups of four waves");
+        const int grp = kPingPong ? wave >> 2 : 0;
         // Operand reads run one k-group ahead of the MFMAs that use them: the
         // first group's reads are issued together, then each MFMA is followed
         // by one read of the next group (explicit schedule groups), so the LDS
@@ -419,12 +426,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         }
         f32x16 S[2];
         u32x4 Pk[4];
-        const int n_phases = n_tiles > 0 ? 2 * n_tiles + 2 : 0;
+        const int n_phases = n_tiles > 0 ? 2 * n_tiles + (kPingPong ? 2 : 1) : 0;
         for (int k = 0; k < n_phases; ++k) {
             const int p2 = k >> 1;
             if (!(k & 1) && p2 >= 1 && p2 + 2 < n_tiles) issue(p2 + 2, (p2 + 2) % NBUF);
-            if (!(k & 1) && grp == 1 && p2 < n_tiles && (sFlags[p2 % NBUF] >> 1))
-                fixup(p2 % NBUF, 4 * 64, 4 * 64);            // group 1 is in its vector-ALU phase
+            if (kPingPong) {
+                if (!(k & 1) && grp == 1 && p2 < n_tiles && (sFlags[p2 % NBUF] >> 1))
+                    fixup(p2 % NBUF, 4 * 64, 4 * 64);        // group 1 is in its vector-ALU phase
+            } else if ((k & 1) && p2 < n_tiles && (sFlags[p2 % NBUF] >> 1)) {
+                fixup(p2 % NBUF, 0, NW * 64);                // all waves, before P.V(p2) two phases on
+            }
 
             const int j = (k - grp) >> 1;                    // this group's tile in this phase
             if (((k + grp) & 1) == 0) {                      // matrix-core phase
@@ -439,8 +450,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                     if (m + 1 < n_tiles) wait_vmcnt<IPW>();
                     else wait_vmcnt<0>();
                 }
+                // One barrier per phase pair: it publishes tile m and retires the
+                // stage that the next issue reuses.  Between barriers the two
+                // groups run their phases in opposite order (matrix then vector,
+                // vector then matrix), which keeps them out of step on each SIMD.
+                lds_barrier();
             }
-            lds_barrier();
         }
 
         // ---- epilogue
