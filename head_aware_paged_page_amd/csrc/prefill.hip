@@ -46,7 +46,8 @@ struct PrefillParams {
     const int32_t *tok_ptr, *q_pos0, *cls, *window, *row_ptr;
     const int4 *entries;
     const int32_t *item_ptr, *item_ptr2, *part_ptr, *nsplit;
-    float *part_o, *part_lse;
+    _Float16 *part_o;   // split partials, normalised, fp16 [part][row][D]
+    float *part_lse;
     int n_seq, n_rows, G, ps, tpt, Hq;
     int64_t n_phys;
     float scale_log2;   // softmax_scale * log2(e)
@@ -478,14 +479,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             if (P.lse && h == 0) P.lse[(int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g] = lse;
         } else {
             const int64_t part = (int64_t)P.part_ptr[r] + local;
-            float *po = P.part_o + (part * BM + row) * D;
+            _Float16 *po = P.part_o + (part * BM + row) * D;
     #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
     #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int d = 32 * dt + 8 * q4 + 4 * h;
-                    *(float4 *)(po + d) = make_float4(acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv,
-                                                      acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv);
+                    const f32x4 v = {acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv, acc[dt][4 * q4 + 2] * inv,
+                                     acc[dt][4 * q4 + 3] * inv};
+                    *(f16x4 *)(po + d) = __builtin_convertvector(v, f16x4);
                 }
             if (h == 0) P.part_lse[part * BM + row] = lse;
         }
@@ -495,16 +497,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // Combines the kv splits of every split q-tile: O = sum_s e^{lse_s-M} o_s / sum_s e^{lse_s-M}.
 // Launched over the same work items: item (q-tile, split s) merges rows
 // [s * ceil(rows/ns), (s+1) * ceil(rows/ns)) of its q-tile, so all splits share
-// the work.  One wave per row: the split weights are formed once per row (in
-// LDS), then each lane accumulates its dims over the splits.
+// the work.  Sixteen lanes per row (four rows per wave, sixteen per workgroup
+// pass); each lane reads its row's split LSEs (the same addresses for the row's
+// lanes), then accumulates its D/16 dims over the splits.  The partials are
+// normalised (|o| <= max |v|), so fp16 keeps them to about 5e-4 relative.
 template <int D>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, int BM) {
-    __shared__ float sw[4][kMaxSplits];
+    constexpr int LPR = 16, DPL = D / LPR;           // lanes per row, dims per lane
+    static_assert(DPL % 4 == 0, "whole float4 loads per lane");
     int r, local;
     item_of(P.item_ptr, P.item_ptr2, P.n_rows, blockIdx.x, &r, &local);
     const int ns = P.nsplit[r];
     if (ns == 1) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane / LPR, li = lane % LPR;
     const int qt = local / ns, sp_i = local % ns;
     const int seq = r % P.n_seq, slot = r / P.n_seq;
     const int tok_base = P.tok_ptr[seq];
@@ -514,49 +520,40 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, int
     const int per = (nrows + ns - 1) / ns;
     const int r0 = sp_i * per, r1 = min(nrows, r0 + per);
     const int64_t part0 = (int64_t)P.part_ptr[r] + (int64_t)qt * ns;   // splits part0 .. part0+ns-1
-    constexpr int DPL = D / 64;                                      // dims per lane
-    for (int row = r0 + wave; row < r1; row += 4) {
+    for (int row = r0 + 4 * wave + sub; row - sub < r1; row += 16) {
+        if (row >= r1) continue;
+        const float *lse = P.part_lse + part0 * BM + row;
         float M = -INFINITY;
-        for (int s = lane; s < ns; s += 64) M = fmaxf(M, P.part_lse[(part0 + s) * BM + row]);
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
-        float z = 0.f;
-        for (int s = lane; s < ns; s += 64) {
-            const float l = P.part_lse[(part0 + s) * BM + row];
-            const float wgt = M == -INFINITY ? 0.f : __expf(l - M);
-            sw[wave][s] = wgt;
-            z += wgt;
-        }
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) z += __shfl_xor(z, m, 64);
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_wave_barrier();
-        float o[DPL];
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, lse[(int64_t)s * BM]);
+        float o[DPL], z = 0.f;
 #pragma unroll
         for (int i = 0; i < DPL; ++i) o[i] = 0.f;
-        const float *src = P.part_o + (part0 * BM + row) * D + DPL * lane;
-#pragma unroll 8
-        for (int s = 0; s < ns; ++s) {
-            const float wgt = sw[wave][s];
-            const float *q = src + (int64_t)s * BM * D;
-            if (DPL == 2) {
-                const float2 v = *(const float2 *)q;
-                o[0] += wgt * v.x;
-                o[DPL - 1] += wgt * v.y;
-            } else {
-                o[0] += wgt * q[0];
+        if (M != -INFINITY) {
+            const _Float16 *src = P.part_o + (part0 * BM + row) * D + DPL * li;
+#pragma unroll 4
+            for (int s = 0; s < ns; ++s) {
+                const float wgt = __expf(lse[(int64_t)s * BM] - M);
+                z += wgt;
+#pragma unroll
+                for (int i = 0; i < DPL / 4; ++i) {
+                    const f32x4 v = __builtin_convertvector(*(const f16x4 *)(src + (int64_t)s * BM * D + 4 * i), f32x4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[4 * i + e] += wgt * v[e];
+                }
             }
         }
         const float inv = z > 0.f ? 1.f / z : 0.f;
         const int tq = row / P.G, g = row % P.G;
         const int64_t orow = (int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * P.G + g;
-        if (DPL == 2) {
-            *(uint32_t *)(P.out + orow * D + 2 * lane) = pack_bf16x2(o[0] * inv, o[DPL - 1] * inv);
+        uint32_t pk[DPL / 2];
+#pragma unroll
+        for (int i = 0; i < DPL / 2; ++i) pk[i] = pack_bf16x2(o[2 * i] * inv, o[2 * i + 1] * inv);
+        if (DPL == 8) {
+            *(u32x4 *)(P.out + orow * D + DPL * li) = u32x4{pk[0], pk[1 % (DPL / 2)], pk[2 % (DPL / 2)], pk[3 % (DPL / 2)]};
         } else {
-            P.out[orow * D + lane] = f32_to_bf16(o[0] * inv);
+            *(u32x2 *)(P.out + orow * D + DPL * li) = u32x2{pk[0], pk[1 % (DPL / 2)]};
         }
-        if (P.lse && lane == 0) P.lse[orow] = z > 0.f ? M + logf(z) : -INFINITY;
-        __builtin_amdgcn_wave_barrier();
+        if (P.lse && li == 0) P.lse[orow] = z > 0.f ? M + logf(z) : -INFINITY;
     }
 }
 
@@ -652,7 +649,7 @@ int launch_prefill(const AttnArgs &a, const Plan &p, int64_t n_tok, hipStream_t 
     P.item_ptr2 = (const int32_t *)(w + p.off_item_ptr2);
     P.part_ptr = (const int32_t *)(w + p.off_part_ptr);
     P.nsplit = (const int32_t *)(w + p.off_nsplit);
-    P.part_o = (float *)(w + p.off_part_o);
+    P.part_o = (_Float16 *)(w + p.off_part_o);
     P.part_lse = (float *)(w + p.off_part_lse);
     P.n_seq = a.n_seq;
     P.n_rows = p.n_rows;

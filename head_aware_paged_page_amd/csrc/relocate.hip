@@ -8,7 +8,7 @@
 // delta * w_i.  The angle is formed and reduced modulo 2*pi in fp64, its
 // sine/cosine taken in fp64 and the rotation applied in fp32.
 //
-// HBM-bound streaming: a workgroup takes a run of 8 list items (staged in LDS)
+// HBM-bound streaming: a workgroup takes a run of 4 list items (staged in LDS)
 // and issues all their loads at once (streaming, non-temporal loads and stores:
 // every byte is touched once; the table builder lists pages in address order,
 // so a run is mostly one contiguous stretch of the pool).  While the loads are
@@ -21,7 +21,7 @@ namespace sp {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPagesPerBlock = 8;
+constexpr int kPagesPerBlock = 4;
 constexpr int kBatch = 4;             // units per thread with loads in flight together
 constexpr int kMaxHalf = 128;         // head_dim / 2
 constexpr double kTwoPiHi = 6.283185307179586232;      // 2*pi rounded to fp64
