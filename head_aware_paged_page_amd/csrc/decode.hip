@@ -37,6 +37,15 @@ struct DecodeParams {
     float scale_log2;
 };
 
+// Launch plan of a call with few rows, built on the host and passed by value
+// (kernel arguments), so such calls need no plan kernel: same meaning as the
+// workspace arrays of the same names.
+constexpr int kInlineRows = 192;
+struct InlinePlan {
+    int32_t item_ptr[kInlineRows + 1], item_ptr2[kInlineRows + 1], part_ptr[kInlineRows + 1];
+    int32_t nsplit[kInlineRows];
+};
+
 template <int D>
 struct Block {
     u32x4 k[2][D / 32];   // S^T A operands: [key tile][k-step]
@@ -97,9 +106,9 @@ __device__ __forceinline__ int block_pos(const Block<D> &B, int j) {
     return tk < z ? y + tk : kPosInvalid;
 }
 
-template <int D, int PS>
+template <int D, int PS, bool INL>
 __global__ __launch_bounds__(NWD * 64) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_bf16_kernel(
-    DecodeParams P) {
+    DecodeParams P, InlinePlan L) {
     constexpr int DS = D / 32;   // k-steps of S^T
     constexpr int DT = D / 16;   // dim tiles of O^T
     __shared__ float sM[NWD][16], sL[NWD][16];
@@ -110,8 +119,9 @@ __global__ __launch_bounds__(NWD * 64) __attribute__((amdgpu_waves_per_eu(3, 3))
     const int n = lane & 15, grp = lane >> 4;
 
     int r, sp_i;
-    item_of(P.item_ptr, P.item_ptr2, P.n_rows, blockIdx.x, &r, &sp_i);
-    const int ns = P.nsplit[r];
+    if (INL) item_of(L.item_ptr, L.item_ptr2, P.n_rows, blockIdx.x, &r, &sp_i);
+    else item_of(P.item_ptr, P.item_ptr2, P.n_rows, blockIdx.x, &r, &sp_i);
+    const int ns = INL ? L.nsplit[r] : P.nsplit[r];
     const int seq = r % P.n_seq, slot = r / P.n_seq;
     const int G = P.G;
     constexpr int ps = PS;
@@ -225,7 +235,7 @@ __global__ __launch_bounds__(NWD * 64) __attribute__((amdgpu_waves_per_eu(3, 3))
 #pragma unroll
         for (int v = 0; v < 4; ++v) sO[wave][16 * dt + 4 * grp + v][n] = acc[dt][v];
     __syncthreads();
-    const int64_t part = ns > 1 ? (int64_t)P.part_ptr[r] + sp_i : 0;
+    const int64_t part = ns > 1 ? (int64_t)(INL ? L.part_ptr[r] : P.part_ptr[r]) + sp_i : 0;
     for (int idx = threadIdx.x; idx < G * D; idx += NWD * 64) {
         const int hh = idx / D, d = idx % D;
         float M = -INFINITY;
@@ -253,31 +263,48 @@ __global__ __launch_bounds__(NWD * 64) __attribute__((amdgpu_waves_per_eu(3, 3))
     }
 }
 
-// One thread per (row, head, dim) output of a split row.
-template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams P) {
-    const int r = blockIdx.x;
-    const int ns = P.nsplit[r];
+// Merges the splits of every split row: one wave per (row, head).  The lanes
+// read the split LSEs together (lane s, s+64, ...), form the weights
+// e^{lse_s - M} in LDS, then each lane accumulates its D/64 dims over the
+// splits: O = sum_s w_s o_s / sum_s w_s.
+template <int D, bool INL>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams P, InlinePlan L) {
+    __shared__ float sw[kMaxSplits];
+    const int r = blockIdx.x, hh = blockIdx.y;
+    const int ns = INL ? L.nsplit[r] : P.nsplit[r];
     if (ns == 1) return;
+    const int lane = threadIdx.x;
     const int seq = r % P.n_seq, slot = r / P.n_seq, G = P.G;
-    const int idx = blockIdx.y * 64 + threadIdx.x;
-    if (idx >= G * D) return;
-    const int hh = idx / D, d = idx % D;
-    const int64_t part0 = P.part_ptr[r];
+    const int64_t part0 = INL ? L.part_ptr[r] : P.part_ptr[r];
     float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, P.part_lse[(part0 + s) * G + hh]);
-    float o = 0.f, z = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll 4
-        for (int s = 0; s < ns; ++s) {
-            const float w = __expf(P.part_lse[(part0 + s) * G + hh] - M);
-            o += w * P.part_o[((part0 + s) * G + hh) * D + d];
-            z += w;
-        }
+    for (int s = lane; s < ns; s += 64) M = fmaxf(M, P.part_lse[(part0 + s) * G + hh]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+    float z = 0.f;
+    for (int s = lane; s < ns; s += 64) {
+        const float wgt = M == -INFINITY ? 0.f : __expf(P.part_lse[(part0 + s) * G + hh] - M);
+        sw[s] = wgt;
+        z += wgt;
     }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) z += __shfl_xor(z, m, 64);
+    __syncthreads();
+    constexpr int DPL = D / 64;
+    float o[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) o[i] = 0.f;
+    const float *src = P.part_o + (part0 * G + hh) * D + DPL * lane;
+#pragma unroll 8
+    for (int s = 0; s < ns; ++s) {
+        const float wgt = sw[s];
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) o[i] += wgt * src[(int64_t)s * G * D + i];
+    }
+    const float inv = z > 0.f ? 1.f / z : 0.f;
     const int64_t orow = (int64_t)seq * P.Hq + (int64_t)slot * G + hh;
-    P.out[orow * D + d] = f32_to_bf16(z > 0.f ? o / z : 0.f);
-    if (P.lse && d == 0) P.lse[orow] = z > 0.f ? M + logf(z) : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) P.out[orow * D + DPL * lane + i] = f32_to_bf16(o[i] * inv);
+    if (P.lse && lane == 0) P.lse[orow] = z > 0.f ? M + logf(z) : -INFINITY;
 }
 
 }  // namespace
@@ -288,8 +315,30 @@ int launch_decode_f32(const AttnArgs &a, hipStream_t stream);
 
 int launch_decode(const AttnArgs &a, const Plan &p, hipStream_t stream) {
     if (a.dtype == SP_F32) return launch_decode_f32(a, stream);
-    int rc = launch_plan(p, a.d_row_ptr, nullptr, a.n_seq, a.ws, stream);
-    if (rc) return rc;
+    // Few rows: the plan (the same integer formulas as the plan kernel) goes in
+    // the kernel arguments; otherwise the plan kernel writes it to the workspace.
+    const bool inl = p.n_rows <= kInlineRows && a.h_row_ptr != nullptr;
+    InlinePlan L;
+    if (inl) {
+        int32_t cl = 0, cs = 0, cp = 0;
+        for (int r = 0; r < p.n_rows; ++r) {
+            int ns, it;
+            row_items(a.h_row_ptr[r + 1] - a.h_row_ptr[r], 1, p.chunk_pages, &ns, &it);
+            L.nsplit[r] = ns;
+            L.item_ptr[r] = cl;
+            L.item_ptr2[r] = cs;
+            L.part_ptr[r] = cp;
+            if (ns > 1) { cl += it; cp += it; }
+            else cs += it;
+        }
+        L.item_ptr[p.n_rows] = cl;
+        L.item_ptr2[p.n_rows] = cs;
+        L.part_ptr[p.n_rows] = cp;
+    } else {
+        L.item_ptr[0] = 0;
+        const int rc = launch_plan(p, a.d_row_ptr, nullptr, a.n_seq, a.ws, stream);
+        if (rc) return rc;
+    }
     char *w = (char *)a.ws;
     DecodeParams P;
     P.q = (const bf16 *)a.q;
@@ -316,11 +365,16 @@ int launch_decode(const AttnArgs &a, const Plan &p, hipStream_t stream) {
     P.n_phys = a.n_phys;
     P.scale_log2 = a.scale * kLog2e;
     const dim3 grid((unsigned)p.n_items);
-    const dim3 mgrid(p.n_rows, (a.group * a.head_dim + 63) / 64);
-#define SP_DECODE_CASE(DD, PSV)                                                                     \
-    if (a.head_dim == DD && a.page_size == PSV) {                                                   \
-        hipLaunchKernelGGL((decode_bf16_kernel<DD, PSV>), grid, dim3(NWD * 64), 0, stream, P);     \
-        if (p.n_parts) hipLaunchKernelGGL(decode_merge_kernel<DD>, mgrid, dim3(64), 0, stream, P); \
+    const dim3 mgrid(p.n_rows, a.group);
+#define SP_DECODE_CASE(DD, PSV)                                                                                 \
+    if (a.head_dim == DD && a.page_size == PSV) {                                                               \
+        if (inl) {                                                                                              \
+            hipLaunchKernelGGL((decode_bf16_kernel<DD, PSV, true>), grid, dim3(NWD * 64), 0, stream, P, L);    \
+            if (p.n_parts) hipLaunchKernelGGL((decode_merge_kernel<DD, true>), mgrid, dim3(64), 0, stream, P, L); \
+        } else {                                                                                                \
+            hipLaunchKernelGGL((decode_bf16_kernel<DD, PSV, false>), grid, dim3(NWD * 64), 0, stream, P, L);   \
+            if (p.n_parts) hipLaunchKernelGGL((decode_merge_kernel<DD, false>), mgrid, dim3(64), 0, stream, P, L); \
+        }                                                                                                       \
     }
     SP_DECODE_CASE(128, 16) else SP_DECODE_CASE(128, 32) else SP_DECODE_CASE(64, 16) else SP_DECODE_CASE(64, 32)
     else return fail(SP_EUNSUPPORTED, "bf16 decode head_dim %d page_size %d", a.head_dim, a.page_size);

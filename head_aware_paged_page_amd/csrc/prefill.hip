@@ -558,20 +558,30 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, int
 }
 
 // Writes the work-item prefix sums of the launch plan into the workspace; one
-// workgroup, the same integer formulas as the host plan (row_items).  Items of
+// wave, the same integer formulas as the host plan (row_items).  Items of
 // split rows are numbered first (item_ptr), those of unsplit rows after them
-// (item_ptr2, counted from zero; see item_of).
-__global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ row_ptr,
-                                                   const int32_t *__restrict__ tok_ptr, int n_seq, int n_rows,
-                                                   int tpt, int chunk, int32_t *item_ptr, int32_t *item_ptr2,
-                                                   int32_t *part_ptr, int32_t *nsplit, int32_t *zero) {
-    __shared__ int s_l[256], s_s[256], s_p[256];
-    __shared__ int carry_l, carry_s, carry_p;
-    if (threadIdx.x < 64) zero[threadIdx.x] = 0;
-    if (threadIdx.x == 0) { carry_l = 0; carry_s = 0; carry_p = 0; }
-    __syncthreads();
-    for (int base = 0; base < n_rows; base += 256) {
-        const int r = base + threadIdx.x;
+// (item_ptr2, counted from zero; see item_of).  Rows go 64 at a time through
+// wave-wide inclusive scans (no workgroup barriers: the kernel is on the
+// critical path of every call).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(x, off, 64);
+        if (lane >= off) x += t;
+    }
+    return x;
+}
+
+__global__ __launch_bounds__(64) void plan_kernel(const int32_t *__restrict__ row_ptr,
+                                                  const int32_t *__restrict__ tok_ptr, int n_seq, int n_rows,
+                                                  int tpt, int chunk, int32_t *item_ptr, int32_t *item_ptr2,
+                                                  int32_t *part_ptr, int32_t *nsplit, int32_t *zero) {
+    const int lane = threadIdx.x;
+    zero[lane] = 0;
+    int carry_l = 0, carry_s = 0, carry_p = 0;
+    for (int base = 0; base < n_rows; base += 64) {
+        const int r = base + lane;
         int il = 0, is = 0, pt = 0;
         if (r < n_rows) {
             int nq = 1;
@@ -585,30 +595,17 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ r
             if (ns > 1) { il = it; pt = it; }
             else is = it;
         }
-        s_l[threadIdx.x] = il;
-        s_s[threadIdx.x] = is;
-        s_p[threadIdx.x] = pt;
-        __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {   // inclusive scans
-            const int x = threadIdx.x >= off ? s_l[threadIdx.x - off] : 0;
-            const int y = threadIdx.x >= off ? s_s[threadIdx.x - off] : 0;
-            const int z = threadIdx.x >= off ? s_p[threadIdx.x - off] : 0;
-            __syncthreads();
-            s_l[threadIdx.x] += x;
-            s_s[threadIdx.x] += y;
-            s_p[threadIdx.x] += z;
-            __syncthreads();
-        }
+        const int sl = wave_incl_scan(il), ss = wave_incl_scan(is), sp = wave_incl_scan(pt);
         if (r < n_rows) {
-            item_ptr[r] = carry_l + s_l[threadIdx.x] - il;
-            item_ptr2[r] = carry_s + s_s[threadIdx.x] - is;
-            part_ptr[r] = carry_p + s_p[threadIdx.x] - pt;
+            item_ptr[r] = carry_l + sl - il;
+            item_ptr2[r] = carry_s + ss - is;
+            part_ptr[r] = carry_p + sp - pt;
         }
-        __syncthreads();
-        if (threadIdx.x == 255) { carry_l += s_l[255]; carry_s += s_s[255]; carry_p += s_p[255]; }
-        __syncthreads();
+        carry_l += __shfl(sl, 63, 64);
+        carry_s += __shfl(ss, 63, 64);
+        carry_p += __shfl(sp, 63, 64);
     }
-    if (threadIdx.x == 0) {
+    if (lane == 0) {
         item_ptr[n_rows] = carry_l;
         item_ptr2[n_rows] = carry_s;
         part_ptr[n_rows] = carry_p;
@@ -620,7 +617,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ r
 int launch_plan(const Plan &p, const int32_t *d_row_ptr, const int32_t *d_tok_ptr, int n_seq, void *ws,
                 hipStream_t stream) {
     char *w = (char *)ws;
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, d_row_ptr, d_tok_ptr, n_seq, p.n_rows,
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(64), 0, stream, d_row_ptr, d_tok_ptr, n_seq, p.n_rows,
                        p.tok_per_tile, p.chunk_pages, (int32_t *)(w + p.off_item_ptr),
                        (int32_t *)(w + p.off_item_ptr2), (int32_t *)(w + p.off_part_ptr), (int32_t *)(w + p.off_nsplit), (int32_t *)(w + p.off_zero));
     return check_hip(hipGetLastError(), "plan launch");
