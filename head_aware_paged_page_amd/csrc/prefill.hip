@@ -38,6 +38,10 @@ constexpr int BN = kPrefillKeysPerTile;   // 64 keys per tile
 #define SP_PINGPONG 1
 #endif
 constexpr bool kPingPong = SP_PINGPONG;
+#ifndef SP_PRIO_SOFTMAX
+#define SP_PRIO_SOFTMAX 0
+#endif
+constexpr int kPrioSoftmax = SP_PRIO_SOFTMAX;
 
 struct PrefillParams {
     const bf16 *q, *kp, *vp;
@@ -443,7 +447,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 if (j >= 1) pv((j - 1) % NBUF, Pk);
                 if (j < n_tiles) qk(j % NBUF, S);
             } else if (j >= 0 && j < n_tiles) {              // vector-ALU phase
+                // the softmax wave issues first: its SIMD partner's MFMA stream
+                // would otherwise take most issue cycles from it
+                if (kPrioSoftmax) __builtin_amdgcn_s_setprio(kPrioSoftmax);
                 softmax(j % NBUF, sFlags[j % NBUF] & 1, S, Pk);
+                if (kPrioSoftmax) __builtin_amdgcn_s_setprio(0);
             }
             if (k & 1) {                                     // tile (k+1)/2 is used from the next phase on
                 const int m = (k + 1) >> 1;
