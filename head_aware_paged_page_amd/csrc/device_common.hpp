@@ -15,6 +15,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -163,8 +164,20 @@ __device__ __forceinline__ void visible_range(const int4 *__restrict__ E, int e_
 // pass (which must still emit the kernel's launch stub) sees a no-op.
 #if defined(__HIP_DEVICE_COMPILE__)
 #define SP_LDS_DMA16(src, dst) __builtin_amdgcn_global_load_lds((src), (dst), 16, 0, 0)
+// The same load with its LDS destination given as a bare LDS byte address that
+// the compiler cannot trace to a variable.  The compiler then attributes the
+// load to no particular LDS array and inserts no waits for it before later LDS
+// reads: the caller must wait (s_waitcnt vmcnt) before reading what it writes.
+// Kernels that keep several tiles in flight use it so that reading one tile
+// does not wait for the loads of the next ones.
+__device__ __forceinline__ void lds_dma16_unordered(const void *src, const void *dst) {
+    uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);   // wave-uniform
+    asm volatile("" : "+s"(a));
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(uintptr_t)a, 16, 0, 0);
+}
 #else
 #define SP_LDS_DMA16(src, dst) ((void)(src), (void)(dst))
+__device__ __forceinline__ void lds_dma16_unordered(const void *, const void *) {}
 #endif
 
 // Scalar (constant-cache) loads of workgroup-uniform table entries.  Kernels

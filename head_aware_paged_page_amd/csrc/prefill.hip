@@ -42,6 +42,10 @@ constexpr bool kPingPong = SP_PINGPONG;
 #define SP_PRIO_SOFTMAX 0
 #endif
 constexpr int kPrioSoftmax = SP_PRIO_SOFTMAX;
+#ifndef SP_QSCALE
+#define SP_QSCALE 1
+#endif
+constexpr bool kQScale = SP_QSCALE;
 
 struct PrefillParams {
     const bf16 *q, *kp, *vp;
@@ -110,7 +114,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     __shared__ int sPos[NBUF][BN];
     __shared__ int sFlags[NBUF];    // bit 0: no bounds needed; bits 1..ppt: pages with empty key slots
     __shared__ int sNv[NBUF][4];    // tokens held by each page of the tile
-    __shared__ __attribute__((aligned(16))) int4 sEnt[2][64];
 
     __shared__ int s_item;
 
@@ -182,6 +185,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int tq = row / G, g = row % G;
         const int pq = p0 + tq;                    // this lane's query position
         const int lowq = is_local ? pq - W : INT32_MIN;   // visible iff lowq < pos <= pq
+        // The queries are held pre-multiplied by c = scale * log2(e) (rounded
+        // to bf16 once), so the scores leave the matrix cores in the log2
+        // domain of the softmax.
+        const float cl = P.scale_log2;
         bf16x8 qf[DK];
         {
             const bf16 *qrow = P.q + ((int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g) * D;
@@ -189,76 +196,70 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             for (int s = 0; s < DK; ++s) {
                 u32x4 v = {0, 0, 0, 0};
                 if (row_ok) v = *(const u32x4 *)(qrow + 16 * s + 8 * h);
-                qf[s] = u4_as_bf16x8(v);
+                u32x4 w;
+    #pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = pack_bf16x2(bf16_bits_to_f32(v[e] & 0xffffu) * cl, bf16_bits_to_f32(v[e] >> 16) * cl);
+                qf[s] = u4_as_bf16x8(kQScale ? w : v);
             }
         }
         wait_vmcnt<0>();   // queries in registers before the tile loads start
 
-        // ---- tile issue: entries (workgroup-uniform, scalar loads), bounds flags,
-        // key positions, and the global->LDS loads of K and V^T
-        // Page entries stream through LDS too: 64 entries (one 1 KB load by wave 0)
-        // per block, block b+1 requested when block b is first used, so the entry
-        // loads ride in the same in-order stream as the tiles and are covered by
-        // the same waits.  Lanes past the row's end re-read its last entry.
-        auto load_entry_block = [&](int k) {
-            if (wave == 0 && 64 * k < my_hi - my_lo) {
-                const int idx = min(my_lo + 64 * k + lane, e_end - 1);
-                SP_LDS_DMA16(E + idx, &sEnt[k & 1][0]);
-            }
-        };
-        // Entry of page pg (0..ppt-1) of tile t, sanitised: pages past the split
-        // or outside the pool read as {phys 0, no tokens}.  `uniform` reads it
-        // into scalar registers (every lane asks for the same page).
-        auto entry = [&](int t, int pg, bool uniform) {
-            const int i0 = t * ppt;                              // entry index within the split
-            int4 en = sEnt[(i0 >> 6) & 1][(i0 & 63) + pg];       // ppt divides 64: inside the block
-            if (uniform)
-                en = int4{__builtin_amdgcn_readfirstlane(en.x), __builtin_amdgcn_readfirstlane(en.y),
-                          __builtin_amdgcn_readfirstlane(en.z), 0};
-            const bool ok = my_lo + i0 + pg < my_hi && en.x >= 0 && en.x < P.n_phys;
-            return ok ? int4{en.x, en.y, min(en.z, PS), 0} : int4{0, 0, 0, 0};
+        // ---- tile issue: page entries, bounds flags, key positions, and the
+        // global->LDS loads of K and V^T.
+        // The entries come through the constant cache (scalar loads), so they
+        // never share the in-order counter of the tile loads.  Entries past
+        // the split read the split's last.
+        typedef __attribute__((address_space(4))) const i32x4 ci32x4;
+        const ci32x4 *Ec = (const ci32x4 *)(uintptr_t)E;
+        const int n_phys32 = (int)min(P.n_phys, (int64_t)INT32_MAX);
+        i32x4 enx[ppt];
+        auto fetch = [&](int t) {                            // requires t < n_tiles
+    #pragma unroll
+            for (int pg = 0; pg < ppt; ++pg) enx[pg] = Ec[min(my_lo + t * ppt + pg, my_hi - 1)];
         };
         // Tile issue.  Every wave loads its own 1 KB blocks of K and V^T (each
         // inside one page, so it needs that page's entry only).  One wave per
         // tile (rotating) writes the key positions, each page's token count and
         // the tile's flags: bit 0 = every key exists and is visible to every
         // query of the q-tile (no bounds needed), bit 1 + pg = page pg has key
-        // slots without a token (their V^T cells must be zeroed).
+        // slots without a token (their V^T cells must be zeroed).  The entries
+        // are sanitised (pages past the split or outside the pool read as
+        // {phys 0, no tokens}) and picked on the scalar unit.
         auto issue = [&](int t, int st) {
-            const int i0 = t * ppt;
-            // Entries first: the block they come from arrived long ago (the
-            // per-phase waits cover it); reading after the next block's load
-            // would make the compiler wait for every load in flight.
-            int kph[KIW], vph[VIW];
+            // vector values (element = page of the tile), so that picking a
+            // page by a run-time index selects among registers
+            i32x4 ph = {0, 0, 0, 0}, pst = {0, 0, 0, 0}, nvl = {0, 0, 0, 0};
     #pragma unroll
-            for (int q = 0; q < KIW; ++q) kph[q] = entry(t, kpg[q], true).x;
-    #pragma unroll
-            for (int q = 0; q < VIW; ++q) vph[q] = entry(t, vpg[q], true).x;
+            for (int i = 0; i < ppt; ++i) {
+                const i32x4 en = enx[i];
+                const bool ok = my_lo + t * ppt + i < my_hi && en.x >= 0 && en.x < n_phys32;
+                ph[i] = ok ? en.x : 0;
+                pst[i] = ok ? en.y : 0;
+                nvl[i] = ok ? min(en.z, PS) : 0;
+            }
             if (wave == t % NW) {
-                const int4 en = entry(t, lane / PS, false);
-                const int tk = lane % PS;
-                const int pos = tk < en.z ? en.y + tk : kPosInvalid;
+                const int pgl = lane / PS, tk = lane % PS;
+                const int nv = nvl[pgl];
+                const int pos = tk < nv ? pst[pgl] + tk : kPosInvalid;
                 sPos[st][lane] = pos;
-                if (tk == 0) sNv[st][lane / PS] = en.z;
+                if (tk == 0) sNv[st][pgl] = nv;
                 const bool valid = pos != kPosInvalid;
                 const bool full = __all(valid && pos <= p0 && (!is_local || pos > p_last - W));
-                // pages with an empty key slot: their first lane's bit of the ballot
-                const uint64_t part = __ballot(tk == 0 && en.z < PS);
-                uint32_t pmask = 0;
+                uint32_t pmask = 0;                          // pages with an empty key slot
     #pragma unroll
-                for (int pg = 0; pg < ppt; ++pg) pmask |= ((part >> (pg * PS)) & 1) << pg;
+                for (int pg = 0; pg < ppt; ++pg) pmask |= (nvl[pg] < PS ? 1u : 0u) << pg;
                 if (lane == 0) sFlags[st] = (full ? 1 : 0) | (int)(pmask << 1);
             }
-            if (i0 > 0 && (i0 & 63) == 0) load_entry_block((i0 >> 6) + 1);   // before this tile's loads
     #pragma unroll
             for (int q = 0; q < KIW; ++q) {
-                const char *base = (const char *)(P.kp + (int64_t)kph[q] * (PS * D));
-                SP_LDS_DMA16((const bf16 *)(base + koff[q]), &sK[st][(wave * KIW + q) * 512]);
+                const char *base = (const char *)(P.kp + (int64_t)ph[kpg[q]] * (PS * D));
+                lds_dma16_unordered(base + koff[q], &sK[st][(wave * KIW + q) * 512]);
             }
     #pragma unroll
             for (int q = 0; q < VIW; ++q) {
-                const char *base = (const char *)(P.vp + (int64_t)vph[q] * (D * PS));
-                SP_LDS_DMA16((const bf16 *)(base + voff[q]), &sV[st][(wave * VIW + q) * 512]);
+                const char *base = (const char *)(P.vp + (int64_t)ph[vpg[q]] * (D * PS));
+                lds_dma16_unordered(base + voff[q], &sV[st][(wave * VIW + q) * 512]);
             }
         };
         // Zero the V^T slots of keys that hold no token (past a page's n_valid, or
@@ -282,8 +283,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             }
         };
 
-        // ---- running softmax state (log2 domain) and O^T accumulators
-        float m_run = -INFINITY, l_run = 0.f;
+        // ---- running softmax state (log2 domain) and O^T accumulators.  m_ref is
+        // the lane's reference max (-inf until the row's first visible key);
+        // negm holds -m_ref (0 while m_ref is -inf) broadcast over one MFMA
+        // accumulator, the input of the first k-step of S, so the scores arrive
+        // as x - m_ref with x = c * q.k.
+        float m_ref = -INFINITY, l_run = 0.f;
+        f32x16 negm = f32x16{0};
         f32x16 acc[DT];
     #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{0};
@@ -302,35 +308,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         // matrix cores and one keeping its vector ALUs busy at all times.
         //   group 0: phase 2j   = MFMA(j): PV(j-1), QK(j);  phase 2j+1 = softmax(j)
         //   group 1: phase 2j+1 = MFMA(j);                  phase 2j+2 = softmax(j)
-        // Tile m is issued in phase 2m-4 (0..2 before phase 0), waited for at
-        // the end of phase 2m-1, and its stage is free after phase 2m+3.
+        // Tile m is issued in phase 2m-4 by group 1 and 2m-3 by group 0 (tiles
+        // 0..2 by everyone before phase 0), waited for at the end of phase
+        // 2m-1, and its stage is free after phase 2m+3.
         static_assert(NW == 8, "the ping-pong schedule pairs two groups of four waves");
         const int grp = kPingPong ? wave >> 2 : 0;
-        // Operand reads run one k-group ahead of the MFMAs that use them: the
-        // first group's reads are issued together, then each MFMA is followed
-        // by one read of the next group (explicit schedule groups), so the LDS
-        // latency is paid once per product and the live operands stay few.
+        // Operand reads run ahead of the MFMAs that use them (explicit schedule
+        // groups): S^T takes its two 32-key blocks' k-steps alternately, with
+        // the reads two k-steps ahead, so the LDS latency is paid once per
+        // product and few operands are live; P.V reads one k-step ahead.
         auto qk = [&](int st, f32x16 (&S)[2]) {              // S^T = K Q^T of one tile
-            bf16x8 a[2][DK];
+            constexpr int AH = 2;                            // k-steps read ahead
+            bf16x8 a[DK][2];
     #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const bf16 *kbase = &sK[st][krow0 + 32 * kt * D];
+            for (int s = 0; s < DK; ++s)
     #pragma unroll
-                for (int s = 0; s < DK; ++s) a[kt][s] = *(const bf16x8 *)(kbase + ((2 * s + h) ^ kx) * 8);
+                for (int kt = 0; kt < 2; ++kt)
+                    a[s][kt] = *(const bf16x8 *)(&sK[st][krow0 + 32 * kt * D] + ((2 * s + h) ^ kx) * 8);
+    #pragma unroll
+            for (int s = 0; s < DK; ++s)
+    #pragma unroll
+                for (int kt = 0; kt < 2; ++kt) S[kt] = mfma32x32x16(a[s][kt], qf[s], s == 0 ? negm : S[kt]);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * AH, 0);       // reads of k-steps 0 .. AH-1
+    #pragma unroll
+            for (int i = 0; i < 2 * (DK - AH); ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA of k-step i / 2
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // read of k-step i / 2 + AH
             }
-    #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                S[kt] = f32x16{0};
-    #pragma unroll
-                for (int s = 0; s < DK; ++s) S[kt] = mfma32x32x16(a[kt][s], qf[s], S[kt]);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, DK, 0);           // reads of key tile 0
-    #pragma unroll
-            for (int i = 0; i < DK; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA of key tile 0
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // read of key tile 1
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, DK, 0);           // MFMAs of key tile 1
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * AH, 0);       // MFMAs of the last AH k-steps
         };
         auto pv = [&](int st, const u32x4 (&Pk)[4]) {       // O^T += V^T P^T over one tile
             bf16x8 a[4][DT];
@@ -353,48 +358,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             }
             __builtin_amdgcn_sched_group_barrier(0x008, DT, 0);           // MFMAs of k-step 3
         };
-        // Online softmax with a lazily moved reference max (log2 domain, raw scores
-        // times c = scale*log2 e): the reference only moves when a row's max exceeds
-        // it by more than kLazy, so weights stay <= 2^kLazy (harmless in fp32 and
-        // bf16) and the rescale of the accumulators becomes rare.  The final
-        // normalisation by l makes the result independent of the reference.
-        constexpr float kLazy = 8.f;
-        const float cl = P.scale_log2;
-        auto softmax = [&](int st, bool full, f32x16 (&S)[2], u32x4 (&Pk)[4]) {
-            if (!full) {                                     // bounds of a boundary tile
-    #pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-    #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int kpos = sPos[st][32 * kt + 16 * (v >> 3) + 8 * h + (v & 7)];
-                        S[kt][v] = (kpos <= pq && kpos > lowq) ? S[kt][v] : -INFINITY;
-                    }
-            }
-            // row max: four independent chains, then one cross-lane step
-            float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        // Online softmax with a rarely moved reference (log2 domain).  The weights
+        // of a tile are exp2(x - m_ref) straight from the score registers; the
+        // reference only moves when one of them would exceed 2^16 (the lane's
+        // sum of its weights exceeds 2^16, or is inf) or while the row has no
+        // reference yet.  Only then are the scores formed again (the tile is
+        // still resident), the row max taken and the accumulators rescaled.
+        // Weights up to 2^16 are harmless in bf16 and fp32, and once m_ref is a
+        // true row max, l >= 1, so weights that underflow are negligible.  The
+        // final normalisation by l makes the result independent of m_ref.
+        constexpr float kMaxWeight = 65536.f;
+        auto mask = [&](int st, f32x16 (&S)[2]) {            // bounds of a boundary tile
     #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
     #pragma unroll
-                for (int v = 0; v < 16; ++v) m4[(kt * 16 + v) & 3] = fmaxf(m4[(kt * 16 + v) & 3], S[kt][v]);
-            float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-            mx = fmaxf(mx, xor_lane(mx, 32)) * cl;
-            if (__any(mx > m_run + kLazy)) {
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-                l_run *= alpha;
-    #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-                m_run = m_new;
-            }
-            // weights -> packed bf16 P^T operands (exponents <= kLazy; v_exp_f32
-            // flushes results below 2^-126 to zero, which is harmless).  Each
-            // stage runs over all 32 scores in place, so the vector ALU sees 32
-            // independent operations at a time instead of one short chain.
-            const float off = m_run == -INFINITY ? 0.f : -m_run;
-    #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-    #pragma unroll
-                for (int v = 0; v < 16; ++v) S[kt][v] = fmaf(S[kt][v], cl, off);
+                for (int v = 0; v < 16; ++v) {
+                    const int kpos = sPos[st][32 * kt + 16 * (v >> 3) + 8 * h + (v & 7)];
+                    S[kt][v] = (kpos <= pq && kpos > lowq) ? S[kt][v] : -INFINITY;
+                }
+        };
+        // Weights -> packed bf16 P^T operands, in place over all 32 scores per
+        // stage (32 independent operations at a time for the vector ALU); returns
+        // the lane's sum of the weights that P.V uses.  v_exp_f32 flushes results
+        // below 2^-126 to zero, which is harmless.
+        auto weights = [&](f32x16 (&S)[2], u32x4 (&Pk)[4]) {
     #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
     #pragma unroll
@@ -404,25 +391,66 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     #pragma unroll
                 for (int w = 0; w < 4; ++w)
                     Pk[s2][w] = pack_bf16x2(S[s2 >> 1][8 * (s2 & 1) + 2 * w], S[s2 >> 1][8 * (s2 & 1) + 2 * w + 1]);
-            float r4[4] = {0.f, 0.f, 0.f, 0.f};              // the row sum of the weights P.V uses
+            float r4[4] = {0.f, 0.f, 0.f, 0.f};
     #pragma unroll
             for (int s2 = 0; s2 < 4; ++s2)
     #pragma unroll
                 for (int w = 0; w < 4; ++w) r4[w] = sum_bf16x2(Pk[s2][w], r4[w]);
-            const float rs = (r4[0] + r4[1]) + (r4[2] + r4[3]);
+            return (r4[0] + r4[1]) + (r4[2] + r4[3]);
+        };
+        auto scale_shift = [&](f32x16 (&S)[2], float a, float b) {
+    #pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+    #pragma unroll
+                for (int v = 0; v < 16; ++v) S[kt][v] = fmaf(S[kt][v], a, b);
+        };
+        auto softmax = [&](int st, bool full, f32x16 (&S)[2], u32x4 (&Pk)[4]) {
+            if (!full) mask(st, S);
+            const float m_fin = m_ref == -INFINITY ? 0.f : m_ref;
+            if (!kQScale) scale_shift(S, cl, -m_fin);
+            float rs = weights(S, Pk);
+            if (__any(!(rs <= kMaxWeight) || m_ref == -INFINITY)) {
+                qk(st, S);                                   // the scores again
+                if (!full) mask(st, S);
+                float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    #pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+    #pragma unroll
+                    for (int v = 0; v < 16; ++v) m4[(kt * 16 + v) & 3] = fmaxf(m4[(kt * 16 + v) & 3], S[kt][v]);
+                float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+                mx = fmaxf(mx, xor_lane(mx, 32));           // the row's other 32 keys
+                const float m_new = fmaxf(m_ref, kQScale ? mx + m_fin : mx * cl);
+                if (m_new != -INFINITY) {
+                    // nothing is accumulated while m_ref is -inf
+                    const float alpha = m_ref == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+                    l_run *= alpha;
+    #pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+                    m_ref = m_new;
+                    if (kQScale) {
+    #pragma unroll
+                        for (int v = 0; v < 16; ++v) negm[v] = -m_new;
+                    }
+                }
+                const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+                if (kQScale) {
+    #pragma unroll
+                    for (int kt = 0; kt < 2; ++kt) S[kt] += m_fin - m_use;
+                } else {
+                    scale_shift(S, cl, -m_use);
+                }
+                rs = weights(S, Pk);
+            }
             l_run += rs;
         };
 
         static_assert(NBUF == 4, "tiles m-1 .. m+2 occupy the four stages around phase 2m");
-        if (n_tiles > 0) {
-            load_entry_block(0);
-            wait_vmcnt<0>();
-            lds_barrier();
-            load_entry_block(1);
-        }
     #pragma unroll
         for (int j = 0; j < NBUF - 1; ++j)
-            if (j < n_tiles) issue(j, j);
+            if (j < n_tiles) {
+                fetch(j);
+                issue(j, j);
+            }
         if (n_tiles > 0) {
             if (n_tiles > 2) wait_vmcnt<2 * IPW>();
             else if (n_tiles > 1) wait_vmcnt<IPW>();
@@ -434,7 +462,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int n_phases = n_tiles > 0 ? 2 * n_tiles + (kPingPong ? 2 : 1) : 0;
         for (int k = 0; k < n_phases; ++k) {
             const int p2 = k >> 1;
-            if (!(k & 1) && p2 >= 1 && p2 + 2 < n_tiles) issue(p2 + 2, (p2 + 2) % NBUF);
             if (kPingPong) {
                 if (!(k & 1) && grp == 1 && p2 < n_tiles && (sFlags[p2 % NBUF] >> 1))
                     fixup(p2 % NBUF, 4 * 64, 4 * 64);        // group 1 is in its vector-ALU phase
@@ -446,15 +473,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             if (((k + grp) & 1) == 0) {                      // matrix-core phase
                 if (j >= 1) pv((j - 1) % NBUF, Pk);
                 if (j < n_tiles) qk(j % NBUF, S);
-            } else if (j >= 0 && j < n_tiles) {              // vector-ALU phase
-                // the softmax wave issues first: its SIMD partner's MFMA stream
-                // would otherwise take most issue cycles from it
-                if (kPrioSoftmax) __builtin_amdgcn_s_setprio(kPrioSoftmax);
-                softmax(j % NBUF, sFlags[j % NBUF] & 1, S, Pk);
-                if (kPrioSoftmax) __builtin_amdgcn_s_setprio(0);
+            } else {                                         // vector-ALU phase
+                const bool act = j >= 0 && j < n_tiles;
+                const bool full = act && (sFlags[j % NBUF] & 1);
+                // Each group issues its share of tile p2 + 2 at the start of
+                // its vector phase (group 1 in phase 2 p2, group 0 one phase
+                // later): the loads of the two groups never queue at the
+                // address unit together, and the matrix cores of the SIMD keep
+                // working for the other group meanwhile.
+                if (p2 >= 1 && p2 + 2 < n_tiles) issue(p2 + 2, (p2 + 2) % NBUF);
+                if (act) {
+                    // the softmax wave issues first: its SIMD partner's MFMA
+                    // stream would otherwise take most issue cycles from it
+                    if (kPrioSoftmax) __builtin_amdgcn_s_setprio(kPrioSoftmax);
+                    softmax(j % NBUF, full, S, Pk);
+                    if (kPrioSoftmax) __builtin_amdgcn_s_setprio(0);
+                }
             }
             if (k & 1) {                                     // tile (k+1)/2 is used from the next phase on
                 const int m = (k + 1) >> 1;
+                // the entries of both groups' next issue (tile m + 2); the
+                // barrier below waits for them
+                if (m + 2 < n_tiles) fetch(m + 2);
                 if (m < n_tiles) {
                     if (m + 1 < n_tiles) wait_vmcnt<IPW>();
                     else wait_vmcnt<0>();
@@ -470,7 +510,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         // ---- epilogue
         const float l = l_run + xor_lane(l_run, 32);
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        const float lse = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+        const float lse = l > 0.f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
         if (!row_ok) continue;
         if (ns == 1) {
             bf16 *orow = P.out + ((int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g) * D;
