@@ -264,9 +264,8 @@ __global__ __launch_bounds__(NWD * 64) __attribute__((amdgpu_waves_per_eu(3, 3))
 }
 
 // Merges the splits of every split row: one wave per (row, head).  The lanes
-// read the split LSEs together (lane s, s+64, ...), form the weights
-// e^{lse_s - M} in LDS, then each lane accumulates its D/64 dims over the
-// splits: O = sum_s w_s o_s / sum_s w_s.
+// read the split LSEs together (lane s, s+64, ...) and form the weights
+// e^{lse_s - M} in LDS; then O = sum_s w_s o_s / sum_s w_s.
 template <int D, bool INL>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams P, InlinePlan L) {
     __shared__ float sw[kMaxSplits];
@@ -289,21 +288,36 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams P, Inline
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) z += __shfl_xor(z, m, 64);
     __syncthreads();
-    constexpr int DPL = D / 64;
-    float o[DPL];
+    // lane (g, c) accumulates dims 8c .. 8c+7 over splits g, g + SG, ..., so the
+    // loads of all splits are in flight together; the groups are then summed
+    constexpr int CH = D / 8, SG = 64 / CH;
+    const int c = lane % CH, sg = lane / CH;
+    float o[8];
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) o[i] = 0.f;
-    const float *src = P.part_o + (part0 * G + hh) * D + DPL * lane;
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+    const float *src = P.part_o + (part0 * G + hh) * D + 8 * c;
 #pragma unroll 8
-    for (int s = 0; s < ns; ++s) {
+    for (int s = sg; s < ns; s += SG) {
         const float wgt = sw[s];
+        const f32x4 a0 = *(const f32x4 *)(src + (int64_t)s * G * D), a1 = *(const f32x4 *)(src + (int64_t)s * G * D + 4);
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) o[i] += wgt * src[(int64_t)s * G * D + i];
+        for (int e = 0; e < 4; ++e) {
+            o[e] += wgt * a0[e];
+            o[4 + e] += wgt * a1[e];
+        }
     }
+#pragma unroll
+    for (int off = CH; off < 64; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], off, 64);
     const float inv = z > 0.f ? 1.f / z : 0.f;
     const int64_t orow = (int64_t)seq * P.Hq + (int64_t)slot * G + hh;
+    if (sg == 0) {
+        u32x4 pk;
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) P.out[orow * D + DPL * lane + i] = f32_to_bf16(o[i] * inv);
+        for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(o[2 * i] * inv, o[2 * i + 1] * inv);
+        *(u32x4 *)(P.out + orow * D + 8 * c) = pk;
+    }
     if (P.lse && lane == 0) P.lse[orow] = z > 0.f ? M + logf(z) : -INFINITY;
 }
 

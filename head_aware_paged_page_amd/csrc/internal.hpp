@@ -54,6 +54,7 @@ struct Plan {
     int chunk_pages = 0;     // pages per kv split (INT32_MAX = no split)
     int64_t n_items = 0;     // work items (= workgroups of the attention kernel)
     int64_t n_parts = 0;     // work items whose result is a partial to merge
+    int merge_rows = 0;      // prefill: most query rows one split item merges
     // Work items are numbered long-first: the items of split rows (row order),
     // then those of unsplit rows.  item_ptr[r] / item_ptr2[r] = first item of
     // row r in the first / second range (zero-length for rows of the other).

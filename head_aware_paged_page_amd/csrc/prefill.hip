@@ -545,20 +545,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // Combines the kv splits of every split q-tile: O = sum_s e^{lse_s-M} o_s / sum_s e^{lse_s-M}.
 // Launched over the same work items: item (q-tile, split s) merges rows
 // [s * ceil(rows/ns), (s+1) * ceil(rows/ns)) of its q-tile, so all splits share
-// the work.  Sixteen lanes per row (four rows per wave, sixteen per workgroup
-// pass); each lane reads its row's split LSEs (the same addresses for the row's
-// lanes), then accumulates its D/16 dims over the splits.  The partials are
-// normalised (|o| <= max |v|), so fp16 keeps them to about 5e-4 relative.
+// the work, with blockIdx.y spreading an item's rows over workgroups so that
+// every wave merges one row.  The lanes first read the row's split LSEs
+// together (lane s, s + 64, ...) for the max and the normaliser (online, then
+// combined across lanes), then lane (g, c) accumulates dims 8c .. 8c+7 over
+// splits g, g + 64/(D/8), ..., so the loads of all splits are in flight
+// together; the split groups are summed by lane shuffles.  The partials are normalised (|o| <= max |v|), so fp16 keeps
+// them to about 5e-4 relative.
 template <int D>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, int BM) {
-    constexpr int LPR = 16, DPL = D / LPR;           // lanes per row, dims per lane
-    static_assert(DPL % 4 == 0, "whole float4 loads per lane");
+    constexpr int CH = D / 8, SG = 64 / CH;          // dim chunks of 8, split groups
     int r, local;
     item_of(P.item_ptr, P.item_ptr2, P.n_rows, blockIdx.x, &r, &local);
     const int ns = P.nsplit[r];
     if (ns == 1) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int sub = lane / LPR, li = lane % LPR;
+    const int c = lane % CH, sg = lane / CH;
     const int qt = local / ns, sp_i = local % ns;
     const int seq = r % P.n_seq, slot = r / P.n_seq;
     const int tok_base = P.tok_ptr[seq];
@@ -568,40 +570,51 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, int
     const int per = (nrows + ns - 1) / ns;
     const int r0 = sp_i * per, r1 = min(nrows, r0 + per);
     const int64_t part0 = (int64_t)P.part_ptr[r] + (int64_t)qt * ns;   // splits part0 .. part0+ns-1
-    for (int row = r0 + 4 * wave + sub; row - sub < r1; row += 16) {
-        if (row >= r1) continue;
+    for (int row = r0 + 4 * blockIdx.y + wave; row < r1; row += 4 * gridDim.y) {
         const float *lse = P.part_lse + part0 * BM + row;
-        float M = -INFINITY;
-        for (int s = 0; s < ns; ++s) M = fmaxf(M, lse[(int64_t)s * BM]);
-        float o[DPL], z = 0.f;
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) o[i] = 0.f;
-        if (M != -INFINITY) {
-            const _Float16 *src = P.part_o + (part0 * BM + row) * D + DPL * li;
-#pragma unroll 4
-            for (int s = 0; s < ns; ++s) {
-                const float wgt = __expf(lse[(int64_t)s * BM] - M);
-                z += wgt;
-#pragma unroll
-                for (int i = 0; i < DPL / 4; ++i) {
-                    const f32x4 v = __builtin_convertvector(*(const f16x4 *)(src + (int64_t)s * BM * D + 4 * i), f32x4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) o[4 * i + e] += wgt * v[e];
-                }
+        float m = -INFINITY, z = 0.f;                // this lane's splits, online
+        for (int s = lane; s < ns; s += 64) {
+            const float x = lse[(int64_t)s * BM];
+            if (x > m) {
+                z = z * __expf(m - x) + 1.f;
+                m = x;
+            } else if (x != -INFINITY) {
+                z += __expf(x - m);
             }
         }
+        float M = m;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+        z = M == -INFINITY ? 0.f : z * __expf(m - M);   // a lane with no split has z = 0
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = 0.f;
+        if (M != -INFINITY) {
+            const _Float16 *src = P.part_o + (part0 * BM + row) * D + 8 * c;
+#pragma unroll 8
+            for (int s = sg; s < ns; s += SG) {
+                const float wgt = __expf(lse[(int64_t)s * BM] - M);
+                const f16x8 v = *(const f16x8 *)(src + (int64_t)s * BM * D);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] += wgt * (float)v[e];
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+#pragma unroll
+        for (int off = CH; off < 64; off <<= 1)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], off, 64);
         const float inv = z > 0.f ? 1.f / z : 0.f;
         const int tq = row / P.G, g = row % P.G;
         const int64_t orow = (int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * P.G + g;
-        uint32_t pk[DPL / 2];
+        if (sg == 0) {
+            u32x4 pk;
 #pragma unroll
-        for (int i = 0; i < DPL / 2; ++i) pk[i] = pack_bf16x2(o[2 * i] * inv, o[2 * i + 1] * inv);
-        if (DPL == 8) {
-            *(u32x4 *)(P.out + orow * D + DPL * li) = u32x4{pk[0], pk[1 % (DPL / 2)], pk[2 % (DPL / 2)], pk[3 % (DPL / 2)]};
-        } else {
-            *(u32x2 *)(P.out + orow * D + DPL * li) = u32x2{pk[0], pk[1 % (DPL / 2)]};
+            for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(o[2 * i] * inv, o[2 * i + 1] * inv);
+            *(u32x4 *)(P.out + orow * D + 8 * c) = pk;
         }
-        if (P.lse && li == 0) P.lse[orow] = z > 0.f ? M + logf(z) : -INFINITY;
+        if (P.lse && lane == 0) P.lse[orow] = z > 0.f ? M + logf(z) : -INFINITY;
     }
 }
 
@@ -706,13 +719,13 @@ int launch_prefill(const AttnArgs &a, const Plan &p, int64_t n_tok, hipStream_t 
     P.scale_log2 = a.scale * kLog2e;
     P.work_ctr = (int *)(w + p.off_zero + 128);
     P.n_items = (int)p.n_items;
-    const dim3 grid((unsigned)p.n_items);
+    const dim3 mgrid((unsigned)p.n_items, (unsigned)std::max(1, (p.merge_rows + 3) / 4));
     const dim3 grid_persist((unsigned)std::min<int64_t>(p.n_items, kPlanCUs));
 #define SP_PREFILL_CASE(DD, PSV)                                                                        \
     if (a.head_dim == DD && a.page_size == PSV) {                                                       \
         hipLaunchKernelGGL((prefill_bf16_kernel<DD, 8, PSV, 4>), grid_persist, dim3(512), 0, stream, P); \
         if (p.n_parts)                                                                                  \
-            hipLaunchKernelGGL(prefill_merge_kernel<DD>, grid, dim3(256), 0, stream, P, p.rows_per_tile); \
+            hipLaunchKernelGGL(prefill_merge_kernel<DD>, mgrid, dim3(256), 0, stream, P, p.rows_per_tile); \
     }
     SP_PREFILL_CASE(128, 16) else SP_PREFILL_CASE(128, 32) else SP_PREFILL_CASE(128, 64)
     else SP_PREFILL_CASE(64, 16) else SP_PREFILL_CASE(64, 32) else SP_PREFILL_CASE(64, 64)

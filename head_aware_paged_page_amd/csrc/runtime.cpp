@@ -171,7 +171,10 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
                         (long long)e_row);
         row_items((int)e_row, nq, p.chunk_pages, &ns, &it);
         items += it;
-        if (ns > 1) parts += it;
+        if (ns > 1) {
+            parts += it;
+            p.merge_rows = std::max(p.merge_rows, (p.rows_per_tile + ns - 1) / ns);
+        }
     }
     if (items > INT32_MAX) return fail(SP_EINVAL, "too many work items");
     p.n_items = items;
