@@ -159,51 +159,35 @@ __device__ __forceinline__ void visible_range(const int4 *__restrict__ E, int e_
     *hi_out = __builtin_amdgcn_readfirstlane(hi);
 }
 
-// One 16-byte global->LDS load per lane (gfx950 global_load_lds_dwordx4): lane l
-// of the wave writes LDS bytes [dst + 16 l, dst + 16 l + 16); dst must be
-// wave-uniform.  The builtin exists only for the device target, so the host
-// pass (which must still emit the kernel's launch stub) sees a no-op.
+// One 16-byte global->LDS load per lane through a buffer resource (gfx950
+// buffer_load_dwordx4 ... lds): lane l reads bytes [voff_l, voff_l + 16) of the
+// range [base, base + bytes) and the wave writes LDS bytes [dst, dst + 1024),
+// lane l at dst + 16 l.  base, bytes and dst must be wave-uniform; a lane
+// whose voff_l + 16 passes `bytes` gets zeros (the buffer range check).
+//
+// Two properties matter to the kernels that keep several tiles in flight:
+//  * The LDS destination reaches the builtin as a bare LDS byte address that
+//    the compiler cannot trace to a variable, so it inserts no waits for the
+//    load before later LDS reads: the caller must wait (s_waitcnt vmcnt)
+//    before reading what it writes.
+//  * It is a buffer (MUBUF) instruction, not a FLAT one.  While a FLAT-encoded
+//    load that writes LDS (global_load_lds) is outstanding, the compiler
+//    treats the LDS counter as unordered and turns every wait for an LDS read
+//    into lgkmcnt(0), which drains the operand reads queued ahead of the
+//    matrix instructions; with the buffer form those waits stay exact.
+// The builtins exist only for the device target, so the host pass (which must
+// still emit the kernel's launch stub) sees a no-op.
 #if defined(__HIP_DEVICE_COMPILE__)
-#define SP_LDS_DMA16(src, dst) __builtin_amdgcn_global_load_lds((src), (dst), 16, 0, 0)
-// The same load with its LDS destination given as a bare LDS byte address that
-// the compiler cannot trace to a variable.  The compiler then attributes the
-// load to no particular LDS array and inserts no waits for it before later LDS
-// reads: the caller must wait (s_waitcnt vmcnt) before reading what it writes.
-// Kernels that keep several tiles in flight use it so that reading one tile
-// does not wait for the loads of the next ones.
-__device__ __forceinline__ void lds_dma16_unordered(const void *src, const void *dst) {
+__device__ __forceinline__ void lds_dma16_buf(const void *base, uint32_t bytes, uint32_t voff, const void *dst) {
     uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);   // wave-uniform
     asm volatile("" : "+s"(a));
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(uintptr_t)a, 16, 0, 0);
+    // word 3 of the resource: 32-bit data format, the raw-buffer setting of the gfx9 family
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(uintptr_t)a, 16, voff, 0, 0, 0);
 }
 #else
-#define SP_LDS_DMA16(src, dst) ((void)(src), (void)(dst))
-__device__ __forceinline__ void lds_dma16_unordered(const void *, const void *) {}
+__device__ __forceinline__ void lds_dma16_buf(const void *, uint32_t, uint32_t, const void *) {}
 #endif
-
-// Scalar (constant-cache) loads of workgroup-uniform table entries.  Kernels
-// that stream tiles with global->LDS loads keep every other vector load out of
-// their main loop (one in-order counter tracks both), so the page entries go
-// through the scalar path; each block waits for its own result.
-__device__ __forceinline__ int4 sload_int4(const int4 *p) {
-    typedef int v4i __attribute__((ext_vector_type(4)));
-    v4i r = {0, 0, 0, 0};
-#if defined(__HIP_DEVICE_COMPILE__)   // the host pass must not see amdgcn register constraints
-    asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
-#endif
-    return int4{r.x, r.y, r.z, r.w};
-}
-
-__device__ __forceinline__ void sload_int4x4(const int4 *p, int4 &a, int4 &b, int4 &c, int4 &d) {
-    typedef int v16i __attribute__((ext_vector_type(16)));
-    v16i r = {0};
-#if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("s_load_dwordx16 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
-#endif
-    a = int4{r[0], r[1], r[2], r[3]};
-    b = int4{r[4], r[5], r[6], r[7]};
-    c = int4{r[8], r[9], r[10], r[11]};
-    d = int4{r[12], r[13], r[14], r[15]};
-}
 
 }  // namespace sp

@@ -111,9 +111,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     static_assert(RV <= D && D % RV == 0, "a 1 KB block of V^T rows must stay inside one page");
     __shared__ __attribute__((aligned(1024))) bf16 sK[NBUF][BN * D];
     __shared__ __attribute__((aligned(1024))) bf16 sV[NBUF][D * BN];
-    __shared__ int sPos[NBUF][BN];
-    __shared__ int sFlags[NBUF];    // bit 0: no bounds needed; bits 1..ppt: pages with empty key slots
-    __shared__ int sNv[NBUF][4];    // tokens held by each page of the tile
+    __shared__ int sPos[NBUF][BN];  // key positions of a tile that needs bounds
+    __shared__ int sNv[NBUF][4];    // tokens held by each page of a tile with empty key slots
 
     __shared__ int s_item;
 
@@ -219,13 +218,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             for (int pg = 0; pg < ppt; ++pg) enx[pg] = Ec[min(my_lo + t * ppt + pg, my_hi - 1)];
         };
         // Tile issue.  Every wave loads its own 1 KB blocks of K and V^T (each
-        // inside one page, so it needs that page's entry only).  One wave per
-        // tile (rotating) writes the key positions, each page's token count and
-        // the tile's flags: bit 0 = every key exists and is visible to every
-        // query of the q-tile (no bounds needed), bit 1 + pg = page pg has key
-        // slots without a token (their V^T cells must be zeroed).  The entries
-        // are sanitised (pages past the split or outside the pool read as
-        // {phys 0, no tokens}) and picked on the scalar unit.
+        // inside one page, so it needs that page's entry only), and derives the
+        // tile's flags from the entries on the scalar unit into its own ring
+        // `flr` (8 bits per stage): bit 0 = every key exists and is visible to
+        // every query of the q-tile (no bounds needed), bit 1 + pg = page pg has
+        // key slots without a token (their V^T cells must be zeroed).  Only for
+        // a tile that needs them does one wave (rotating) write the key
+        // positions (bounds) or each page's token count (zeroing) to LDS.  The
+        // entries are sanitised (pages past the split or outside the pool read
+        // as {phys 0, no tokens}) and picked on the scalar unit.
+        uint32_t flr = 0;
         auto issue = [&](int t, int st) {
             // vector values (element = page of the tile), so that picking a
             // page by a run-time index selects among registers
@@ -238,36 +240,42 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 pst[i] = ok ? en.y : 0;
                 nvl[i] = ok ? min(en.z, PS) : 0;
             }
+            // Positions inside a page are consecutive, so the bounds test of the
+            // whole tile needs only the first position and token count of each
+            // page: no key slot is empty, the last key is at or before the first
+            // query, and (local) the first key is inside the last query's window.
+            bool all_tok = true;
+            int pmask = 0, pos_min = INT32_MAX, pos_max = INT32_MIN;
+    #pragma unroll
+            for (int i = 0; i < ppt; ++i) {
+                all_tok = all_tok && nvl[i] == PS;
+                pmask |= (nvl[i] < PS ? 1 : 0) << i;
+                pos_min = min(pos_min, pst[i]);
+                pos_max = max(pos_max, pst[i] + PS - 1);
+            }
+            const bool full = all_tok && pos_max <= p0 && (!is_local || pos_min > p_last - W);
+            const uint32_t fl = (full ? 1u : 0u) | (uint32_t)(pmask << 1);
+            flr = __builtin_amdgcn_readfirstlane((flr & ~(0xffu << (8 * st))) | (fl << (8 * st)));
             if (wave == t % NW) {
                 const int pgl = lane / PS, tk = lane % PS;
                 const int nv = nvl[pgl];
-                const int pos = tk < nv ? pst[pgl] + tk : kPosInvalid;
-                sPos[st][lane] = pos;
-                if (tk == 0) sNv[st][pgl] = nv;
-                const bool valid = pos != kPosInvalid;
-                const bool full = __all(valid && pos <= p0 && (!is_local || pos > p_last - W));
-                uint32_t pmask = 0;                          // pages with an empty key slot
-    #pragma unroll
-                for (int pg = 0; pg < ppt; ++pg) pmask |= (nvl[pg] < PS ? 1u : 0u) << pg;
-                if (lane == 0) sFlags[st] = (full ? 1 : 0) | (int)(pmask << 1);
+                if (!full) sPos[st][lane] = tk < nv ? pst[pgl] + tk : kPosInvalid;
+                if (pmask && tk == 0) sNv[st][pgl] = nv;
             }
     #pragma unroll
             for (int q = 0; q < KIW; ++q) {
-                const char *base = (const char *)(P.kp + (int64_t)ph[kpg[q]] * (PS * D));
-                lds_dma16_unordered(base + koff[q], &sK[st][(wave * KIW + q) * 512]);
+                lds_dma16_buf(P.kp + (int64_t)ph[kpg[q]] * (PS * D), PS * D * 2, koff[q], &sK[st][(wave * KIW + q) * 512]);
             }
     #pragma unroll
             for (int q = 0; q < VIW; ++q) {
-                const char *base = (const char *)(P.vp + (int64_t)ph[vpg[q]] * (D * PS));
-                lds_dma16_unordered(base + voff[q], &sV[st][(wave * VIW + q) * 512]);
+                lds_dma16_buf(P.vp + (int64_t)ph[vpg[q]] * (D * PS), D * PS * 2, voff[q], &sV[st][(wave * VIW + q) * 512]);
             }
         };
         // Zero the V^T slots of keys that hold no token (past a page's n_valid, or
         // pages past the split): their weight is zero, but 0 * NaN is not.  The
         // tokens of a page are a prefix of its slots, so a 16-byte cell of 8
         // keys keeps its first clamp(n_valid - 8c, 0, 8) values.
-        auto fixup = [&](int st, int t0, int nt) {     // threads t0 .. t0+nt-1 of the workgroup
-            const int pmask = sFlags[st] >> 1;
+        auto fixup = [&](int st, int pmask, int t0, int nt) {   // threads t0 .. t0+nt-1 of the workgroup
     #pragma unroll
             for (int pg = 0; pg < ppt; ++pg) {
                 if (!((pmask >> pg) & 1)) continue;
@@ -463,10 +471,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         for (int k = 0; k < n_phases; ++k) {
             const int p2 = k >> 1;
             if (kPingPong) {
-                if (!(k & 1) && grp == 1 && p2 < n_tiles && (sFlags[p2 % NBUF] >> 1))
-                    fixup(p2 % NBUF, 4 * 64, 4 * 64);        // group 1 is in its vector-ALU phase
-            } else if ((k & 1) && p2 < n_tiles && (sFlags[p2 % NBUF] >> 1)) {
-                fixup(p2 % NBUF, 0, NW * 64);                // all waves, before P.V(p2) two phases on
+                const int pm = (flr >> (8 * (p2 % NBUF) + 1)) & 0x7f;
+                if (!(k & 1) && grp == 1 && p2 < n_tiles && pm)
+                    fixup(p2 % NBUF, pm, 4 * 64, 4 * 64);    // group 1 is in its vector-ALU phase
+            } else {
+                const int pm = (flr >> (8 * (p2 % NBUF) + 1)) & 0x7f;
+                if ((k & 1) && p2 < n_tiles && pm) fixup(p2 % NBUF, pm, 0, NW * 64);   // all waves, before P.V(p2) two phases on
             }
 
             const int j = (k - grp) >> 1;                    // this group's tile in this phase
@@ -475,7 +485,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 if (j < n_tiles) qk(j % NBUF, S);
             } else {                                         // vector-ALU phase
                 const bool act = j >= 0 && j < n_tiles;
-                const bool full = act && (sFlags[j % NBUF] & 1);
+                const bool full = act && ((flr >> (8 * (j % NBUF))) & 1);
                 // Each group issues its share of tile p2 + 2 at the start of
                 // its vector phase (group 1 in phase 2 p2, group 0 one phase
                 // later): the loads of the two groups never queue at the
