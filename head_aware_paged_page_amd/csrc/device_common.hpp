@@ -161,12 +161,13 @@ __device__ __forceinline__ void visible_range(const int4 *__restrict__ E, int e_
 
 // One 16-byte global->LDS load per lane through a buffer resource (gfx950
 // buffer_load_dwordx4 ... lds): lane l reads bytes [voff_l, voff_l + 16) of the
-// range [base, base + bytes) and the wave writes LDS bytes [dst, dst + 1024),
-// lane l at dst + 16 l.  base, bytes and dst must be wave-uniform; a lane
-// whose voff_l + 16 passes `bytes` gets zeros (the buffer range check).
+// range [base, base + bytes) and the wave writes LDS bytes [lds, lds + 1024)
+// (lds = LDS byte address), lane l at lds + 16 l.  base, bytes and lds must be
+// wave-uniform; a lane whose voff_l + 16 passes `bytes` gets zeros (the buffer
+// range check).
 //
 // Two properties matter to the kernels that keep several tiles in flight:
-//  * The LDS destination reaches the builtin as a bare LDS byte address that
+//  * The LDS destination reaches the builtin as a bare byte address that
 //    the compiler cannot trace to a variable, so it inserts no waits for the
 //    load before later LDS reads: the caller must wait (s_waitcnt vmcnt)
 //    before reading what it writes.
@@ -178,8 +179,8 @@ __device__ __forceinline__ void visible_range(const int4 *__restrict__ E, int e_
 // The builtins exist only for the device target, so the host pass (which must
 // still emit the kernel's launch stub) sees a no-op.
 #if defined(__HIP_DEVICE_COMPILE__)
-__device__ __forceinline__ void lds_dma16_buf(const void *base, uint32_t bytes, uint32_t voff, const void *dst) {
-    uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);   // wave-uniform
+__device__ __forceinline__ void lds_dma16_buf(const void *base, uint32_t bytes, uint32_t voff, uint32_t lds) {
+    uint32_t a = __builtin_amdgcn_readfirstlane(lds);   // wave-uniform
     asm volatile("" : "+s"(a));
     // word 3 of the resource: 32-bit data format, the raw-buffer setting of the gfx9 family
     const __amdgpu_buffer_rsrc_t rs =
@@ -187,7 +188,7 @@ __device__ __forceinline__ void lds_dma16_buf(const void *base, uint32_t bytes, 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(uintptr_t)a, 16, voff, 0, 0, 0);
 }
 #else
-__device__ __forceinline__ void lds_dma16_buf(const void *, uint32_t, uint32_t, const void *) {}
+__device__ __forceinline__ void lds_dma16_buf(const void *, uint32_t, uint32_t, uint32_t) {}
 #endif
 
 }  // namespace sp

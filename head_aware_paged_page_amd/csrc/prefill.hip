@@ -121,17 +121,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     auto swz_k = [](int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
     auto swz_v = [](int d) { return PS == 16 ? 0 : PS == 32 ? ((d >> 2) & 3) : ((d >> 1) & 7); };
 
-    // Per-lane source offsets (bytes within a page) and page slots of this
-    // wave's K and V^T blocks: fixed for the launch.
+    // This wave's K and V^T blocks of a tile: per-lane source offsets (bytes
+    // within a page), the page of the tile they lie in (the same for all of
+    // them) and their LDS byte addresses in stage 0.  Fixed for the launch.
+    constexpr int BPG = PS * D / 512;                                 // 1 KB blocks per page, K and V^T alike
+    static_assert(KIW == VIW && BPG % KIW == 0, "a wave's blocks of a tile must share one page");
+    constexpr uint32_t kStageBytes = BN * D * 2, kPageBytes = PS * D * 2;
     uint32_t koff[KIW], voff[VIW];
-    int kpg[KIW], vpg[VIW];
 #pragma unroll
     for (int q = 0; q < KIW; ++q) {
         const int blk = wave * KIW + q;
         const int row = blk * RK + lane / CPK;                    // key row of the tile
         const int c = (lane % CPK) ^ swz_k(row);
         koff[q] = (uint32_t)(((row % PS) * D + 8 * c) * 2);
-        kpg[q] = __builtin_amdgcn_readfirstlane(blk * RK / PS);
     }
 #pragma unroll
     for (int q = 0; q < VIW; ++q) {
@@ -139,8 +141,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int d = (blk % BPP) * RV + lane / CPV;              // dim row within the page
         const int c = (lane % CPV) ^ swz_v(d);
         voff[q] = (uint32_t)((d * PS + 8 * c) * 2);
-        vpg[q] = __builtin_amdgcn_readfirstlane(blk / BPP);
     }
+    const int pw = __builtin_amdgcn_readfirstlane(wave * KIW / BPG);
+    const uint32_t lds_k0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&sK[0][wave * KIW * 512]);
+    const uint32_t lds_v0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&sV[0][wave * VIW * 512]);
 
     // Persistent workgroups (one per CU) take the work items in their long-first
     // order from a counter: the hardware dispatcher places workgroups in order
@@ -217,59 +221,55 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     #pragma unroll
             for (int pg = 0; pg < ppt; ++pg) enx[pg] = Ec[min(my_lo + t * ppt + pg, my_hi - 1)];
         };
-        // Tile issue.  Every wave loads its own 1 KB blocks of K and V^T (each
-        // inside one page, so it needs that page's entry only), and derives the
-        // tile's flags from the entries on the scalar unit into its own ring
-        // `flr` (8 bits per stage): bit 0 = every key exists and is visible to
-        // every query of the q-tile (no bounds needed), bit 1 + pg = page pg has
-        // key slots without a token (their V^T cells must be zeroed).  Only for
-        // a tile that needs them does one wave (rotating) write the key
-        // positions (bounds) or each page's token count (zeroing) to LDS.  The
-        // entries are sanitised (pages past the split or outside the pool read
-        // as {phys 0, no tokens}) and picked on the scalar unit.
+        // Tile issue.  Every wave loads its own 1 KB blocks of K and V^T (all
+        // inside page pw of the tile), and derives the tile's flags from the
+        // entries on the scalar unit into its own ring `flr` (8 bits per
+        // stage): bit 0 = every key exists and is visible to every query of
+        // the q-tile (no bounds needed), bit 1 + pg = page pg has key slots
+        // without a token (their V^T cells must be zeroed).  Only for a tile
+        // that needs them does one wave (rotating) write the key positions
+        // (bounds) or each page's token count (zeroing) to LDS.  Pages past
+        // the split or outside the pool count as {phys 0, no tokens}.
         uint32_t flr = 0;
         auto issue = [&](int t, int st) {
-            // vector values (element = page of the tile), so that picking a
-            // page by a run-time index selects among registers
-            i32x4 ph = {0, 0, 0, 0}, pst = {0, 0, 0, 0}, nvl = {0, 0, 0, 0};
+            const int e0 = t * ppt, n_e = my_hi - my_lo;
+            // token counts and first positions as vector values (element =
+            // page), so that the bounds writer can pick them by lane
+            i32x4 nvl = {0, 0, 0, 0}, pst = {0, 0, 0, 0};
+            int pmask = 0;
     #pragma unroll
             for (int i = 0; i < ppt; ++i) {
-                const i32x4 en = enx[i];
-                const bool ok = my_lo + t * ppt + i < my_hi && en.x >= 0 && en.x < n_phys32;
-                ph[i] = ok ? en.x : 0;
-                pst[i] = ok ? en.y : 0;
-                nvl[i] = ok ? min(en.z, PS) : 0;
-            }
-            // Positions inside a page are consecutive, so the bounds test of the
-            // whole tile needs only the first position and token count of each
-            // page: no key slot is empty, the last key is at or before the first
-            // query, and (local) the first key is inside the last query's window.
-            bool all_tok = true;
-            int pmask = 0, pos_min = INT32_MAX, pos_max = INT32_MIN;
-    #pragma unroll
-            for (int i = 0; i < ppt; ++i) {
-                all_tok = all_tok && nvl[i] == PS;
+                const bool ok = e0 + i < n_e && (uint32_t)enx[i].x < (uint32_t)n_phys32;
+                nvl[i] = ok ? min(enx[i].z, PS) : 0;
+                pst[i] = enx[i].y;
                 pmask |= (nvl[i] < PS ? 1 : 0) << i;
-                pos_min = min(pos_min, pst[i]);
-                pos_max = max(pos_max, pst[i] + PS - 1);
             }
-            const bool full = all_tok && pos_max <= p0 && (!is_local || pos_min > p_last - W);
+            // A table row ascends by position and a page's positions are
+            // consecutive, so with every slot holding a token the tile spans
+            // [first position of page 0, last of page ppt-1]: no bounds are
+            // needed when that ends at or before the first query and (local)
+            // starts inside the last query's window.
+            const bool full = pmask == 0 && pst[ppt - 1] + (PS - 1) <= p0 && (!is_local || pst[0] > p_last - W);
             const uint32_t fl = (full ? 1u : 0u) | (uint32_t)(pmask << 1);
             flr = __builtin_amdgcn_readfirstlane((flr & ~(0xffu << (8 * st))) | (fl << (8 * st)));
-            if (wave == t % NW) {
+            if ((!full || pmask) && wave == t % NW) {
                 const int pgl = lane / PS, tk = lane % PS;
                 const int nv = nvl[pgl];
                 if (!full) sPos[st][lane] = tk < nv ? pst[pgl] + tk : kPosInvalid;
                 if (pmask && tk == 0) sNv[st][pgl] = nv;
             }
+            int own = enx[0].x;
     #pragma unroll
-            for (int q = 0; q < KIW; ++q) {
-                lds_dma16_buf(P.kp + (int64_t)ph[kpg[q]] * (PS * D), PS * D * 2, koff[q], &sK[st][(wave * KIW + q) * 512]);
-            }
+            for (int i = 1; i < ppt; ++i) own = pw == i ? enx[i].x : own;
+            if (!(e0 + pw < n_e && (uint32_t)own < (uint32_t)n_phys32)) own = 0;
+            own = __builtin_amdgcn_readfirstlane(own);       // wave-uniform: keeps the loads' resources scalar
+            const uint64_t poff = (uint64_t)(uint32_t)own * kPageBytes;
     #pragma unroll
-            for (int q = 0; q < VIW; ++q) {
-                lds_dma16_buf(P.vp + (int64_t)ph[vpg[q]] * (D * PS), D * PS * 2, voff[q], &sV[st][(wave * VIW + q) * 512]);
-            }
+            for (int q = 0; q < KIW; ++q)
+                lds_dma16_buf((const char *)P.kp + poff, kPageBytes, koff[q], lds_k0 + st * kStageBytes + q * 1024);
+    #pragma unroll
+            for (int q = 0; q < VIW; ++q)
+                lds_dma16_buf((const char *)P.vp + poff, kPageBytes, voff[q], lds_v0 + st * kStageBytes + q * 1024);
         };
         // Zero the V^T slots of keys that hold no token (past a page's n_valid, or
         // pages past the split): their weight is zero, but 0 * NaN is not.  The
