@@ -39,12 +39,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ bf16x8 u4_as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// acc + lo + hi of a packed bf16 pair, exact products in fp32 (v_dot2c_f32_bf16 with 1.0).
-__device__ __forceinline__ float sum_bf16x2(uint32_t pair, float acc) {
-    const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
-}
-
 // Zeroes the bf16 elements i >= keep of a 16-byte chunk of 8 bf16.
 __device__ __forceinline__ u32x4 keep_first_bf16(u32x4 v, int keep) {
     if (keep >= 8) return v;

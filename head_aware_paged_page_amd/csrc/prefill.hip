@@ -387,8 +387,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         };
         // Weights -> packed bf16 P^T operands, in place over all 32 scores per
         // stage (32 independent operations at a time for the vector ALU); returns
-        // the lane's sum of the weights that P.V uses.  v_exp_f32 flushes results
-        // below 2^-126 to zero, which is harmless.
+        // the lane's sum of the weights in fp32, before their rounding to bf16
+        // (plain adds: a dot-product instruction here waits for the matrix
+        // cores that the SIMD's other wave keeps busy).  v_exp_f32 flushes
+        // results below 2^-126 to zero, which is harmless.
         auto weights = [&](f32x16 (&S)[2], u32x4 (&Pk)[4]) {
     #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
@@ -401,9 +403,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                     Pk[s2][w] = pack_bf16x2(S[s2 >> 1][8 * (s2 & 1) + 2 * w], S[s2 >> 1][8 * (s2 & 1) + 2 * w + 1]);
             float r4[4] = {0.f, 0.f, 0.f, 0.f};
     #pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2)
+            for (int kt = 0; kt < 2; ++kt)
     #pragma unroll
-                for (int w = 0; w < 4; ++w) r4[w] = sum_bf16x2(Pk[s2][w], r4[w]);
+                for (int v = 0; v < 16; ++v) r4[v & 3] += S[kt][v];
             return (r4[0] + r4[1]) + (r4[2] + r4[3]);
         };
         auto scale_shift = [&](f32x16 (&S)[2], float a, float b) {
