@@ -210,60 +210,50 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
         // ---- tile issue: page entries, bounds flags, key positions, and the
         // global->LDS loads of K and V^T.
-        // The entries come through the constant cache (scalar loads), so they
-        // never share the in-order counter of the tile loads.  Entries past
-        // the split read the split's last.
-        typedef __attribute__((address_space(4))) const i32x4 ci32x4;
-        const ci32x4 *Ec = (const ci32x4 *)(uintptr_t)E;
+        // The entries of a tile are read one vector phase ahead of its issue,
+        // by an ordinary vector load (lane l holds page l % ppt of the tile;
+        // entries past the split read the split's last), so their latency
+        // hides behind a phase of work and they queue in order with the tile
+        // loads.  Tile issue: every wave loads its own 1 KB blocks of K and
+        // V^T (all inside page pw of the tile), and derives the tile's flags
+        // into its own ring `flr` (8 bits per stage): bit 0 = every key exists
+        // and is visible to every query of the q-tile (no bounds needed), bit
+        // 1 + pg = page pg has key slots without a token (their V^T cells must
+        // be zeroed).  Only for a tile that needs them does one wave (rotating)
+        // write the key positions (bounds) or each page's token count
+        // (zeroing) to LDS.  Pages past the split or outside the pool count as
+        // {phys 0, no tokens}.
         const int n_phys32 = (int)min(P.n_phys, (int64_t)INT32_MAX);
-        i32x4 enx[ppt];
-        auto fetch = [&](int t) {                            // requires t < n_tiles
-    #pragma unroll
-            for (int pg = 0; pg < ppt; ++pg) enx[pg] = Ec[min(my_lo + t * ppt + pg, my_hi - 1)];
-        };
-        // Tile issue.  Every wave loads its own 1 KB blocks of K and V^T (all
-        // inside page pw of the tile), and derives the tile's flags from the
-        // entries on the scalar unit into its own ring `flr` (8 bits per
-        // stage): bit 0 = every key exists and is visible to every query of
-        // the q-tile (no bounds needed), bit 1 + pg = page pg has key slots
-        // without a token (their V^T cells must be zeroed).  Only for a tile
-        // that needs them does one wave (rotating) write the key positions
-        // (bounds) or each page's token count (zeroing) to LDS.  Pages past
-        // the split or outside the pool count as {phys 0, no tokens}.
+        const int pgi = lane % ppt;                          // page of the entry a lane holds
+        auto eload = [&](int t) -> int4 { return E[min(my_lo + t * ppt + pgi, my_hi - 1)]; };
+        int4 ent = int4{0, 0, 0, 0};                         // entries of the next tile to issue
         uint32_t flr = 0;
-        auto issue = [&](int t, int st) {
-            const int e0 = t * ppt, n_e = my_hi - my_lo;
-            // token counts and first positions as vector values (element =
-            // page), so that the bounds writer can pick them by lane
-            i32x4 nvl = {0, 0, 0, 0}, pst = {0, 0, 0, 0};
-            int pmask = 0;
-    #pragma unroll
-            for (int i = 0; i < ppt; ++i) {
-                const bool ok = e0 + i < n_e && (uint32_t)enx[i].x < (uint32_t)n_phys32;
-                nvl[i] = ok ? min(enx[i].z, PS) : 0;
-                pst[i] = enx[i].y;
-                pmask |= (nvl[i] < PS ? 1 : 0) << i;
-            }
+        // the flags, bounds and page of tile t (entries e) into stage st;
+        // returns the byte offset of this wave's page in the pools
+        auto prep = [&](int t, int st, const int4 &e) -> uint64_t {
+            const bool ok = t * ppt + pgi < my_hi - my_lo && (uint32_t)e.x < (uint32_t)n_phys32;
+            const int nv = ok ? min(e.z, PS) : 0;
+            const uint32_t pmask = (uint32_t)__ballot(nv < PS) & ((1u << ppt) - 1);
             // A table row ascends by position and a page's positions are
             // consecutive, so with every slot holding a token the tile spans
             // [first position of page 0, last of page ppt-1]: no bounds are
             // needed when that ends at or before the first query and (local)
             // starts inside the last query's window.
-            const bool full = pmask == 0 && pst[ppt - 1] + (PS - 1) <= p0 && (!is_local || pst[0] > p_last - W);
-            const uint32_t fl = (full ? 1u : 0u) | (uint32_t)(pmask << 1);
+            const int pos_first = __builtin_amdgcn_readlane(e.y, 0);
+            const int pos_last = __builtin_amdgcn_readlane(e.y, ppt - 1) + (PS - 1);
+            const bool full = pmask == 0 && pos_last <= p0 && (!is_local || pos_first > p_last - W);
+            const uint32_t fl = (full ? 1u : 0u) | (pmask << 1);
             flr = __builtin_amdgcn_readfirstlane((flr & ~(0xffu << (8 * st))) | (fl << (8 * st)));
             if ((!full || pmask) && wave == t % NW) {
                 const int pgl = lane / PS, tk = lane % PS;
-                const int nv = nvl[pgl];
-                if (!full) sPos[st][lane] = tk < nv ? pst[pgl] + tk : kPosInvalid;
-                if (pmask && tk == 0) sNv[st][pgl] = nv;
+                const int nvp = __shfl(nv, pgl, 64), pst = __shfl(e.y, pgl, 64);
+                if (!full) sPos[st][lane] = tk < nvp ? pst + tk : kPosInvalid;
+                if (pmask && tk == 0) sNv[st][pgl] = nvp;
             }
-            int own = enx[0].x;
-    #pragma unroll
-            for (int i = 1; i < ppt; ++i) own = pw == i ? enx[i].x : own;
-            if (!(e0 + pw < n_e && (uint32_t)own < (uint32_t)n_phys32)) own = 0;
-            own = __builtin_amdgcn_readfirstlane(own);       // wave-uniform: keeps the loads' resources scalar
-            const uint64_t poff = (uint64_t)(uint32_t)own * kPageBytes;
+            const int own = __builtin_amdgcn_readlane(ok ? e.x : 0, pw);
+            return (uint64_t)(uint32_t)own * kPageBytes;
+        };
+        auto dmas = [&](int st, uint64_t poff) {
     #pragma unroll
             for (int q = 0; q < KIW; ++q)
                 lds_dma16_buf((const char *)P.kp + poff, kPageBytes, koff[q], lds_k0 + st * kStageBytes + q * 1024);
@@ -455,12 +445,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         };
 
         static_assert(NBUF == 4, "tiles m-1 .. m+2 occupy the four stages around phase 2m");
+        {
+            // tiles 0 .. 2: their entries read together, then issued in order
+            int4 e3[NBUF - 1];
     #pragma unroll
-        for (int j = 0; j < NBUF - 1; ++j)
-            if (j < n_tiles) {
-                fetch(j);
-                issue(j, j);
-            }
+            for (int j = 0; j < NBUF - 1; ++j) e3[j] = j < n_tiles ? eload(j) : int4{0, 0, 0, 0};
+    #pragma unroll
+            for (int j = 0; j < NBUF - 1; ++j)
+                if (j < n_tiles) dmas(j, prep(j, j, e3[j]));
+        }
         if (n_tiles > 0) {
             if (n_tiles > 2) wait_vmcnt<2 * IPW>();
             else if (n_tiles > 1) wait_vmcnt<IPW>();
@@ -493,7 +486,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 // later): the loads of the two groups never queue at the
                 // address unit together, and the matrix cores of the SIMD keep
                 // working for the other group meanwhile.
-                if (p2 >= 1 && p2 + 2 < n_tiles) issue(p2 + 2, (p2 + 2) % NBUF);
+                // Vector phase: prepare tile p2 + 2 from the entries read last
+                // phase, issue its loads, read the entries of tile p2 + 3.
+                const bool iss = p2 >= 1 && p2 + 2 < n_tiles;
+                const uint64_t poff = iss ? prep(p2 + 2, (p2 + 2) % NBUF, ent) : 0;
+                if (iss) dmas((p2 + 2) % NBUF, poff);
+                if (p2 + 3 < n_tiles) ent = eload(p2 + 3);
                 if (act) {
                     // the softmax wave issues first: its SIMD partner's MFMA
                     // stream would otherwise take most issue cycles from it
@@ -504,11 +502,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             }
             if (k & 1) {                                     // tile (k+1)/2 is used from the next phase on
                 const int m = (k + 1) >> 1;
-                // the entries of both groups' next issue (tile m + 2); the
-                // barrier below waits for them
-                if (m + 2 < n_tiles) fetch(m + 2);
+                // Every wave's loads newer than those of tile m: the loads of
+                // tile m + 1 and the entries of tile m + 2.
                 if (m < n_tiles) {
-                    if (m + 1 < n_tiles) wait_vmcnt<IPW>();
+                    if (m + 2 < n_tiles) wait_vmcnt<IPW + 1>();
+                    else if (m + 1 < n_tiles) wait_vmcnt<IPW>();
                     else wait_vmcnt<0>();
                 }
                 // One barrier per phase pair: it publishes tile m and retires the
