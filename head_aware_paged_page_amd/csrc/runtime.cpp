@@ -1,6 +1,8 @@
 // Host runtime of libsegpaged: errors, launch planning, argument validation and
 // the device entry points (the kernels live in the .hip files).
 #include <algorithm>
+#include <functional>
+#include <map>
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
@@ -99,59 +101,73 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
     }
     const int min_chunk = std::max(1, kMinSplitKeys / page_size);
     if (kind == SP_WS_PREFILL) {
-        // One persistent workgroup per CU takes the items long-first.  If the
-        // unsplit work already fills the CUs, nothing is split.  Otherwise the
-        // chunk minimises an estimate of the makespan (in 64-key tiles, each
-        // item paying a fixed setup): the long items (of split rows) run side
-        // by side, and the short ones share the CUs that the long ones leave
-        // free (list-scheduling bound: total / CUs + largest), spilling onto
-        // all CUs once the long items end.
-        if (units >= kPlanCUs) {
-            p.chunk_pages = INT_MAX;
-        } else {
-            const int ppt = std::max(1, kPrefillKeysPerTile / page_size);
-            auto cost = [&](int64_t pages) { return (double)((pages + ppt - 1) / ppt + kPrefillSetupTiles); };
-            int e_max = 1;
-            for (int r = 0; r < n_rows; ++r) e_max = std::max(e_max, h_row_ptr[r + 1] - h_row_ptr[r]);
-            double best = 0;
-            int best_c = INT_MAX;
-            for (int k = 1; k <= kMaxSplits; ++k) {
-                const int c = (e_max + k - 1) / k;
-                if (c < min_chunk) break;
-                if (k > 1 && c == (e_max + k - 2) / (k - 1)) continue;   // same chunk as k-1
-                int64_t n_long = 0;
-                double L = 0, s_tot = 0, s_max = 0;
-                for (int r = 0; r < n_rows; ++r) {
-                    const int q = r % n_seq;
-                    const int nq = (h_tok_ptr[q + 1] - h_tok_ptr[q] + p.tok_per_tile - 1) / p.tok_per_tile;
-                    int ns, it;
-                    const int e = h_row_ptr[r + 1] - h_row_ptr[r];
-                    row_items(e, nq, c, &ns, &it);
-                    if (ns > 1) {
-                        n_long += it;
-                        L = std::max(L, cost((e + ns - 1) / ns));
-                    } else if (nq > 0) {
-                        s_tot += nq * cost(e);
-                        s_max = std::max(s_max, cost(e));
+        // One persistent workgroup per CU takes the items long-first from a
+        // counter: list scheduling, longest item first.  Every candidate chunk
+        // (the longest row split k ways, k = 1, 2, ...) is scored by running
+        // that schedule over the items' estimated costs (64-key tiles of the
+        // row's table plus a fixed set-up per item); the shortest makespan
+        // wins, and a finer chunk must beat a coarser one by 1 %.  Items of a
+        // row share one cost, so the schedule runs per cost class on a
+        // histogram of CU loads: each class fills the least loaded CUs first.
+        const int ppt = std::max(1, kPrefillKeysPerTile / page_size);
+        auto cost = [&](int64_t pages) { return (double)((pages + ppt - 1) / ppt + kPrefillSetupTiles); };
+        int e_max = 1;
+        for (int r = 0; r < n_rows; ++r) e_max = std::max(e_max, h_row_ptr[r + 1] - h_row_ptr[r]);
+        std::map<double, int64_t, std::greater<double>> cls;   // cost -> items, longest first
+        std::map<double, int64_t> loads;                       // CU load -> CUs
+        auto makespan = [&](int c, int64_t *n_items) {
+            cls.clear();
+            *n_items = 0;
+            for (int r = 0; r < n_rows; ++r) {
+                const int q = r % n_seq;
+                const int nq = (h_tok_ptr[q + 1] - h_tok_ptr[q] + p.tok_per_tile - 1) / p.tok_per_tile;
+                if (nq == 0) continue;
+                int ns, it;
+                const int e = h_row_ptr[r + 1] - h_row_ptr[r];
+                row_items(e, nq, c, &ns, &it);
+                cls[cost((e + ns - 1) / ns)] += it;
+                *n_items += it;
+            }
+            loads.clear();
+            loads[0.0] = kPlanCUs;
+            for (const auto &kv : cls) {
+                int64_t n = kv.second;
+                while (n > 0) {
+                    auto lo = loads.begin();
+                    const double lvl = lo->first;
+                    const int64_t m = lo->second;
+                    if (n >= m) {   // every CU at the lowest level takes items while it stays lowest
+                        int64_t each = n / m;
+                        const auto nx = std::next(lo);
+                        if (nx != loads.end()) each = std::min<int64_t>(each, (int64_t)((nx->first - lvl) / kv.first) + 1);
+                        loads.erase(lo);
+                        loads[lvl + each * kv.first] += m;
+                        n -= each * m;
+                    } else {
+                        lo->second -= n;
+                        loads[lvl + kv.first] += n;
+                        n = 0;
                     }
                 }
-                double est;
-                if (n_long >= kPlanCUs) {
-                    est = (double)((n_long + kPlanCUs - 1) / kPlanCUs) * L + s_tot / kPlanCUs;
-                } else {
-                    const double free_cus = (double)(kPlanCUs - n_long);
-                    double sh = s_tot > 0 ? s_tot / free_cus + s_max : 0;
-                    if (sh > L && L > 0) sh = L + (s_tot - free_cus * L) / kPlanCUs + s_max;
-                    est = std::max(L, sh);
-                }
-                if (best_c == INT_MAX || est < best) {
-                    best = est;
-                    best_c = c;
-                }
-                if (n_long > 2 * kPlanCUs) break;                    // finer chunks only add rounds
             }
-            p.chunk_pages = best_c;
+            return loads.rbegin()->first;
+        };
+        int64_t n0 = 0;
+        double best = makespan(INT_MAX, &n0);
+        int best_c = INT_MAX;
+        for (int k = 2; k <= kMaxSplits; ++k) {
+            const int c = (e_max + k - 1) / k;
+            if (c < min_chunk) break;
+            if (c == (e_max + k - 2) / (k - 1)) continue;   // same chunk as k-1
+            int64_t n_items = 0;
+            const double est = makespan(c, &n_items);
+            if (est < 0.99 * best) {
+                best = est;
+                best_c = c;
+            }
+            if (n_items > 16 * kPlanCUs) break;   // finer chunks only add set-ups
         }
+        p.chunk_pages = best_c;
     } else {
         const int64_t c = (work + kTargetDecodeItems - 1) / kTargetDecodeItems;
         p.chunk_pages = (int)std::min<int64_t>(kDecodeMaxChunk, std::max<int64_t>(min_chunk, c));
