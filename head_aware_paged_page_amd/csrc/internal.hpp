@@ -28,6 +28,7 @@ constexpr int kDecodeWaves = 4;
 // Every split still streams at least kMinSplitKeys keys.
 constexpr int kPlanCUs = 256;
 constexpr int kPrefillSetupTiles = 3;      // fixed cost of a prefill item, in 64-key tiles
+constexpr double kMergeTiles = 1.5;        // merge pass per split prefill item, in 64-key tiles of one CU
 constexpr int kTargetDecodeItems = 384;
 constexpr int kMinSplitKeys = 512;
 constexpr int kMaxSplits = 1024;

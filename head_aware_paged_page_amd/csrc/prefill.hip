@@ -553,24 +553,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 }
 
 // Combines the kv splits of every split q-tile: O = sum_s e^{lse_s-M} o_s / sum_s e^{lse_s-M}.
-// Launched over the same work items: item (q-tile, split s) merges rows
-// [s * ceil(rows/ns), (s+1) * ceil(rows/ns)) of its q-tile, so all splits share
-// the work, with blockIdx.y spreading an item's rows over workgroups so that
-// every wave merges one row.  The lanes first read the row's split LSEs
-// together (lane s, s + 64, ...) for the max and the normaliser (online, then
-// combined across lanes), then lane (g, c) accumulates dims 8c .. 8c+7 over
-// splits g, g + 64/(D/8), ..., so the loads of all splits are in flight
-// together; the split groups are summed by lane shuffles.  The partials are normalised (|o| <= max |v|), so fp16 keeps
-// them to about 5e-4 relative.
-template <int D>
+// Launched over the split items (numbered first): item (q-tile, split s) merges
+// rows [s * ceil(rows/ns), (s+1) * ceil(rows/ns)) of its q-tile, so all splits
+// share the work, and blockIdx.y spreads those rows over workgroups.  A lane
+// owns 8 dims of one row and splits g, g + SG, g + 2 SG, ... (D/8 lanes per
+// row and split group); it merges them online (running max, rescaled sums)
+// with the loads of several splits in flight together, and the SG split
+// groups of a row are combined by lane exchanges at the end.  SG = 1 suits
+// many rows with few splits each, SG > 1 few rows with many splits.  The
+// partials are normalised (|o| <= max |v|), so fp16 keeps them to about
+// 5e-4 relative.
+template <int D, int SG>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, int BM) {
-    constexpr int CH = D / 8, SG = 64 / CH;          // dim chunks of 8, split groups
+    constexpr int CH = D / 8, RPW = 64 / (CH * SG), RPB = 4 * RPW;   // rows per wave / workgroup
+    static_assert(RPW >= 1 && 64 % (CH * SG) == 0, "a wave holds whole rows");
     int r, local;
     item_of(P.item_ptr, P.item_ptr2, P.n_rows, blockIdx.x, &r, &local);
     const int ns = P.nsplit[r];
     if (ns == 1) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int c = lane % CH, sg = lane / CH;
+    const int c = lane % CH, g0 = (lane / CH) % SG;
     const int qt = local / ns, sp_i = local % ns;
     const int seq = r % P.n_seq, slot = r / P.n_seq;
     const int tok_base = P.tok_ptr[seq];
@@ -578,54 +580,51 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, int
     const int ntok = min(P.tpt, P.tok_ptr[seq + 1] - tok_base - t0);
     const int nrows = ntok * P.G;
     const int per = (nrows + ns - 1) / ns;
-    const int r0 = sp_i * per, r1 = min(nrows, r0 + per);
+    const int row = sp_i * per + blockIdx.y * RPB + wave * RPW + lane / (CH * SG);
+    if (row >= min(nrows, (sp_i + 1) * per)) return;   // whole rows: the exchanges below stay inside one
     const int64_t part0 = (int64_t)P.part_ptr[r] + (int64_t)qt * ns;   // splits part0 .. part0+ns-1
-    for (int row = r0 + 4 * blockIdx.y + wave; row < r1; row += 4 * gridDim.y) {
-        const float *lse = P.part_lse + part0 * BM + row;
-        float m = -INFINITY, z = 0.f;                // this lane's splits, online
-        for (int s = lane; s < ns; s += 64) {
-            const float x = lse[(int64_t)s * BM];
-            if (x > m) {
-                z = z * __expf(m - x) + 1.f;
-                m = x;
-            } else if (x != -INFINITY) {
-                z += __expf(x - m);
-            }
+    const float *lse = P.part_lse + part0 * BM + row;
+    const _Float16 *src = P.part_o + (part0 * BM + row) * D + 8 * c;
+    float m = -INFINITY, z = 0.f, o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+#pragma unroll 4
+    for (int s = g0; s < ns; s += SG) {
+        const float x = lse[(int64_t)s * BM];
+        const f16x8 v = *(const f16x8 *)(src + (int64_t)s * BM * D);
+        if (x == -INFINITY) continue;                 // a split that sees no key
+        if (x > m) {
+            const float a = __expf(m - x);            // 0 while m is -inf
+            z *= a;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] *= a;
+            m = x;
         }
-        float M = m;
+        const float wgt = __expf(x - m);
+        z += wgt;
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-        z = M == -INFINITY ? 0.f : z * __expf(m - M);   // a lane with no split has z = 0
-        float o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = 0.f;
-        if (M != -INFINITY) {
-            const _Float16 *src = P.part_o + (part0 * BM + row) * D + 8 * c;
-#pragma unroll 8
-            for (int s = sg; s < ns; s += SG) {
-                const float wgt = __expf(lse[(int64_t)s * BM] - M);
-                const f16x8 v = *(const f16x8 *)(src + (int64_t)s * BM * D);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] += wgt * (float)v[e];
-            }
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
-#pragma unroll
-        for (int off = CH; off < 64; off <<= 1)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], off, 64);
-        const float inv = z > 0.f ? 1.f / z : 0.f;
-        const int tq = row / P.G, g = row % P.G;
-        const int64_t orow = (int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * P.G + g;
-        if (sg == 0) {
-            u32x4 pk;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(o[2 * i] * inv, o[2 * i + 1] * inv);
-            *(u32x4 *)(P.out + orow * D + 8 * c) = pk;
-        }
-        if (P.lse && lane == 0) P.lse[orow] = z > 0.f ? M + logf(z) : -INFINITY;
+        for (int e = 0; e < 8; ++e) o[e] += wgt * (float)v[e];
     }
+#pragma unroll
+    for (int off = CH; off < CH * SG; off <<= 1) {    // combine the split groups of the row
+        const float m2 = __shfl_xor(m, off, 64);
+        const float mm = fmaxf(m, m2);
+        const float a = mm == -INFINITY ? 0.f : __expf(m - mm);
+        const float b = mm == -INFINITY ? 0.f : __expf(m2 - mm);
+        z = z * a + __shfl_xor(z, off, 64) * b;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = o[e] * a + __shfl_xor(o[e], off, 64) * b;
+        m = mm;
+    }
+    if (g0 != 0) return;
+    const float inv = z > 0.f ? 1.f / z : 0.f;
+    const int tq = row / P.G, g = row % P.G;
+    const int64_t orow = (int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * P.G + g;
+    u32x4 pk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(o[2 * i] * inv, o[2 * i + 1] * inv);
+    *(u32x4 *)(P.out + orow * D + 8 * c) = pk;
+    if (P.lse && c == 0) P.lse[orow] = z > 0.f ? m + logf(z) : -INFINITY;
 }
 
 // Writes the work-item prefix sums of the launch plan into the workspace; one
@@ -729,13 +728,19 @@ int launch_prefill(const AttnArgs &a, const Plan &p, int64_t n_tok, hipStream_t 
     P.scale_log2 = a.scale * kLog2e;
     P.work_ctr = (int *)(w + p.off_zero + 128);
     P.n_items = (int)p.n_items;
-    const dim3 mgrid((unsigned)p.n_items, (unsigned)std::max(1, (p.merge_rows + 3) / 4));
+    // merge: split groups per row from the rows each split item merges
+    const bool merge_wide = p.merge_rows <= 16;
+    const int merge_rpb = 4 * 64 / (a.head_dim / 8) / (merge_wide ? 4 : 1);   // rows per merge workgroup
+    const dim3 mgrid((unsigned)std::max<int64_t>(1, p.n_parts),
+                     (unsigned)std::max(1, (p.merge_rows + merge_rpb - 1) / merge_rpb));
     const dim3 grid_persist((unsigned)std::min<int64_t>(p.n_items, kPlanCUs));
 #define SP_PREFILL_CASE(DD, PSV)                                                                        \
     if (a.head_dim == DD && a.page_size == PSV) {                                                       \
         hipLaunchKernelGGL((prefill_bf16_kernel<DD, 8, PSV, 4>), grid_persist, dim3(512), 0, stream, P); \
-        if (p.n_parts)                                                                                  \
-            hipLaunchKernelGGL(prefill_merge_kernel<DD>, mgrid, dim3(256), 0, stream, P, p.rows_per_tile); \
+        if (p.n_parts && merge_wide)                                                                    \
+            hipLaunchKernelGGL((prefill_merge_kernel<DD, 4>), mgrid, dim3(256), 0, stream, P, p.rows_per_tile); \
+        else if (p.n_parts)                                                                             \
+            hipLaunchKernelGGL((prefill_merge_kernel<DD, 1>), mgrid, dim3(256), 0, stream, P, p.rows_per_tile); \
     }
     SP_PREFILL_CASE(128, 16) else SP_PREFILL_CASE(128, 32) else SP_PREFILL_CASE(128, 64)
     else SP_PREFILL_CASE(64, 16) else SP_PREFILL_CASE(64, 32) else SP_PREFILL_CASE(64, 64)

@@ -109,6 +109,9 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
         // wins, and a finer chunk must beat a coarser one by 1 %.  Items of a
         // row share one cost, so the schedule runs per cost class on a
         // histogram of CU loads: each class fills the least loaded CUs first.
+        // A split item also writes its partial result (about a tile's time)
+        // and the merge reads it back after the main pass (kMergeTiles per
+        // item, spread over the CUs).
         const int ppt = std::max(1, kPrefillKeysPerTile / page_size);
         auto cost = [&](int64_t pages) { return (double)((pages + ppt - 1) / ppt + kPrefillSetupTiles); };
         int e_max = 1;
@@ -118,6 +121,7 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
         auto makespan = [&](int c, int64_t *n_items) {
             cls.clear();
             *n_items = 0;
+            int64_t n_parts = 0;
             for (int r = 0; r < n_rows; ++r) {
                 const int q = r % n_seq;
                 const int nq = (h_tok_ptr[q + 1] - h_tok_ptr[q] + p.tok_per_tile - 1) / p.tok_per_tile;
@@ -125,8 +129,9 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
                 int ns, it;
                 const int e = h_row_ptr[r + 1] - h_row_ptr[r];
                 row_items(e, nq, c, &ns, &it);
-                cls[cost((e + ns - 1) / ns)] += it;
+                cls[cost((e + ns - 1) / ns) + (ns > 1 ? 1.0 : 0.0)] += it;
                 *n_items += it;
+                if (ns > 1) n_parts += it;
             }
             loads.clear();
             loads[0.0] = kPlanCUs;
@@ -150,7 +155,7 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
                     }
                 }
             }
-            return loads.rbegin()->first;
+            return loads.rbegin()->first + kMergeTiles * (double)n_parts / kPlanCUs;
         };
         int64_t n0 = 0;
         double best = makespan(INT_MAX, &n0);
@@ -196,7 +201,9 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
     p.n_items = items;
     p.n_parts = parts;
     p.off_part_o = off;
-    off += align_up(sizeof(float) * (size_t)parts * p.rows_per_tile * head_dim, 256);
+    // partial outputs: fp16 for prefill (normalised), fp32 for decode
+    const size_t po_bytes = kind == SP_WS_PREFILL ? 2 : sizeof(float);
+    off += align_up(po_bytes * (size_t)parts * p.rows_per_tile * head_dim, 256);
     p.off_part_lse = off;
     off += align_up(sizeof(float) * (size_t)parts * p.rows_per_tile, 256);
     p.bytes = std::max<size_t>(off, 256);
