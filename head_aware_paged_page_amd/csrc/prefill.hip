@@ -147,14 +147,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const uint32_t lds_v0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&sV[0][wave * VIW * 512]);
 
     // Persistent workgroups (one per CU) take the work items in their long-first
-    // order from a counter: the hardware dispatcher places workgroups in order
-    // and would hold short items back until a long one ends.
-    for (;;) {
-        if (tid == 0) s_item = atomicAdd(P.work_ctr, 1);
-        __syncthreads();                     // also: every wave is done with the previous item
-        const int b = s_item;
-        __syncthreads();
-        if (b >= P.n_items) break;
+    // order: the hardware dispatcher places workgroups in order and would hold
+    // short items back until a long one ends.  Workgroup w starts with item w;
+    // the next item comes from a counter (items gridDim.x, gridDim.x + 1, ...),
+    // asked for a few phases before the current item ends, so that the answer
+    // is there when it ends and the order of asking still follows the order in
+    // which workgroups fall free.
+    for (int b = blockIdx.x; b < P.n_items;) {
+        int ticket = 0;                                  // thread 0's next counter value
 
         // ---- work item
         int r, local;
@@ -171,6 +171,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int W = is_local ? P.window[slot] : 0;
         const int nrows = ntok * G;
 
+        // ---- queries of this wave: row = 32*wave + n -> (token, head), read
+        // now and scaled once the first tile loads are out
+        const int row = 32 * wave + n;
+        const bool row_ok = row < nrows;
+        const int tq = row / G, g = row % G;
+        const int pq = p0 + tq;                    // this lane's query position
+        const int lowq = is_local ? pq - W : INT32_MIN;   // visible iff lowq < pos <= pq
+        u32x4 qraw[DK];
+        // The queries are held pre-multiplied by c = scale * log2(e) (rounded
+        // to bf16 once), so the scores leave the matrix cores in the log2
+        // domain of the softmax.
+        const float cl = P.scale_log2;
+        bf16x8 qf[DK];
+        {
+            const bf16 *qrow = P.q + ((int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g) * D;
+    #pragma unroll
+            for (int s = 0; s < DK; ++s) {
+                qraw[s] = u32x4{0, 0, 0, 0};
+                if (row_ok) qraw[s] = *(const u32x4 *)(qrow + 16 * s + 8 * h);
+            }
+        }
+
         // ---- the q-tile's visible entry range, then this split's share
         const int e_beg = P.row_ptr[r], e_end = P.row_ptr[r + 1];
         const int4 *E = P.entries;
@@ -182,31 +204,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int my_hi = min(hi, my_lo + chunk);
         const int n_tiles = (my_hi - my_lo + ppt - 1) / ppt;
 
-        // ---- queries of this wave: row = 32*wave + n -> (token, head)
-        const int row = 32 * wave + n;
-        const bool row_ok = row < nrows;
-        const int tq = row / G, g = row % G;
-        const int pq = p0 + tq;                    // this lane's query position
-        const int lowq = is_local ? pq - W : INT32_MIN;   // visible iff lowq < pos <= pq
-        // The queries are held pre-multiplied by c = scale * log2(e) (rounded
-        // to bf16 once), so the scores leave the matrix cores in the log2
-        // domain of the softmax.
-        const float cl = P.scale_log2;
-        bf16x8 qf[DK];
-        {
-            const bf16 *qrow = P.q + ((int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g) * D;
-    #pragma unroll
-            for (int s = 0; s < DK; ++s) {
-                u32x4 v = {0, 0, 0, 0};
-                if (row_ok) v = *(const u32x4 *)(qrow + 16 * s + 8 * h);
-                u32x4 w;
-    #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w[e] = pack_bf16x2(bf16_bits_to_f32(v[e] & 0xffffu) * cl, bf16_bits_to_f32(v[e] >> 16) * cl);
-                qf[s] = u4_as_bf16x8(kQScale ? w : v);
-            }
-        }
-        wait_vmcnt<0>();   // queries in registers before the tile loads start
 
         // ---- tile issue: page entries, bounds flags, key positions, and the
         // global->LDS loads of K and V^T.
@@ -454,6 +451,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             for (int j = 0; j < NBUF - 1; ++j)
                 if (j < n_tiles) dmas(j, prep(j, j, e3[j]));
         }
+    #pragma unroll
+        for (int s = 0; s < DK; ++s) {
+            u32x4 w;
+    #pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w[e] = pack_bf16x2(bf16_bits_to_f32(qraw[s][e] & 0xffffu) * cl, bf16_bits_to_f32(qraw[s][e] >> 16) * cl);
+            qf[s] = u4_as_bf16x8(kQScale ? w : qraw[s]);
+        }
         if (n_tiles > 0) {
             if (n_tiles > 2) wait_vmcnt<2 * IPW>();
             else if (n_tiles > 1) wait_vmcnt<IPW>();
@@ -463,7 +468,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         f32x16 S[2];
         u32x4 Pk[4];
         const int n_phases = n_tiles > 0 ? 2 * n_tiles + (kPingPong ? 2 : 1) : 0;
+        const int k_ticket = max(0, n_phases - 4);
+        if (n_phases == 0 && tid == 0) ticket = (int)atomicInc((unsigned *)P.work_ctr, 0xffffffffu);
         for (int k = 0; k < n_phases; ++k) {
+            if (k == k_ticket && tid == 0) ticket = (int)atomicInc((unsigned *)P.work_ctr, 0xffffffffu);
             const int p2 = k >> 1;
             if (kPingPong) {
                 const int pm = (flr >> (8 * (p2 % NBUF) + 1)) & 0x7f;
@@ -521,8 +529,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const float l = l_run + xor_lane(l_run, 32);
         const float inv = l > 0.f ? 1.f / l : 0.f;
         const float lse = l > 0.f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
-        if (!row_ok) continue;
-        if (ns == 1) {
+        if (!row_ok) {
+            // a row past the q-tile's tokens: nothing to write
+        } else if (ns == 1) {
             bf16 *orow = P.out + ((int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g) * D;
     #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
@@ -549,6 +558,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 }
             if (h == 0) P.part_lse[part * BM + row] = lse;
         }
+        if (tid == 0) s_item = (int)gridDim.x + ticket;
+        __syncthreads();                     // every wave is done with this item; s_item is written
+        b = __builtin_amdgcn_readfirstlane(s_item);
+        __syncthreads();                     // read before the next item's ticket overwrites it
     }   // work items
 }
 
