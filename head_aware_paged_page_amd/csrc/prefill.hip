@@ -31,17 +31,6 @@ namespace sp {
 namespace {
 
 constexpr int BN = kPrefillKeysPerTile;   // 64 keys per tile
-// Ping-pong (the two wave groups of a SIMD in opposite phases) is the default:
-// on gfx950 it measured about 2.5x faster per tile than running both groups'
-// phases in step, which remains available as a build option for comparison.
-#ifndef SP_PINGPONG
-#define SP_PINGPONG 1
-#endif
-constexpr bool kPingPong = SP_PINGPONG;
-#ifndef SP_PRIO_SOFTMAX
-#define SP_PRIO_SOFTMAX 0
-#endif
-constexpr int kPrioSoftmax = SP_PRIO_SOFTMAX;
 #ifndef SP_QSCALE
 #define SP_QSCALE 1
 #endif
@@ -307,7 +296,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         // 0..2 by everyone before phase 0), waited for at the end of phase
         // 2m-1, and its stage is free after phase 2m+3.
         static_assert(NW == 8, "the ping-pong schedule pairs two groups of four waves");
-        const int grp = kPingPong ? wave >> 2 : 0;
+        const int grp = wave >> 2;
         // Operand reads run ahead of the MFMAs that use them (explicit schedule
         // groups): S^T takes its two 32-key blocks' k-steps alternately, with
         // the reads two k-steps ahead, so the LDS latency is paid once per
@@ -467,61 +456,63 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         }
         f32x16 S[2];
         u32x4 Pk[4];
-        const int n_phases = n_tiles > 0 ? 2 * n_tiles + (kPingPong ? 2 : 1) : 0;
-        const int k_ticket = max(0, n_phases - 4);
-        if (n_phases == 0 && tid == 0) ticket = (int)atomicInc((unsigned *)P.work_ctr, 0xffffffffu);
-        for (int k = 0; k < n_phases; ++k) {
-            if (k == k_ticket && tid == 0) ticket = (int)atomicInc((unsigned *)P.work_ctr, 0xffffffffu);
-            const int p2 = k >> 1;
-            if (kPingPong) {
-                const int pm = (flr >> (8 * (p2 % NBUF) + 1)) & 0x7f;
-                if (!(k & 1) && grp == 1 && p2 < n_tiles && pm)
-                    fixup(p2 % NBUF, pm, 4 * 64, 4 * 64);    // group 1 is in its vector-ALU phase
-            } else {
-                const int pm = (flr >> (8 * (p2 % NBUF) + 1)) & 0x7f;
-                if ((k & 1) && p2 < n_tiles && pm) fixup(p2 % NBUF, pm, 0, NW * 64);   // all waves, before P.V(p2) two phases on
+        // Each group runs its own loop (the branch on the group skips the other
+        // loop), so that a phase carries no test of which kind it is.  Both
+        // loops run n_it iterations of one workgroup barrier each.
+        // Iteration i of a group: its matrix phase (P.V of tile i-1, then S of
+        // tile i) and its vector phase (group 0: the softmax of tile i after
+        // the matrix phase; group 1: the softmax of tile i-1 before it), then
+        // the barrier.  Each vector phase first issues tile i + 2
+        // (prepared from the entries read one vector phase earlier) and reads
+        // the entries of tile i + 3.  Tile m is issued in iteration m-2 and
+        // waited for at the end of iteration m-1; its stage is free after
+        // iteration m+1.
+        const int n_it = n_tiles > 0 ? n_tiles + 1 : 0;
+        auto vphase = [&](int i, int js) {
+            const bool act = js >= 0 && js < n_tiles;
+            const bool full = act && ((flr >> (8 * (js % NBUF))) & 1);
+            const bool iss = i >= 1 && i + 2 < n_tiles;
+            const uint64_t poff = iss ? prep(i + 2, (i + 2) % NBUF, ent) : 0;
+            if (iss) dmas((i + 2) % NBUF, poff);
+            if (i + 3 < n_tiles) ent = eload(i + 3);
+            if (act) softmax(js % NBUF, full, S, Pk);
+        };
+        auto mphase = [&](int i) {
+            if (i >= 1) pv((i - 1) % NBUF, Pk);
+            if (i < n_tiles) qk(i % NBUF, S);
+        };
+        auto sync = [&](int i) {                             // tile i+1 is used from the next iteration on
+            const int m = i + 1;
+            // every wave's loads newer than those of tile m: the loads of tile
+            // m + 1 and the entries of tile m + 2
+            if (m < n_tiles) {
+                if (m + 2 < n_tiles) wait_vmcnt<IPW + 1>();
+                else if (m + 1 < n_tiles) wait_vmcnt<IPW>();
+                else wait_vmcnt<0>();
             }
-
-            const int j = (k - grp) >> 1;                    // this group's tile in this phase
-            if (((k + grp) & 1) == 0) {                      // matrix-core phase
-                if (j >= 1) pv((j - 1) % NBUF, Pk);
-                if (j < n_tiles) qk(j % NBUF, S);
-            } else {                                         // vector-ALU phase
-                const bool act = j >= 0 && j < n_tiles;
-                const bool full = act && ((flr >> (8 * (j % NBUF))) & 1);
-                // Each group issues its share of tile p2 + 2 at the start of
-                // its vector phase (group 1 in phase 2 p2, group 0 one phase
-                // later): the loads of the two groups never queue at the
-                // address unit together, and the matrix cores of the SIMD keep
-                // working for the other group meanwhile.
-                // Vector phase: prepare tile p2 + 2 from the entries read last
-                // phase, issue its loads, read the entries of tile p2 + 3.
-                const bool iss = p2 >= 1 && p2 + 2 < n_tiles;
-                const uint64_t poff = iss ? prep(p2 + 2, (p2 + 2) % NBUF, ent) : 0;
-                if (iss) dmas((p2 + 2) % NBUF, poff);
-                if (p2 + 3 < n_tiles) ent = eload(p2 + 3);
-                if (act) {
-                    // the softmax wave issues first: its SIMD partner's MFMA
-                    // stream would otherwise take most issue cycles from it
-                    if (kPrioSoftmax) __builtin_amdgcn_s_setprio(kPrioSoftmax);
-                    softmax(j % NBUF, full, S, Pk);
-                    if (kPrioSoftmax) __builtin_amdgcn_s_setprio(0);
-                }
+            // it publishes tile m and retires the stage that the next issue reuses
+            lds_barrier();
+        };
+        if (n_it == 0 && tid == 0) ticket = (int)atomicInc((unsigned *)P.work_ctr, 0xffffffffu);
+        if (grp == 0) {
+            const int i_ticket = max(0, n_it - 2);
+            for (int i = 0; i < n_it; ++i) {
+                if (i == i_ticket && tid == 0) ticket = (int)atomicInc((unsigned *)P.work_ctr, 0xffffffffu);
+                mphase(i);
+                __builtin_amdgcn_sched_barrier(0);
+                vphase(i, i);
+                __builtin_amdgcn_sched_barrier(0);
+                sync(i);
             }
-            if (k & 1) {                                     // tile (k+1)/2 is used from the next phase on
-                const int m = (k + 1) >> 1;
-                // Every wave's loads newer than those of tile m: the loads of
-                // tile m + 1 and the entries of tile m + 2.
-                if (m < n_tiles) {
-                    if (m + 2 < n_tiles) wait_vmcnt<IPW + 1>();
-                    else if (m + 1 < n_tiles) wait_vmcnt<IPW>();
-                    else wait_vmcnt<0>();
-                }
-                // One barrier per phase pair: it publishes tile m and retires the
-                // stage that the next issue reuses.  Between barriers the two
-                // groups run their phases in opposite order (matrix then vector,
-                // vector then matrix), which keeps them out of step on each SIMD.
-                lds_barrier();
+        } else {
+            for (int i = 0; i < n_it; ++i) {
+                const int pm = (flr >> (8 * (i % NBUF) + 1)) & 0x7f;
+                if (i < n_tiles && pm) fixup(i % NBUF, pm, 4 * 64, 4 * 64);   // before P.V(i), one iteration on
+                vphase(i, i - 1);
+                __builtin_amdgcn_sched_barrier(0);
+                mphase(i);
+                __builtin_amdgcn_sched_barrier(0);
+                sync(i);
             }
         }
 
