@@ -101,6 +101,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     __shared__ __attribute__((aligned(1024))) bf16 sK[NBUF][BN * D];
     __shared__ __attribute__((aligned(1024))) bf16 sV[NBUF][D * BN];
     __shared__ int sPos[NBUF][BN];  // key positions of a tile that needs bounds
+    __shared__ __attribute__((aligned(16))) int4 sEnt[NW][2][4];   // per wave: page entries of its next tiles
     __shared__ int sNv[NBUF][4];    // tokens held by each page of a tile with empty key slots
 
     __shared__ int s_item;
@@ -134,6 +135,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int pw = __builtin_amdgcn_readfirstlane(wave * KIW / BPG);
     const uint32_t lds_k0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&sK[0][wave * KIW * 512]);
     const uint32_t lds_v0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&sV[0][wave * VIW * 512]);
+    const uint32_t lds_e0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&sEnt[wave][0][0]);
 
     // Persistent workgroups (one per CU) take the work items in their long-first
     // order: the hardware dispatcher places workgroups in order and would hold
@@ -196,11 +198,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
         // ---- tile issue: page entries, bounds flags, key positions, and the
         // global->LDS loads of K and V^T.
-        // The entries of a tile are read one vector phase ahead of its issue,
-        // by an ordinary vector load (lane l holds page l % ppt of the tile;
+        // The entries of a tile are read one vector phase ahead of its issue
+        // (tiles 0 .. 2: at the start of the item), by a global->LDS load into
+        // the wave's own slot (lane l < ppt fetches page l of the tile;
         // entries past the split read the split's last), so their latency
         // hides behind a phase of work and they queue in order with the tile
-        // loads.  Tile issue: every wave loads its own 1 KB blocks of K and
+        // loads; a vector load into registers instead makes the compiler wait
+        // for every load in flight before using it.  Tile issue: every wave loads its own 1 KB blocks of K and
         // V^T (all inside page pw of the tile), and derives the tile's flags
         // into its own ring `flr` (8 bits per stage): bit 0 = every key exists
         // and is visible to every query of the q-tile (no bounds needed), bit
@@ -212,7 +216,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int n_phys32 = (int)min(P.n_phys, (int64_t)INT32_MAX);
         const int pgi = lane % ppt;                          // page of the entry a lane holds
         auto eload = [&](int t) -> int4 { return E[min(my_lo + t * ppt + pgi, my_hi - 1)]; };
-        int4 ent = int4{0, 0, 0, 0};                         // entries of the next tile to issue
+        // entries of tile t into slot t & 1 of this wave, read back (after the
+        // wait that covers them) as lane l: page l % ppt
+        auto eload_lds = [&](int t) {
+            if (lane < ppt)
+                lds_dma16_buf(E + my_lo, (uint32_t)(my_hi - my_lo) * 16u,
+                              (uint32_t)min(t * ppt + lane, my_hi - my_lo - 1) * 16u, lds_e0 + (t & 1) * 64);
+        };
+        auto eread_lds = [&](int t) -> int4 {
+            asm volatile("" ::: "memory");                   // written by a load the compiler does not see
+            return sEnt[wave][t & 1][pgi];
+        };
         uint32_t flr = 0;
         // the flags, bounds and page of tile t (entries e) into stage st;
         // returns the byte offset of this wave's page in the pools
@@ -436,6 +450,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             int4 e3[NBUF - 1];
     #pragma unroll
             for (int j = 0; j < NBUF - 1; ++j) e3[j] = j < n_tiles ? eload(j) : int4{0, 0, 0, 0};
+            if (n_tiles > NBUF - 1) eload_lds(NBUF - 1);   // the first tile the loop issues
     #pragma unroll
             for (int j = 0; j < NBUF - 1; ++j)
                 if (j < n_tiles) dmas(j, prep(j, j, e3[j]));
@@ -471,10 +486,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         auto vphase = [&](int i, int js) {
             const bool act = js >= 0 && js < n_tiles;
             const bool full = act && ((flr >> (8 * (js % NBUF))) & 1);
-            const bool iss = i >= 1 && i + 2 < n_tiles;
-            const uint64_t poff = iss ? prep(i + 2, (i + 2) % NBUF, ent) : 0;
-            if (iss) dmas((i + 2) % NBUF, poff);
-            if (i + 3 < n_tiles) ent = eload(i + 3);
+            if (i >= 1 && i + 2 < n_tiles) {
+                // prepare tile i + 2 from the entries read last vector phase
+                // (the loads newer than them: at most the IPW of tile i + 1,
+                // and the counter ticket), read the entries of tile i + 3,
+                // then issue the loads of tile i + 2
+                wait_vmcnt<IPW>();
+                const uint64_t poff = prep(i + 2, (i + 2) % NBUF, eread_lds(i + 2));
+                if (i + 3 < n_tiles) eload_lds(i + 3);
+                dmas((i + 2) % NBUF, poff);
+            }
             if (act) softmax(js % NBUF, full, S, Pk);
         };
         auto mphase = [&](int i) {
@@ -484,10 +505,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         auto sync = [&](int i) {                             // tile i+1 is used from the next iteration on
             const int m = i + 1;
             // every wave's loads newer than those of tile m: the loads of tile
-            // m + 1 and the entries of tile m + 2
+            // m + 1, after the entry read of tile m + 2 (from iteration 1 on),
+            // which is small and finishes first, so waiting for all but the
+            // last IPW also covers it (thread 0's counter ticket, taken late
+            // in an item, only makes this wait longer)
             if (m < n_tiles) {
-                if (m + 2 < n_tiles) wait_vmcnt<IPW + 1>();
-                else if (m + 1 < n_tiles) wait_vmcnt<IPW>();
+                if (m + 1 < n_tiles) wait_vmcnt<IPW>();
                 else wait_vmcnt<0>();
             }
             // it publishes tile m and retires the stage that the next issue reuses
