@@ -483,16 +483,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         // waited for at the end of iteration m-1; its stage is free after
         // iteration m+1.
         const int n_it = n_tiles > 0 ? n_tiles + 1 : 0;
-        auto vphase = [&](int i, int js) {
+        // e: the entries of tile i + 2, read back at the start of the
+        // iteration (the barrier ending the previous one waited for them: they
+        // were loaded before the loads of tile i + 1)
+        auto vphase = [&](int i, int js, const int4 &e) {
             const bool act = js >= 0 && js < n_tiles;
             const bool full = act && ((flr >> (8 * (js % NBUF))) & 1);
             if (i >= 1 && i + 2 < n_tiles) {
-                // prepare tile i + 2 from the entries read last vector phase
-                // (the loads newer than them: at most the IPW of tile i + 1,
-                // and the counter ticket), read the entries of tile i + 3,
-                // then issue the loads of tile i + 2
-                wait_vmcnt<IPW>();
-                const uint64_t poff = prep(i + 2, (i + 2) % NBUF, eread_lds(i + 2));
+                // prepare tile i + 2, read the entries of tile i + 3, then
+                // issue the loads of tile i + 2
+                const uint64_t poff = prep(i + 2, (i + 2) % NBUF, e);
                 if (i + 3 < n_tiles) eload_lds(i + 3);
                 dmas((i + 2) % NBUF, poff);
             }
@@ -521,9 +521,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             const int i_ticket = max(0, n_it - 2);
             for (int i = 0; i < n_it; ++i) {
                 if (i == i_ticket && tid == 0) ticket = (int)atomicInc((unsigned *)P.work_ctr, 0xffffffffu);
+                const int4 e = eread_lds(i + 2);                 // lands during the matrix phase
                 mphase(i);
                 __builtin_amdgcn_sched_barrier(0);
-                vphase(i, i);
+                vphase(i, i, e);
                 __builtin_amdgcn_sched_barrier(0);
                 sync(i);
             }
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             for (int i = 0; i < n_it; ++i) {
                 const int pm = (flr >> (8 * (i % NBUF) + 1)) & 0x7f;
                 if (i < n_tiles && pm) fixup(i % NBUF, pm, 4 * 64, 4 * 64);   // before P.V(i), one iteration on
-                vphase(i, i - 1);
+                vphase(i, i - 1, eread_lds(i + 2));
                 __builtin_amdgcn_sched_barrier(0);
                 mphase(i);
                 __builtin_amdgcn_sched_barrier(0);
