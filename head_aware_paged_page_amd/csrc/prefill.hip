@@ -540,6 +540,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             }
         }
 
+        // The next item, published before the epilogue's stores are issued, so
+        // that waiting for the counter's answer (long since arrived) does not
+        // also wait for them.
+        if (tid == 0) s_item = (int)gridDim.x + ticket;
+
         // ---- epilogue
         const float l = l_run + xor_lane(l_run, 32);
         const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -573,10 +578,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 }
             if (h == 0) P.part_lse[part * BM + row] = lse;
         }
-        if (tid == 0) s_item = (int)gridDim.x + ticket;
-        __syncthreads();                     // every wave is done with this item; s_item is written
+        // Barriers on LDS only: every wave is done with this item's LDS (its tile
+        // loads were all waited for in the last iteration) and s_item is
+        // written; the epilogue's global stores stay in flight while the next
+        // item starts (nothing in this kernel reads them).
+        lds_barrier();
         b = __builtin_amdgcn_readfirstlane(s_item);
-        __syncthreads();                     // read before the next item's ticket overwrites it
+        lds_barrier();                       // read before the next item's ticket overwrites it
     }   // work items
 }
 
