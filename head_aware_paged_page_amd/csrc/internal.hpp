@@ -27,7 +27,8 @@ constexpr int kDecodeWaves = 4;
 // 256 CUs of the chip once; decode aims at about one streaming split per CU.
 // Every split still streams at least kMinSplitKeys keys.
 constexpr int kPlanCUs = 256;
-constexpr int kPrefillSetupTiles = 3;      // fixed cost of a prefill item, in 64-key tiles
+constexpr int kPrefillSetupTiles = 6;      // fixed cost of a prefill item (set-up, result, hand-off), in 64-key tiles
+constexpr int kPrefillEdgeTiles = 3;       // extra cost of a row end inside an item (bounds, fix-ups), in tiles
 constexpr double kMergeTiles = 1.5;        // merge pass per split prefill item, in 64-key tiles of one CU
 constexpr int kTargetDecodeItems = 384;
 constexpr int kMinSplitKeys = 512;

@@ -111,9 +111,16 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
         // histogram of CU loads: each class fills the least loaded CUs first.
         // A split item also writes its partial result (about a tile's time)
         // and the merge reads it back after the main pass (kMergeTiles per
-        // item, spread over the CUs).
+        // item, spread over the CUs).  An item that holds an end of its row
+        // (the start of a windowed row, the query tokens' own keys) pays for
+        // the tiles there that need bounds or zeroed value slots; the host
+        // cannot tell windowed rows from others, so every row start counts.
+        // The kernel cuts a q-tile's visible pages into ns chunks of
+        // ceil(pages / ns) rounded up to whole tiles; the last takes the rest.
         const int ppt = std::max(1, kPrefillKeysPerTile / page_size);
-        auto cost = [&](int64_t pages) { return (double)((pages + ppt - 1) / ppt + kPrefillSetupTiles); };
+        auto cost = [&](int64_t pages, int edges) {
+            return (double)((pages + ppt - 1) / ppt + kPrefillSetupTiles + edges * kPrefillEdgeTiles);
+        };
         int e_max = 1;
         for (int r = 0; r < n_rows; ++r) e_max = std::max(e_max, h_row_ptr[r + 1] - h_row_ptr[r]);
         std::map<double, int64_t, std::greater<double>> cls;   // cost -> items, longest first
@@ -129,9 +136,17 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
                 int ns, it;
                 const int e = h_row_ptr[r + 1] - h_row_ptr[r];
                 row_items(e, nq, c, &ns, &it);
-                cls[cost((e + ns - 1) / ns) + (ns > 1 ? 1.0 : 0.0)] += it;
                 *n_items += it;
-                if (ns > 1) n_parts += it;
+                if (ns == 1) {
+                    cls[cost(e, 2)] += it;
+                    continue;
+                }
+                n_parts += it;
+                const int64_t ch = ((e + ns - 1) / ns + ppt - 1) / ppt * ppt;
+                const int64_t last = std::max<int64_t>(1, e - (int64_t)(ns - 1) * ch);
+                cls[cost(ch, 1) + 1.0] += nq;                             // first chunk: the row start
+                if (ns > 2) cls[cost(ch, 0) + 1.0] += (int64_t)nq * (ns - 2);
+                cls[cost(last, 1) + 1.0] += nq;                           // last chunk: the query tokens
             }
             loads.clear();
             loads[0.0] = kPlanCUs;
