@@ -31,6 +31,7 @@ constexpr int kPrefillSetupTiles = 6;      // fixed cost of a prefill item (set-
 constexpr int kPrefillEdgeTiles = 3;       // extra cost of a row end inside an item (bounds, fix-ups), in tiles
 constexpr double kMergeTiles = 1.5;        // merge pass per split prefill item, in 64-key tiles of one CU
 constexpr int kTargetDecodeItems = 384;
+constexpr int kDecodeWgPerCU = 2;          // decode workgroups per CU the plan aims for
 constexpr int kMinSplitKeys = 512;
 constexpr int kMaxSplits = 1024;
 constexpr int kDecodeMaxChunk = 512;       // pages of one decode split (its entries are staged in LDS)

@@ -189,8 +189,38 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
         }
         p.chunk_pages = best_c;
     } else {
-        const int64_t c = (work + kTargetDecodeItems - 1) / kTargetDecodeItems;
-        p.chunk_pages = (int)std::min<int64_t>(kDecodeMaxChunk, std::max<int64_t>(min_chunk, c));
+        // Every item is resident at once (three fit on a CU), and a CU's share
+        // of the HBM stream depends on how many it holds: one decode workgroup
+        // per CU streams at about 4.5 TB/s chip-wide, two at about 6.6, and a
+        // CU holding one more than the rest finishes last.  So the chunk is the
+        // finest whose items fit kDecodeWgPerCU per CU (the item count falls
+        // as the chunk grows, so a bisection finds it); rows that alone
+        // outnumber that fall back to a fixed item target.
+        int e_max = 1;
+        for (int r = 0; r < n_rows; ++r) e_max = std::max(e_max, h_row_ptr[r + 1] - h_row_ptr[r]);
+        auto n_items = [&](int c) {
+            int64_t n = 0;
+            for (int r = 0; r < n_rows; ++r) {
+                int ns, it;
+                row_items(h_row_ptr[r + 1] - h_row_ptr[r], 1, c, &ns, &it);
+                n += it;
+            }
+            return n;
+        };
+        const int64_t slots = (int64_t)kDecodeWgPerCU * kPlanCUs;
+        int lo_c = std::max(min_chunk, (e_max + kMaxSplits - 1) / kMaxSplits);
+        int hi_c = std::max(lo_c, std::min(kDecodeMaxChunk, e_max));
+        if (n_items(hi_c) <= slots) {
+            while (lo_c < hi_c) {
+                const int mid = lo_c + (hi_c - lo_c) / 2;
+                if (n_items(mid) <= slots) hi_c = mid;
+                else lo_c = mid + 1;
+            }
+            p.chunk_pages = lo_c;
+        } else {
+            const int64_t c = (work + kTargetDecodeItems - 1) / kTargetDecodeItems;
+            p.chunk_pages = (int)std::min<int64_t>(kDecodeMaxChunk, std::max<int64_t>(min_chunk, c));
+        }
     }
     int64_t items = 0, parts = 0;
     for (int r = 0; r < n_rows; ++r) {
