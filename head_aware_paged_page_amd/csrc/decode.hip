@@ -37,14 +37,6 @@ struct DecodeParams {
     float scale_log2;
 };
 
-// Launch plan of a call with few rows, built on the host and passed by value
-// (kernel arguments), so such calls need no plan kernel: same meaning as the
-// workspace arrays of the same names.
-constexpr int kInlineRows = 192;
-struct InlinePlan {
-    int32_t item_ptr[kInlineRows + 1], item_ptr2[kInlineRows + 1], part_ptr[kInlineRows + 1];
-    int32_t nsplit[kInlineRows];
-};
 
 template <int D>
 struct Block {
@@ -334,20 +326,7 @@ int launch_decode(const AttnArgs &a, const Plan &p, hipStream_t stream) {
     const bool inl = p.n_rows <= kInlineRows && a.h_row_ptr != nullptr;
     InlinePlan L;
     if (inl) {
-        int32_t cl = 0, cs = 0, cp = 0;
-        for (int r = 0; r < p.n_rows; ++r) {
-            int ns, it;
-            row_items(a.h_row_ptr[r + 1] - a.h_row_ptr[r], 1, p.chunk_pages, &ns, &it);
-            L.nsplit[r] = ns;
-            L.item_ptr[r] = cl;
-            L.item_ptr2[r] = cs;
-            L.part_ptr[r] = cp;
-            if (ns > 1) { cl += it; cp += it; }
-            else cs += it;
-        }
-        L.item_ptr[p.n_rows] = cl;
-        L.item_ptr2[p.n_rows] = cs;
-        L.part_ptr[p.n_rows] = cp;
+        fill_inline_plan(p.n_rows, a.n_seq, a.h_row_ptr, nullptr, 1, p.chunk_pages, &L);
     } else {
         L.item_ptr[0] = 0;
         const int rc = launch_plan(p, a.d_row_ptr, nullptr, a.n_seq, a.ws, stream);

@@ -86,6 +86,45 @@ __device__ __forceinline__ int find_row(const int32_t *item_ptr, int n_rows, int
     return lo;
 }
 
+// Launch plan of a call with few rows, built on the host and passed by value
+// (kernel arguments), so such calls need no plan kernel: same meaning as the
+// workspace arrays of the same names (see item_of).
+constexpr int kInlineRows = 192;
+struct InlinePlan {
+    int32_t item_ptr[kInlineRows + 1], item_ptr2[kInlineRows + 1], part_ptr[kInlineRows + 1];
+    int32_t nsplit[kInlineRows];
+};
+
+// Host: fills L for n_rows <= kInlineRows rows, with the integer formulas of
+// the plan kernel.  h_tok_ptr: query tokens per sequence (prefill; its
+// q-tiles of tpt tokens), or nullptr (decode: one q-tile per row).
+inline void fill_inline_plan(int n_rows, int n_seq, const int32_t *h_row_ptr, const int32_t *h_tok_ptr, int tpt,
+                             int chunk_pages, InlinePlan *L) {
+    int32_t cl = 0, cs = 0, cp = 0;
+    for (int r = 0; r < n_rows; ++r) {
+        int nq = 1;
+        if (h_tok_ptr) {
+            const int q = r % n_seq;
+            nq = (h_tok_ptr[q + 1] - h_tok_ptr[q] + tpt - 1) / tpt;
+        }
+        int ns, it;
+        row_items(h_row_ptr[r + 1] - h_row_ptr[r], nq, chunk_pages, &ns, &it);
+        L->nsplit[r] = ns;
+        L->item_ptr[r] = cl;
+        L->item_ptr2[r] = cs;
+        L->part_ptr[r] = cp;
+        if (ns > 1) {
+            cl += it;
+            cp += it;
+        } else {
+            cs += it;
+        }
+    }
+    L->item_ptr[n_rows] = cl;
+    L->item_ptr2[n_rows] = cs;
+    L->part_ptr[n_rows] = cp;
+}
+
 // Row and index within the row of work item b.  Items are numbered long-first:
 // [0, item_ptr[n_rows]) are the items of split rows (first item of row r at
 // item_ptr[r]), the rest those of unsplit rows (at item_ptr[n_rows] + item_ptr2[r]).
@@ -184,5 +223,31 @@ __device__ __forceinline__ void lds_dma16_buf(const void *base, uint32_t bytes, 
 #else
 __device__ __forceinline__ void lds_dma16_buf(const void *, uint32_t, uint32_t, uint32_t) {}
 #endif
+
+// Work tickets of a persistent kernel from a 64-bit counter in the workspace
+// whose high half is the epoch of the call counting in it (a host counter,
+// never 0), so no call needs the counter cleared first.  A ticket is issued
+// early (ticket_issue: the counter's value before this increment) and
+// resolved when it is needed, so that nothing waits for the atomic before
+// then.  A value from another epoch means no ticket of this call was handed
+// out before: the first such wave installs {epoch, 1} and takes count 0, the
+// others then take a count again.  Every failed exchange means another wave
+// changed the counter since it was read, and before the install only each
+// wave's one increment can do so, so the loop ends.
+__device__ __forceinline__ unsigned long long ticket_issue(unsigned long long *ctr) {
+    typedef __attribute__((address_space(1))) unsigned long gul;
+    return __builtin_amdgcn_atomic_inc64((volatile gul *)(gul *)ctr, ~0ull, __ATOMIC_RELAXED, "agent");
+}
+__device__ __forceinline__ int ticket_resolve(unsigned long long *ctr, uint32_t epoch, unsigned long long v) {
+    if ((uint32_t)(v >> 32) == epoch) return (int)(uint32_t)v;
+    const unsigned long long first = ((unsigned long long)epoch << 32) + 1;
+    unsigned long long cur = v + 1;      // what this wave's increment left, if nothing moved it since
+    for (;;) {
+        const unsigned long long seen = atomicCAS(ctr, cur, first);
+        if (seen == cur) return 0;
+        if ((uint32_t)(seen >> 32) == epoch) return (int)(uint32_t)ticket_issue(ctr);
+        cur = seen;
+    }
+}
 
 }  // namespace sp

@@ -75,6 +75,7 @@ int launch_relocate(const void *k_in, void *k_out, int dtype, int page_size, int
 struct AttnArgs {
     int dtype, head_dim, page_size, group, n_seq, n_slot;
     const int32_t *h_row_ptr;   // host copy of d_row_ptr (launch planning)
+    const int32_t *h_tok_ptr;   // host copy of d_tok_ptr (prefill launch planning); decode: nullptr
     const int32_t *d_tok_ptr;   // prefill: [n_seq+1]; decode: nullptr
     const int32_t *d_q_pos;     // prefill: first query position per seq; decode: query position
     const int32_t *d_cls, *d_window, *d_row_ptr;

@@ -25,6 +25,8 @@
 // score registers of each lane are exactly the 8 consecutive keys the second
 // product's B operand wants - no shuffles between the two products.
 // Bounds come from positions and only boundary tiles evaluate them.
+#include <atomic>
+
 #include "device_common.hpp"
 
 namespace sp {
@@ -48,7 +50,8 @@ struct PrefillParams {
     int n_seq, n_rows, G, ps, tpt, Hq;
     int64_t n_phys;
     float scale_log2;   // softmax_scale * log2(e)
-    int *work_ctr;       // next work item to take; zeroed by the plan kernel
+    unsigned long long *work_ctr;   // work tickets: {epoch, count} (ticket_issue / ticket_resolve)
+    uint32_t epoch;                 // this call's epoch (never 0)
     int n_items;
 };
 
@@ -75,9 +78,9 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
-template <int D, int NW, int PS, int NBUF>
+template <int D, int NW, int PS, int NBUF, bool INL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(
-    PrefillParams P) {
+    PrefillParams P, InlinePlan L) {
     constexpr int BM = 32 * NW;
     constexpr int DK = D / 16;     // k-steps of the QK^T product
     constexpr int DT = D / 32;     // 32-dim tiles of the output
@@ -145,12 +148,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // is there when it ends and the order of asking still follows the order in
     // which workgroups fall free.
     for (int b = blockIdx.x; b < P.n_items;) {
-        int ticket = 0;                                  // thread 0's next counter value
+        unsigned long long ticket = 0;                   // thread 0's counter value, resolved at the item's end
 
         // ---- work item
         int r, local;
-        item_of(P.item_ptr, P.item_ptr2, P.n_rows, b, &r, &local);
-        const int ns = P.nsplit[r];
+        if constexpr (INL) item_of(L.item_ptr, L.item_ptr2, P.n_rows, b, &r, &local);
+        else item_of(P.item_ptr, P.item_ptr2, P.n_rows, b, &r, &local);
+        const int ns = INL ? L.nsplit[r] : P.nsplit[r];
         const int qt = local / ns, sp_i = local % ns;
         const int seq = r % P.n_seq, slot = r / P.n_seq;
         const int tok_base = P.tok_ptr[seq];
@@ -516,11 +520,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             // it publishes tile m and retires the stage that the next issue reuses
             lds_barrier();
         };
-        if (n_it == 0 && tid == 0) ticket = (int)atomicInc((unsigned *)P.work_ctr, 0xffffffffu);
+        if (n_it == 0 && tid == 0) ticket = ticket_issue(P.work_ctr);
         if (grp == 0) {
             const int i_ticket = max(0, n_it - 2);
             for (int i = 0; i < n_it; ++i) {
-                if (i == i_ticket && tid == 0) ticket = (int)atomicInc((unsigned *)P.work_ctr, 0xffffffffu);
+                if (i == i_ticket && tid == 0) ticket = ticket_issue(P.work_ctr);
                 const int4 e = eread_lds(i + 2);                 // lands during the matrix phase
                 mphase(i);
                 __builtin_amdgcn_sched_barrier(0);
@@ -543,7 +547,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         // The next item, published before the epilogue's stores are issued, so
         // that waiting for the counter's answer (long since arrived) does not
         // also wait for them.
-        if (tid == 0) s_item = (int)gridDim.x + ticket;
+        if (tid == 0) s_item = (int)gridDim.x + ticket_resolve(P.work_ctr, P.epoch, ticket);
 
         // ---- epilogue
         const float l = l_run + xor_lane(l_run, 32);
@@ -565,7 +569,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 }
             if (P.lse && h == 0) P.lse[(int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g] = lse;
         } else {
-            const int64_t part = (int64_t)P.part_ptr[r] + local;
+            const int64_t part = (int64_t)(INL ? L.part_ptr[r] : P.part_ptr[r]) + local;
             _Float16 *po = P.part_o + (part * BM + row) * D;
     #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
@@ -599,13 +603,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // many rows with few splits each, SG > 1 few rows with many splits.  The
 // partials are normalised (|o| <= max |v|), so fp16 keeps them to about
 // 5e-4 relative.
-template <int D, int SG>
-__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, int BM) {
+template <int D, int SG, bool INL>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, InlinePlan L, int BM) {
     constexpr int CH = D / 8, RPW = 64 / (CH * SG), RPB = 4 * RPW;   // rows per wave / workgroup
     static_assert(RPW >= 1 && 64 % (CH * SG) == 0, "a wave holds whole rows");
     int r, local;
-    item_of(P.item_ptr, P.item_ptr2, P.n_rows, blockIdx.x, &r, &local);
-    const int ns = P.nsplit[r];
+    if constexpr (INL) item_of(L.item_ptr, L.item_ptr2, P.n_rows, blockIdx.x, &r, &local);
+    else item_of(P.item_ptr, P.item_ptr2, P.n_rows, blockIdx.x, &r, &local);
+    const int ns = INL ? L.nsplit[r] : P.nsplit[r];
     if (ns == 1) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c = lane % CH, g0 = (lane / CH) % SG;
@@ -618,7 +623,7 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, int
     const int per = (nrows + ns - 1) / ns;
     const int row = sp_i * per + blockIdx.y * RPB + wave * RPW + lane / (CH * SG);
     if (row >= min(nrows, (sp_i + 1) * per)) return;   // whole rows: the exchanges below stay inside one
-    const int64_t part0 = (int64_t)P.part_ptr[r] + (int64_t)qt * ns;   // splits part0 .. part0+ns-1
+    const int64_t part0 = (int64_t)(INL ? L.part_ptr[r] : P.part_ptr[r]) + (int64_t)qt * ns;   // splits part0 .. part0+ns-1
     const float *lse = P.part_lse + part0 * BM + row;
     const _Float16 *src = P.part_o + (part0 * BM + row) * D + 8 * c;
     float m = -INFINITY, z = 0.f, o[8];
@@ -731,10 +736,34 @@ int launch_plan(const Plan &p, const int32_t *d_row_ptr, const int32_t *d_tok_pt
 
 int launch_prefill_f32(const AttnArgs &a, int64_t n_tok, hipStream_t stream);
 
+template <int D, int PS, bool INL>
+void launch_prefill_kernels(const PrefillParams &P, const InlinePlan &L, const Plan &p, bool merge_wide, dim3 grid,
+                            dim3 mgrid, hipStream_t stream) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, 8, PS, 4, INL>), grid, dim3(512), 0, stream, P, L);
+    if (p.n_parts && merge_wide)
+        hipLaunchKernelGGL((prefill_merge_kernel<D, 4, INL>), mgrid, dim3(256), 0, stream, P, L, p.rows_per_tile);
+    else if (p.n_parts)
+        hipLaunchKernelGGL((prefill_merge_kernel<D, 1, INL>), mgrid, dim3(256), 0, stream, P, L, p.rows_per_tile);
+}
+
 int launch_prefill(const AttnArgs &a, const Plan &p, int64_t n_tok, hipStream_t stream) {
     if (a.dtype == SP_F32) return launch_prefill_f32(a, n_tok, stream);
-    int rc = launch_plan(p, a.d_row_ptr, a.d_tok_ptr, a.n_seq, a.ws, stream);
-    if (rc) return rc;
+    // Few rows: the plan goes in the kernel arguments (no plan kernel, and an
+    // item's first reads are of kernel arguments); otherwise the plan kernel
+    // writes it to the workspace.  Either way the ticket counter needs no
+    // clearing: each call counts under its own epoch.
+    const bool inl = p.n_rows <= kInlineRows && a.h_row_ptr != nullptr && a.h_tok_ptr != nullptr;
+    InlinePlan L;
+    if (inl) {
+        fill_inline_plan(p.n_rows, a.n_seq, a.h_row_ptr, a.h_tok_ptr, p.tok_per_tile, p.chunk_pages, &L);
+    } else {
+        L.item_ptr[0] = 0;
+        const int rc = launch_plan(p, a.d_row_ptr, a.d_tok_ptr, a.n_seq, a.ws, stream);
+        if (rc) return rc;
+    }
+    static std::atomic<uint32_t> epochs{0};
+    uint32_t epoch = epochs.fetch_add(1) + 1;
+    if (epoch == 0) epoch = epochs.fetch_add(1) + 1;   // 0 is what a cleared counter holds
     char *w = (char *)a.ws;
     PrefillParams P;
     P.q = (const bf16 *)a.q;
@@ -762,7 +791,8 @@ int launch_prefill(const AttnArgs &a, const Plan &p, int64_t n_tok, hipStream_t 
     P.Hq = a.n_slot * a.group;
     P.n_phys = a.n_phys;
     P.scale_log2 = a.scale * kLog2e;
-    P.work_ctr = (int *)(w + p.off_zero + 128);
+    P.work_ctr = (unsigned long long *)(w + p.off_zero + 128);
+    P.epoch = epoch;
     P.n_items = (int)p.n_items;
     // merge: split groups per row from the rows each split item merges
     const bool merge_wide = p.merge_rows <= 16;
@@ -770,13 +800,10 @@ int launch_prefill(const AttnArgs &a, const Plan &p, int64_t n_tok, hipStream_t 
     const dim3 mgrid((unsigned)std::max<int64_t>(1, p.n_parts),
                      (unsigned)std::max(1, (p.merge_rows + merge_rpb - 1) / merge_rpb));
     const dim3 grid_persist((unsigned)std::min<int64_t>(p.n_items, kPlanCUs));
-#define SP_PREFILL_CASE(DD, PSV)                                                                        \
-    if (a.head_dim == DD && a.page_size == PSV) {                                                       \
-        hipLaunchKernelGGL((prefill_bf16_kernel<DD, 8, PSV, 4>), grid_persist, dim3(512), 0, stream, P); \
-        if (p.n_parts && merge_wide)                                                                    \
-            hipLaunchKernelGGL((prefill_merge_kernel<DD, 4>), mgrid, dim3(256), 0, stream, P, p.rows_per_tile); \
-        else if (p.n_parts)                                                                             \
-            hipLaunchKernelGGL((prefill_merge_kernel<DD, 1>), mgrid, dim3(256), 0, stream, P, p.rows_per_tile); \
+#define SP_PREFILL_CASE(DD, PSV)                                                                     \
+    if (a.head_dim == DD && a.page_size == PSV) {                                                    \
+        if (inl) launch_prefill_kernels<DD, PSV, true>(P, L, p, merge_wide, grid_persist, mgrid, stream);  \
+        else launch_prefill_kernels<DD, PSV, false>(P, L, p, merge_wide, grid_persist, mgrid, stream);     \
     }
     SP_PREFILL_CASE(128, 16) else SP_PREFILL_CASE(128, 32) else SP_PREFILL_CASE(128, 64)
     else SP_PREFILL_CASE(64, 16) else SP_PREFILL_CASE(64, 32) else SP_PREFILL_CASE(64, 64)

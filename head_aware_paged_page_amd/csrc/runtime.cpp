@@ -346,7 +346,7 @@ extern "C" int segpaged_prefill(int dtype, int head_dim, int page_size, int grou
     if (((uintptr_t)workspace) % 256) return fail(SP_EINVAL, "workspace must be 256-byte aligned");
     const int64_t n_tok = h_tok_ptr[n_seq];
     if (n_tok == 0) return SP_OK;
-    sp::AttnArgs a{dtype, head_dim, page_size, group, n_seq, n_slot, h_row_ptr, d_tok_ptr, d_q_pos0, d_cls, d_window,
+    sp::AttnArgs a{dtype, head_dim, page_size, group, n_seq, n_slot, h_row_ptr, h_tok_ptr, d_tok_ptr, d_q_pos0, d_cls, d_window,
                    d_row_ptr, d_entries, q, k_pool, v_pool, n_phys, softmax_scale, out, lse, workspace};
     return sp::launch_prefill(a, p, n_tok, (hipStream_t)stream);
 }
@@ -367,7 +367,7 @@ extern "C" int segpaged_decode(int dtype, int head_dim, int page_size, int group
     if (workspace_bytes < p.bytes)
         return fail(SP_EWORKSPACE, "workspace %zu bytes, %zu needed", workspace_bytes, p.bytes);
     if (((uintptr_t)workspace) % 256) return fail(SP_EINVAL, "workspace must be 256-byte aligned");
-    sp::AttnArgs a{dtype, head_dim, page_size, group, n_seq, n_slot, h_row_ptr, nullptr, d_q_pos, d_cls, d_window,
+    sp::AttnArgs a{dtype, head_dim, page_size, group, n_seq, n_slot, h_row_ptr, nullptr, nullptr, d_q_pos, d_cls, d_window,
                    d_row_ptr, d_entries, q, k_pool, v_pool, n_phys, softmax_scale, out, lse, workspace};
     return sp::launch_decode(a, p, (hipStream_t)stream);
 }
