@@ -131,22 +131,29 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
             int64_t n_parts = 0;
             for (int r = 0; r < n_rows; ++r) {
                 const int q = r % n_seq;
-                const int nq = (h_tok_ptr[q + 1] - h_tok_ptr[q] + p.tok_per_tile - 1) / p.tok_per_tile;
+                const int nt = h_tok_ptr[q + 1] - h_tok_ptr[q];
+                const int nq = (nt + p.tok_per_tile - 1) / p.tok_per_tile;
                 if (nq == 0) continue;
                 int ns, it;
                 const int e = h_row_ptr[r + 1] - h_row_ptr[r];
                 row_items(e, nq, c, &ns, &it);
                 *n_items += it;
-                if (ns == 1) {
-                    cls[cost(e, 2)] += it;
-                    continue;
+                if (ns > 1) n_parts += it;
+                for (int j = 0; j < nq; ++j) {
+                    // q-tile j sees at most the row's pages less those of the
+                    // chunk's later tokens (exact for a row without a window)
+                    const int t_end = std::min(nt, (j + 1) * p.tok_per_tile);
+                    const int64_t v = std::max(1, e - (nt - t_end) / page_size);
+                    if (ns == 1) {
+                        cls[cost(v, 2)] += 1;
+                        continue;
+                    }
+                    const int64_t ch = ((v + ns - 1) / ns + ppt - 1) / ppt * ppt;
+                    const int64_t last = std::max<int64_t>(1, v - (int64_t)(ns - 1) * ch);
+                    cls[cost(ch, 1) + 1.0] += 1;                          // first chunk: the row start
+                    if (ns > 2) cls[cost(ch, 0) + 1.0] += ns - 2;
+                    cls[cost(last, 1) + 1.0] += 1;                        // last chunk: the query tokens
                 }
-                n_parts += it;
-                const int64_t ch = ((e + ns - 1) / ns + ppt - 1) / ppt * ppt;
-                const int64_t last = std::max<int64_t>(1, e - (int64_t)(ns - 1) * ch);
-                cls[cost(ch, 1) + 1.0] += nq;                             // first chunk: the row start
-                if (ns > 2) cls[cost(ch, 0) + 1.0] += (int64_t)nq * (ns - 2);
-                cls[cost(last, 1) + 1.0] += nq;                           // last chunk: the query tokens
             }
             loads.clear();
             loads[0.0] = kPlanCUs;
