@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "internal.hpp"
@@ -223,6 +224,15 @@ __device__ __forceinline__ void lds_dma16_buf(const void *base, uint32_t bytes, 
 #else
 __device__ __forceinline__ void lds_dma16_buf(const void *, uint32_t, uint32_t, uint32_t) {}
 #endif
+
+// Host: the epoch of a call that counts in an epoch-tagged workspace counter
+// (ticket_issue / ticket_resolve); never 0, which is what a cleared counter holds.
+inline uint32_t next_epoch() {
+    static std::atomic<uint32_t> epochs{0};
+    uint32_t e = epochs.fetch_add(1) + 1;
+    if (e == 0) e = epochs.fetch_add(1) + 1;
+    return e;
+}
 
 // Work tickets of a persistent kernel from a 64-bit counter in the workspace
 // whose high half is the epoch of the call counting in it (a host counter,

@@ -25,8 +25,6 @@
 // score registers of each lane are exactly the 8 consecutive keys the second
 // product's B operand wants - no shuffles between the two products.
 // Bounds come from positions and only boundary tiles evaluate them.
-#include <atomic>
-
 #include "device_common.hpp"
 
 namespace sp {
@@ -761,9 +759,7 @@ int launch_prefill(const AttnArgs &a, const Plan &p, int64_t n_tok, hipStream_t 
         const int rc = launch_plan(p, a.d_row_ptr, a.d_tok_ptr, a.n_seq, a.ws, stream);
         if (rc) return rc;
     }
-    static std::atomic<uint32_t> epochs{0};
-    uint32_t epoch = epochs.fetch_add(1) + 1;
-    if (epoch == 0) epoch = epochs.fetch_add(1) + 1;   // 0 is what a cleared counter holds
+    const uint32_t epoch = next_epoch();
     char *w = (char *)a.ws;
     PrefillParams P;
     P.q = (const bf16 *)a.q;
