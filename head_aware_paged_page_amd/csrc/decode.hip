@@ -132,6 +132,16 @@ __global__ __launch_bounds__(NWD * 64) __attribute__((amdgpu_waves_per_eu(3, 3))
     const int my_hi = min(hi, my_lo + min(chunk, kDecodeMaxChunk));
     const int n_blocks = (my_hi - my_lo + ppb - 1) / ppb;
 
+    // Q^T B operand: head n of the slot, dims 32*s + 8*grp (read before the
+    // barrier below, so their latency overlaps that of the entries)
+    bf16x8 qf[DS];
+    {
+        const bool ok = n < G;
+        const bf16 *qrow = P.q + ((int64_t)seq * P.Hq + (int64_t)slot * G + (ok ? n : 0)) * D + 8 * grp;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) qf[s] = u4_as_bf16x8(ok ? *(const u32x4 *)(qrow + 32 * s) : u32x4{0, 0, 0, 0});
+    }
+
     // this split's table entries -> LDS, sanitised (out-of-range pages hold no token)
     for (int i = threadIdx.x; i < my_hi - my_lo; i += NWD * 64) {
         int4 en = E[my_lo + i];
@@ -141,14 +151,6 @@ __global__ __launch_bounds__(NWD * 64) __attribute__((amdgpu_waves_per_eu(3, 3))
     }
     __syncthreads();
 
-    // Q^T B operand: head n of the slot, dims 32*s + 8*grp
-    bf16x8 qf[DS];
-    {
-        const bool ok = n < G;
-        const bf16 *qrow = P.q + ((int64_t)seq * P.Hq + (int64_t)slot * G + (ok ? n : 0)) * D + 8 * grp;
-#pragma unroll
-        for (int s = 0; s < DS; ++s) qf[s] = u4_as_bf16x8(ok ? *(const u32x4 *)(qrow + 32 * s) : u32x4{0, 0, 0, 0});
-    }
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 acc[DT];

@@ -614,16 +614,20 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, Inl
     const int c = lane % CH, g0 = (lane / CH) % SG;
     const int qt = local / ns, sp_i = local % ns;
     const int seq = r % P.n_seq, slot = r / P.n_seq;
+    // Split s merges rows [s * per, (s + 1) * per) of the q-tile, per taken
+    // from the tile's row count BM (as the grid is), so that the partials'
+    // addresses do not wait for the q-tile's token count; rows past it are
+    // read (from inside the tile's partials) but not written.
+    const int per = (BM + ns - 1) / ns;
+    const int row = sp_i * per + blockIdx.y * RPB + wave * RPW + lane / (CH * SG);
+    const int rl = min(row, BM - 1);
     const int tok_base = P.tok_ptr[seq];
     const int t0 = qt * P.tpt;
     const int ntok = min(P.tpt, P.tok_ptr[seq + 1] - tok_base - t0);
     const int nrows = ntok * P.G;
-    const int per = (nrows + ns - 1) / ns;
-    const int row = sp_i * per + blockIdx.y * RPB + wave * RPW + lane / (CH * SG);
-    if (row >= min(nrows, (sp_i + 1) * per)) return;   // whole rows: the exchanges below stay inside one
     const int64_t part0 = (int64_t)(INL ? L.part_ptr[r] : P.part_ptr[r]) + (int64_t)qt * ns;   // splits part0 .. part0+ns-1
-    const float *lse = P.part_lse + part0 * BM + row;
-    const _Float16 *src = P.part_o + (part0 * BM + row) * D + 8 * c;
+    const float *lse = P.part_lse + part0 * BM + rl;
+    const _Float16 *src = P.part_o + (part0 * BM + rl) * D + 8 * c;
     float m = -INFINITY, z = 0.f, o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
@@ -655,7 +659,7 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, Inl
         for (int e = 0; e < 8; ++e) o[e] = o[e] * a + __shfl_xor(o[e], off, 64) * b;
         m = mm;
     }
-    if (g0 != 0) return;
+    if (g0 != 0 || row >= min(nrows, (sp_i + 1) * per)) return;   // whole rows: the exchanges above stay inside one
     const float inv = z > 0.f ? 1.f / z : 0.f;
     const int tq = row / P.G, g = row % P.G;
     const int64_t orow = (int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * P.G + g;
