@@ -181,6 +181,11 @@ int rope_relocate(const void *k_in, void *k_out, int dtype, int page_size, int h
  * kind SP_WS_PREFILL uses h_tok_ptr[n_seq+1] (query tokens of each sequence);
  * kind SP_WS_DECODE ignores it (one query token per sequence).  h_row_ptr is
  * the host copy of the call's row_ptr.  Writes *bytes (> 0).
+ *
+ * The workspace needs no initialisation: a call neither relies on what it
+ * holds before the call nor leaves anything a later call relies on (its work
+ * counter is tagged with the call's own epoch).  Calls that use the same
+ * workspace must not run concurrently (same stream, or ordered by events).
  */
 int segpaged_workspace_bytes(int kind, int dtype, int head_dim, int page_size, int group,
                              int n_seq, int n_slot, const int32_t *h_tok_ptr,
