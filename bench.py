@@ -200,7 +200,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs the hot path on a single MI355X and has no "
+        print("bench.py measures one GPU: the hot path runs on a single MI355X and has no "
               "multi-GPU mode (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 

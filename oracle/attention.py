@@ -12,7 +12,7 @@ Sources:
     arithmetic - every query still takes dot products with the keys and
     averages the values.
 
-Readings (listed in DESIGN.md): softmax scale 1/sqrt(D); LSE in natural log;
+Readings where the pages are silent: softmax scale 1/sqrt(D); LSE in natural log;
 query head h of a call belongs to slot h // group (contiguous GQA groups);
 attention is causal among new tokens for every class.
 """

@@ -16,7 +16,7 @@ Rotary embedding itself is the RoFormer construction (Su et al.), in the
 half-split pairing used by the Llama/Qwen model families the pages name:
 coordinate i is paired with i + D/2, frequency w_i = theta^(-2i/D), and the pair
 is rotated by the angle pos * w_i.  The pages do not fix the pairing; it is one
-constant for both sides, so parity does not depend on it (listed in the design doc).
+constant for both sides, so parity does not depend on it.
 """
 from __future__ import annotations
 

@@ -15,7 +15,7 @@ Sources, by the pages' titles:
     logical->physical block table, blocks taken from a global free pool on
     demand, the last block filled before a new one is claimed.
 
-Readings where the pages are silent (listed again in the design doc):
+Readings where the pages are silent:
   * A slot is one (layer, KV head); all query heads of its group share its
     class, table and pages.
   * Allocation order: slot -> sequence -> segment -> page, then the pages of the
