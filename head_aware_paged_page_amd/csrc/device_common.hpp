@@ -243,7 +243,9 @@ inline uint32_t next_epoch() {
 // out before: the first such wave installs {epoch, 1} and takes count 0, the
 // others then take a count again.  Every failed exchange means another wave
 // changed the counter since it was read, and before the install only each
-// wave's one increment can do so, so the loop ends.
+// wave's one increment can do so, so the loop ends.  (Epochs repeat only
+// after 2^32 - 1 calls; a workspace would have to sit unused for exactly
+// that many calls of the process for its counter to be mistaken as current.)
 __device__ __forceinline__ unsigned long long ticket_issue(unsigned long long *ctr) {
     typedef __attribute__((address_space(1))) unsigned long gul;
     return __builtin_amdgcn_atomic_inc64((volatile gul *)(gul *)ctr, ~0ull, __ATOMIC_RELAXED, "agent");
