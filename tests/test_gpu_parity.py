@@ -361,6 +361,22 @@ def test_end_to_end_32k():
     check_decode(w, rows=rows, keys_fn=reloc_keys)
 
 
+
+def test_many_rows_with_splits():
+    """More rows than fit a plan in the kernel arguments (200 > 192), so the plan
+    kernel writes both plans to the workspace, with rows long enough that prefill
+    and decode both split them: the merge kernels then read the workspace plan."""
+    classes = [(GLOBAL, 0) if s % 2 == 0 else (LOCAL, 64) for s in range(50)]
+    lay = custom_layout(seg_lens=[[6000]] * 4, offline=[[0]] * 4, n_prefill=16, n_decode=1, classes=classes,
+                        page_size=16, head_dim=64, group=2, dtype="bf16", name="many_rows", seed=3)
+    assert lay.n_slot * lay.n_seq == 200
+    w = _wl(lay)
+    rows = [slot * lay.n_seq + seq for slot in (0, 1, 24, 48, 49) for seq in range(lay.n_seq)]
+    w.prefill()
+    check_prefill(w, rows=rows)
+    w.decode()
+    check_decode(w, rows=rows)
+
 @pytest.mark.parametrize("fill", ["ones", "random"])
 def test_workspace_contents_do_not_matter(fill):
     """The prefill's work-ticket counter lives in the caller's workspace, which no
