@@ -96,11 +96,24 @@ struct InlinePlan {
     int32_t nsplit[kInlineRows];
 };
 
-// Host: fills L for n_rows <= kInlineRows rows, with the integer formulas of
-// the plan kernel.  h_tok_ptr: query tokens per sequence (prefill; its
-// q-tiles of tpt tokens), or nullptr (decode: one q-tile per row).
+// The prefill's inline plan: the same arrays for up to kPrefillInlineRows
+// rows, plus the call's row_ptr and tok_ptr, so that an item's first reads
+// of them are kernel arguments too (the struct stays under 4 KB of kernel
+// arguments with the prefill's parameters).
+constexpr int kPrefillInlineRows = 128;
+struct PrefillInlinePlan {
+    int32_t item_ptr[kPrefillInlineRows + 1], item_ptr2[kPrefillInlineRows + 1], part_ptr[kPrefillInlineRows + 1];
+    int32_t nsplit[kPrefillInlineRows];
+    int32_t row_ptr[kPrefillInlineRows + 1], tok_ptr[kPrefillInlineRows + 1];
+};
+
+// Host: fills L's item arrays for n_rows rows (at most the struct's capacity),
+// with the integer formulas of the plan kernel.  h_tok_ptr: query tokens per
+// sequence (prefill; its q-tiles of tpt tokens), or nullptr (decode: one
+// q-tile per row).
+template <class Plan_>
 inline void fill_inline_plan(int n_rows, int n_seq, const int32_t *h_row_ptr, const int32_t *h_tok_ptr, int tpt,
-                             int chunk_pages, InlinePlan *L) {
+                             int chunk_pages, Plan_ *L) {
     int32_t cl = 0, cs = 0, cp = 0;
     for (int r = 0; r < n_rows; ++r) {
         int nq = 1;

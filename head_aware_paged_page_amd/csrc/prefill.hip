@@ -78,7 +78,7 @@ __device__ __forceinline__ void lds_barrier() {
 
 template <int D, int NW, int PS, int NBUF, bool INL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(
-    PrefillParams P, InlinePlan L) {
+    PrefillParams P, PrefillInlinePlan L) {
     constexpr int BM = 32 * NW;
     constexpr int DK = D / 16;     // k-steps of the QK^T product
     constexpr int DT = D / 32;     // 32-dim tiles of the output
@@ -155,9 +155,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int ns = INL ? L.nsplit[r] : P.nsplit[r];
         const int qt = local / ns, sp_i = local % ns;
         const int seq = r % P.n_seq, slot = r / P.n_seq;
-        const int tok_base = P.tok_ptr[seq];
+        const int tok_base = INL ? L.tok_ptr[seq] : P.tok_ptr[seq];
         const int t0 = qt * P.tpt;
-        const int ntok = min(P.tpt, P.tok_ptr[seq + 1] - tok_base - t0);
+        const int ntok = min(P.tpt, (INL ? L.tok_ptr[seq + 1] : P.tok_ptr[seq + 1]) - tok_base - t0);
         const int p0 = P.q_pos0[seq] + t0, p_last = p0 + ntok - 1;
         const int G = P.G;
         const bool is_local = P.cls[slot] == SP_LOCAL;
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         }
 
         // ---- the q-tile's visible entry range, then this split's share
-        const int e_beg = P.row_ptr[r], e_end = P.row_ptr[r + 1];
+        const int e_beg = INL ? L.row_ptr[r] : P.row_ptr[r], e_end = INL ? L.row_ptr[r + 1] : P.row_ptr[r + 1];
         const int4 *E = P.entries;
         int lo, hi;
         visible_range(E, e_beg, e_end, p_last, is_local, p0 - W, &lo, &hi);
@@ -602,7 +602,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // partials are normalised (|o| <= max |v|), so fp16 keeps them to about
 // 5e-4 relative.
 template <int D, int SG, bool INL>
-__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, InlinePlan L, int BM) {
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, PrefillInlinePlan L, int BM) {
     constexpr int CH = D / 8, RPW = 64 / (CH * SG), RPB = 4 * RPW;   // rows per wave / workgroup
     static_assert(RPW >= 1 && 64 % (CH * SG) == 0, "a wave holds whole rows");
     int r, local;
@@ -621,9 +621,9 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, Inl
     const int per = (BM + ns - 1) / ns;
     const int row = sp_i * per + blockIdx.y * RPB + wave * RPW + lane / (CH * SG);
     const int rl = min(row, BM - 1);
-    const int tok_base = P.tok_ptr[seq];
+    const int tok_base = INL ? L.tok_ptr[seq] : P.tok_ptr[seq];
     const int t0 = qt * P.tpt;
-    const int ntok = min(P.tpt, P.tok_ptr[seq + 1] - tok_base - t0);
+    const int ntok = min(P.tpt, (INL ? L.tok_ptr[seq + 1] : P.tok_ptr[seq + 1]) - tok_base - t0);
     const int nrows = ntok * P.G;
     const int64_t part0 = (int64_t)(INL ? L.part_ptr[r] : P.part_ptr[r]) + (int64_t)qt * ns;   // splits part0 .. part0+ns-1
     const float *lse = P.part_lse + part0 * BM + rl;
@@ -739,7 +739,7 @@ int launch_plan(const Plan &p, const int32_t *d_row_ptr, const int32_t *d_tok_pt
 int launch_prefill_f32(const AttnArgs &a, int64_t n_tok, hipStream_t stream);
 
 template <int D, int PS, bool INL>
-void launch_prefill_kernels(const PrefillParams &P, const InlinePlan &L, const Plan &p, bool merge_wide, dim3 grid,
+void launch_prefill_kernels(const PrefillParams &P, const PrefillInlinePlan &L, const Plan &p, bool merge_wide, dim3 grid,
                             dim3 mgrid, hipStream_t stream) {
     hipLaunchKernelGGL((prefill_bf16_kernel<D, 8, PS, 4, INL>), grid, dim3(512), 0, stream, P, L);
     if (p.n_parts && merge_wide)
@@ -754,10 +754,12 @@ int launch_prefill(const AttnArgs &a, const Plan &p, int64_t n_tok, hipStream_t 
     // item's first reads are of kernel arguments); otherwise the plan kernel
     // writes it to the workspace.  Either way the ticket counter needs no
     // clearing: each call counts under its own epoch.
-    const bool inl = p.n_rows <= kInlineRows && a.h_row_ptr != nullptr && a.h_tok_ptr != nullptr;
-    InlinePlan L;
+    const bool inl = p.n_rows <= kPrefillInlineRows && a.h_row_ptr != nullptr && a.h_tok_ptr != nullptr;
+    PrefillInlinePlan L;
     if (inl) {
         fill_inline_plan(p.n_rows, a.n_seq, a.h_row_ptr, a.h_tok_ptr, p.tok_per_tile, p.chunk_pages, &L);
+        for (int r = 0; r <= p.n_rows; ++r) L.row_ptr[r] = a.h_row_ptr[r];
+        for (int q = 0; q <= a.n_seq; ++q) L.tok_ptr[q] = a.h_tok_ptr[q];
     } else {
         L.item_ptr[0] = 0;
         const int rc = launch_plan(p, a.d_row_ptr, a.d_tok_ptr, a.n_seq, a.ws, stream);

@@ -363,7 +363,8 @@ def test_end_to_end_32k():
 
 
 def test_many_rows_with_splits():
-    """More rows than fit a plan in the kernel arguments (200 > 192), so the plan
+    """More rows than fit a plan in the kernel arguments (200 > 128 for prefill,
+    > 192 for decode), so the plan
     kernel writes both plans to the workspace, with rows long enough that prefill
     and decode both split them: the merge kernels then read the workspace plan."""
     classes = [(GLOBAL, 0) if s % 2 == 0 else (LOCAL, 64) for s in range(50)]
