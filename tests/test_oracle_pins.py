@@ -268,3 +268,36 @@ def test_allocation_is_a_prefix_of_the_free_list_and_disjoint():
     assert len(set(storage.tolist())) == len(storage)
     with pytest.raises(MemoryError):
         otab.allocate(lay, free[: len(storage) - 1])
+
+
+# ---------------------------------------------------------------- per-head page pack / unpack
+from oracle import pack as opack  # noqa: E402
+
+
+def _hand_pool(n_pages, ps, D):
+    k = np.array([[[100 * p + 10 * s + d for d in range(D)] for s in range(ps)] for p in range(n_pages)], np.float64)
+    v = np.array([[[-(100 * p + 10 * d + s) for s in range(ps)] for d in range(D)] for p in range(n_pages)], np.float64)
+    return k, v
+
+
+def test_pack_matches_hand_worked_example():
+    """tests/golden/pack_by_hand.json: packed pages of a hand-written table, worked out by hand."""
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pack_by_hand.json")))
+    k, v = _hand_pool(g["n_pages"], g["page_size"], g["head_dim"])
+    kp, vp = opack.pack(k, v, np.array(g["phys"]))
+    assert np.array_equal(kp, np.array(g["k_packed"], np.float64))
+    assert np.array_equal(vp, np.array(g["v_packed"], np.float64))
+
+
+def test_pack_unpack_round_trip_restores_exactly_the_listed_pages():
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((40, 16, 8))
+    v = rng.standard_normal((40, 8, 16))
+    phys = rng.choice(40, size=17, replace=False)
+    kp, vp = opack.pack(k, v, phys)
+    assert kp.nbytes + vp.nbytes == 17 * (k[0].nbytes + v[0].nbytes)   # bytes = listed pages only
+    k2, v2 = opack.unpack(kp, vp, phys, np.zeros_like(k), np.zeros_like(v))
+    listed = np.zeros(40, bool)
+    listed[phys] = True
+    assert np.array_equal(k2[listed], k[listed]) and np.array_equal(v2[listed], v[listed])
+    assert not k2[~listed].any() and not v2[~listed].any()
