@@ -294,6 +294,29 @@ def main():
         "roofline": roof,
         "calls": calls,
     }
+    # A row beyond the step, measured on its own: the per-head visible-page
+    # pack (the pages the decode tables list, gathered in table order), not
+    # part of the step or its value.  Bytes: every listed K and V page read
+    # once and written once.
+    import head_aware_paged_page_amd.segpaged as sp
+    n_ent = int(w.td["row_ptr"][-1])
+    k_pk = torch.empty((n_ent,) + tuple(w.k_pool.shape[1:]), dtype=w.k_pool.dtype, device="cuda")
+    v_pk = torch.empty((n_ent,) + tuple(w.v_pool.shape[1:]), dtype=w.v_pool.dtype, device="cuda")
+    for _ in range(3):
+        sp.pack_pages(w.k_pool, w.v_pool, w.d_entries, n_ent, k_pk, v_pk)
+    torch.cuda.synchronize()
+    pe = [HipEvent() for _ in range(2)]
+    reps = 20
+    pe[0].record(stream)
+    for _ in range(reps):
+        sp.pack_pages(w.k_pool, w.v_pool, w.d_entries, n_ent, k_pk, v_pk)
+    pe[1].record(stream)
+    torch.cuda.synchronize()
+    t_pack = HipEvent.elapsed_ms(pe[0], pe[1]) / reps
+    pack_bytes = 2 * (k_pk.numel() + v_pk.numel()) * k_pk.element_size()
+    res["beyond_step"] = {"pack_pages": {"ms": round(t_pack, 4), "GB/s": round(pack_bytes / t_pack / 1e6, 1),
+                                         "frac_hbm": round(pack_bytes / t_pack / 1e-3 / PEAK_HBM, 4),
+                                         "bytes": pack_bytes, "pages": n_ent}}
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a CPU sample ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -90,5 +90,7 @@ struct AttnArgs {
 
 int launch_prefill(const AttnArgs &a, const Plan &p, int64_t n_tok, hipStream_t s);
 int launch_decode(const AttnArgs &a, const Plan &p, hipStream_t s);
+int launch_page_copy(bool unpack, const void *d_entries, int64_t n, const void *src_k, const void *src_v,
+                     void *dst_k, void *dst_v, int64_t n_phys, int page_bytes, hipStream_t s);
 
 }  // namespace sp

@@ -378,3 +378,34 @@ extern "C" int segpaged_decode(int dtype, int head_dim, int page_size, int group
                    d_row_ptr, d_entries, q, k_pool, v_pool, n_phys, softmax_scale, out, lse, workspace};
     return sp::launch_decode(a, p, (hipStream_t)stream);
 }
+
+static int page_copy(bool unpack, int dtype, int head_dim, int page_size, int64_t n_entries, const sp_entry *d_entries,
+                     const void *src_k, const void *src_v, void *dst_k, void *dst_v, int64_t n_phys, void *stream) {
+    sp::clear_error();
+    if (dtype != SP_F32 && dtype != SP_BF16) return fail(SP_EINVAL, "dtype %d", dtype);
+    if (head_dim < 16 || head_dim > 256 || head_dim % 16)
+        return fail(SP_EUNSUPPORTED, "head_dim %d (16..256, multiple of 16)", head_dim);
+    if (page_size < 1 || page_size > 1024) return fail(SP_EUNSUPPORTED, "page_size %d (1..1024)", page_size);
+    if (n_entries < 0 || n_phys < 0) return fail(SP_EINVAL, "n_entries=%lld n_phys=%lld", (long long)n_entries,
+                                                  (long long)n_phys);
+    if (n_entries == 0) return SP_OK;
+    if (!d_entries || !src_k || !src_v || !dst_k || !dst_v) return fail(SP_EINVAL, "a pointer is NULL");
+    const int64_t page_bytes = (int64_t)page_size * head_dim * (dtype == SP_F32 ? 4 : 2);
+    if (page_bytes > INT32_MAX) return fail(SP_EINVAL, "page too large");
+    return sp::launch_page_copy(unpack, d_entries, n_entries, src_k, src_v, dst_k, dst_v, n_phys, (int)page_bytes,
+                                (hipStream_t)stream);
+}
+
+extern "C" int segpaged_pack_pages(int dtype, int head_dim, int page_size, int64_t n_entries,
+                                   const sp_entry *d_entries, const void *k_pool, const void *v_pool, int64_t n_phys,
+                                   void *k_out, void *v_out, void *stream) {
+    return page_copy(false, dtype, head_dim, page_size, n_entries, d_entries, k_pool, v_pool, k_out, v_out, n_phys,
+                     stream);
+}
+
+extern "C" int segpaged_unpack_pages(int dtype, int head_dim, int page_size, int64_t n_entries,
+                                     const sp_entry *d_entries, const void *k_in, const void *v_in, void *k_pool,
+                                     void *v_pool, int64_t n_phys, void *stream) {
+    return page_copy(true, dtype, head_dim, page_size, n_entries, d_entries, k_in, v_in, k_pool, v_pool, n_phys,
+                     stream);
+}

@@ -45,13 +45,15 @@ def lib() -> ctypes.CDLL:
         L.segpaged_workspace_bytes.argtypes = [I, I, I, I, I, I, I, P, P, ctypes.POINTER(SZ)]
         L.segpaged_prefill.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, I64, F, P, P, P, SZ, P]
         L.segpaged_decode.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, I64, F, P, P, P, SZ, P]
+        L.segpaged_pack_pages.argtypes = [I, I, I, I64, P, P, P, I64, P, P, P]
+        L.segpaged_unpack_pages.argtypes = [I, I, I, I64, P, P, P, P, P, I64, P]
         L.segpaged_strerror.restype = ctypes.c_char_p
         L.segpaged_strerror.argtypes = [I]
         L.segpaged_last_error.restype = ctypes.c_char_p
         L.segpaged_last_error.argtypes = []
         L.segpaged_version.restype = I
         for fn in ("segpaged_build_tables", "rope_relocate", "segpaged_workspace_bytes", "segpaged_prefill",
-                   "segpaged_decode"):
+                   "segpaged_decode", "segpaged_pack_pages", "segpaged_unpack_pages"):
             getattr(L, fn).restype = I
         _lib = L
     return _lib
@@ -174,6 +176,25 @@ def decode(q, k_pool, v_pool, *, page_size, group, n_seq, n_slot, h_row_ptr, d_q
                                _dptr(k_pool), _dptr(v_pool), k_pool.shape[0], float(scale), _dptr(out), _dptr(lse),
                                _dptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "segpaged_decode")
+
+
+
+def pack_pages(k_pool, v_pool, d_entries, n_entries: int, k_out, v_out, stream=None):
+    """segpaged_pack_pages.  Pools [n_phys, ps, D] (K) and [n_phys, D, ps] (V); outputs [n_entries, ...] alike."""
+    D = k_pool.shape[-1]
+    rc = lib().segpaged_pack_pages(_dtype_code(k_pool), D, k_pool.shape[1], int(n_entries), _dptr(d_entries),
+                                   _dptr(k_pool), _dptr(v_pool), k_pool.shape[0], _dptr(k_out), _dptr(v_out),
+                                   _stream(stream))
+    _check(rc, "segpaged_pack_pages")
+
+
+def unpack_pages(k_in, v_in, d_entries, n_entries: int, k_pool, v_pool, stream=None):
+    """segpaged_unpack_pages: packed page e back to pool page d_entries[e].phys."""
+    D = k_pool.shape[-1]
+    rc = lib().segpaged_unpack_pages(_dtype_code(k_pool), D, k_pool.shape[1], int(n_entries), _dptr(d_entries),
+                                     _dptr(k_in), _dptr(v_in), _dptr(k_pool), _dptr(v_pool), k_pool.shape[0],
+                                     _stream(stream))
+    _check(rc, "segpaged_unpack_pages")
 
 
 def version() -> int:

@@ -248,6 +248,34 @@ int segpaged_decode(int dtype, int head_dim, int page_size, int group, int n_seq
 const char *segpaged_strerror(int status);
 const char *segpaged_last_error(void);
 
+/*
+ * segpaged_pack_pages / segpaged_unpack_pages - gather the pages that a set of
+ * table entries lists, in entry order, into contiguous K and V buffers, and
+ * scatter such buffers back into pools (device).
+ *
+ * Defines: the product profile's section 3 and the is96.com commentary's
+ * paragraphs on the per-head page table: a head reads only the pages its
+ * table lists, so when prefill and decode run on different machines only
+ * those pages need to move; these calls are the single-GPU gather and
+ * scatter around such a transfer.  For e = 0 .. n_entries-1, p = d_entries[e].phys:
+ *   pack:   k_out[e] = k_pool[p]   ([page_size][head_dim])
+ *           v_out[e] = v_pool[p]   ([head_dim][page_size])
+ *   unpack: k_pool[p] = k_in[e],  v_pool[p] = v_in[e]
+ * Whole pages are copied; a p outside [0, n_phys) packs as zeros and is
+ * skipped by unpack.  d_entries is typically a table's entries
+ * (d_row_ptr[n_rows] of them).  All buffers are device memory owned by the
+ * caller; packed buffers hold n_entries pages.  Unpacking entries that list
+ * the same page twice leaves either copy.  dtype SP_BF16 or SP_F32.
+ * Errors: SP_EINVAL (bad size, NULL pointer), SP_EUNSUPPORTED (head_dim,
+ * page_size); a launch failure returns its HIP error mapped as for the other calls.
+ */
+int segpaged_pack_pages(int dtype, int head_dim, int page_size, int64_t n_entries, const sp_entry *d_entries,
+                        const void *k_pool, const void *v_pool, int64_t n_phys, void *k_out, void *v_out,
+                        void *stream);
+int segpaged_unpack_pages(int dtype, int head_dim, int page_size, int64_t n_entries, const sp_entry *d_entries,
+                          const void *k_in, const void *v_in, void *k_pool, void *v_pool, int64_t n_phys,
+                          void *stream);
+
 /* ABI version (major * 100 + minor). */
 int segpaged_version(void);
 

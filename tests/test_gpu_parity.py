@@ -378,6 +378,38 @@ def test_many_rows_with_splits():
     w.decode()
     check_decode(w, rows=rows)
 
+
+def _raw(t):
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["small0", "32k"])
+def test_pack_unpack_pages_bit_exact(name):
+    """Per-head visible-page pack (the pages the decode tables list, in table
+    order) and unpack, against the oracle, bit for bit on the raw page bytes
+    (NaN-filled empty slots included).  On the small layout two entries are
+    pointed outside the pool: they pack as zeros and unpack to nothing."""
+    from oracle import pack as opack
+    import head_aware_paged_page_amd.segpaged as sp
+    w = _wl(_small(0)) if name == "small0" else cached("32k")
+    ent = torch.as_tensor(np.asarray(w.td["entries"]).reshape(-1, 4), dtype=torch.int32).clone()
+    if name == "small0":
+        ent[1, 0] = w.n_phys + 5
+        ent[-1, 0] = -1
+    n = ent.shape[0]
+    d_ent = ent.cuda()
+    k_out = torch.empty((n,) + tuple(w.k_pool.shape[1:]), dtype=w.k_pool.dtype, device="cuda")
+    v_out = torch.empty((n,) + tuple(w.v_pool.shape[1:]), dtype=w.v_pool.dtype, device="cuda")
+    sp.pack_pages(w.k_pool, w.v_pool, d_ent, n, k_out, v_out)
+    k_zero, v_zero = torch.zeros_like(w.k_pool), torch.zeros_like(w.v_pool)
+    sp.unpack_pages(k_out, v_out, d_ent, n, k_zero, v_zero)
+    torch.cuda.synchronize()
+    phys = ent[:, 0].numpy()
+    kp, vp = opack.pack(_raw(w.k_pool), _raw(w.v_pool), phys)
+    assert np.array_equal(_raw(k_out), kp) and np.array_equal(_raw(v_out), vp)
+    ku, vu = opack.unpack(kp, vp, phys, np.zeros_like(kp, shape=w.k_pool.shape), np.zeros_like(vp, shape=w.v_pool.shape))
+    assert np.array_equal(_raw(k_zero), ku) and np.array_equal(_raw(v_zero), vu)
+
 @pytest.mark.parametrize("fill", ["ones", "random"])
 def test_workspace_contents_do_not_matter(fill):
     """The prefill's work-ticket counter lives in the caller's workspace, which no
