@@ -14,8 +14,8 @@ namespace sp {
 namespace {
 
 constexpr int kPackThreads = 256;
-constexpr int kPackPages = 4;    // table entries per workgroup
-constexpr int kPackBatch = 8;    // 16-byte chunks per thread in flight together
+constexpr int kPackPages = 2;    // table entries per workgroup (1, 2 and 4 with 4-16 loads measured within 1 %; 4 with 8: 8 % slower)
+constexpr int kPackBatch = 4;    // 16-byte chunks per thread in flight together
 
 // UNPACK = false: dst_k/dst_v are the packed buffers, src the pools;
 // UNPACK = true: src the packed buffers, dst the pools.  An entry whose page

@@ -39,6 +39,7 @@ KERNELS = [
     ("decode_merge_kernel", "segpaged_decode", "decode_merge_kernel"),
     ("prefill_f32_kernel", "segpaged_prefill", "prefill_f32_kernel"),
     ("decode_f32_kernel", "segpaged_decode", "decode_f32_kernel"),
+    ("page_copy_kernel", "segpaged_pack_pages", "page_copy_kernel"),
 ]
 KERNEL_SOURCES = {
     "rope_relocate": ["relocate.hip"],
