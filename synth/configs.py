@@ -60,6 +60,15 @@ CONFIGS = {
                   seg_lo=2048, seg_hi=8192, off_lo=0, off_hi=65536),
         n_prefill=256, n_decode=1,
     ),
+    # Head-level recovery prefill: the global slots of the 32K workload
+    # recomputed in full, every context token a query (causal, one chunk).
+    "recovery32k": dict(
+        idx=5, n_layers=1, n_kv=10, group=4, head_dim=128, dtype="bf16", page_size=16,
+        theta=10000.0, k_scale=0.5,
+        slot_classes=[(GLOBAL, 0)] * 10,
+        seqs=dict(kind="fixed", seg_lens=[], offline=[]),
+        n_prefill=30000, n_decode=1,
+    ),
 }
 
 ORDER = ["tiny", "32k", "16k", "128k", "batch"]
