@@ -8,17 +8,27 @@ resident in HBM before the timed region:
   segpaged_prefill the new-token chunk of every (layer, KV head) slot, one call
   segpaged_decode  one decode token per sequence over every slot
 The page tables are built once beforehand by segpaged_build_tables on the
-host; its time is reported separately (build_tables_ms).
+host; its time is reported separately (build_tables), as is the host-side
+launch planning inside each prefill and decode call (plan_host_ms).
 
-Work counted is algorithmic only:
+Cache-clean timing.  The chip's last-level cache (256 MB) could serve a call
+data that the previous call just read (decode reads the global slots' pages
+prefill read a moment before).  So the pools exist in R identical replicas and
+step i runs relocate on replica i mod R, prefill on replica (i+1) mod R and
+decode on replica (i+2) mod R: with R = 3, at least one full relocation pass
+(about 1 GB at 32K) lies between two calls that touch the same replica.  A
+workload whose pools are too large for three copies runs with R = 1; its
+calls each move several GB.
+
+Work counted is algorithmic only, from the host tables (never from the GPU):
   prefill FLOPs = 4 * head_dim per (query row, visible key) pair;
   prefill bytes = K and V of every page in each head's table, read once
-                  (the chunk's queries share them) + q/out;
+                  (the chunk's queries share them) + q/out + table entries;
   relocate bytes = 2 * (valid segment-key elements) * elem + 16 B per list item;
   decode bytes  = per slot, visible keys * 2 * head_dim * elem (K and V read
                   once, shared by the group's heads) + q/out + table entries.
-Visible counts are read back from the HIP path itself with zero queries
-(every weight is then exactly 1, so exp(LSE) is the count).
+A key of a table entry (pos_start, n_valid) is visible to a query at position
+p when its position is <= p and, for a local slot of window W, > p - W.
 
 The reported value is the whole step's share of the MI355X roofline:
 100 * (max(prefill FLOPs / 2.5 PFLOP/s, prefill bytes / 8 TB/s)
@@ -26,17 +36,21 @@ The reported value is the whole step's share of the MI355X roofline:
 (A 64-token chunk over a shared KV page does 4 * 256 rows FLOPs per 4 bytes
 of K and V: about 256 FLOP/B, below the chip's 312 FLOP/B ridge, so the
 prefill of such a chunk is bound by HBM, not by the matrix cores.)
+
+With the default workload (32K) the same line also carries the 128K
+microbenchmark, measured the same way, under "config_128k".
 """
 from __future__ import annotations
 
 import argparse
 import glob
-import hashlib
 import json
-import math
+import multiprocessing as mp
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -45,6 +59,7 @@ METRIC = "segpaged prefill TFLOP/s + decode/relocate GB/s at 32K & 128K, % of ro
 PEAK_BF16_FLOPS = 2.5e15
 PEAK_FP32_FLOPS = 157.3e12
 PEAK_HBM = 8.0e12
+LOCAL = 1
 WORKLOAD_TEXT = {
     "32k": "32K RAG: 8 layers x 8 KV heads (64 slots), 32 q-heads/8 KV (G=4), head_dim 128, bf16, page 16; "
            "6 reused segments x 5000 tokens (offline base 0) + 64-token question + 1 decode token; "
@@ -59,6 +74,8 @@ WORKLOAD_TEXT = {
     "recovery32k": "head-level recovery prefill: the 10 global slots of the 32K workload (G=4, head_dim 128, bf16, "
                    "page 16) recomputed in full, 30000 context tokens as one causal query chunk + 1 decode token",
 }
+MAX_REPLICA_BYTES = 24 << 30     # pools of all replicas together
+MAX_CPU_QUERIES = 128            # query tokens per row the oracle baseline runs (evenly spaced)
 from head_aware_paged_page_amd.profiling import source_hash  # noqa: E402
 
 
@@ -74,83 +91,136 @@ def committed_traffic(call: str, workload: str):
     return None
 
 
-def algorithmic_work(w, torch):
-    """Visible counts from the HIP path with zero queries, then FLOPs / bytes."""
-    import numpy as np
+# ----------------------------------------------------------------------------- algorithmic work
+
+def table_visible_counts(row_ptr, entries, cls, window, n_seq, q_pos_of_seq):
+    """Visible keys of each query of each row, from the row's table alone.
+
+    Row r = slot * n_seq + seq; entries[:, 1:3] = (pos_start, n_valid) in
+    ascending position.  Returns a list over rows of int64 arrays, one count per
+    position in q_pos_of_seq[seq]: the table's keys at positions <= p, less
+    (local slots) those at positions <= p - W."""
+    out = []
+    for r in range(len(row_ptr) - 1):
+        slot, seq = divmod(r, n_seq)
+        e = np.asarray(entries[row_ptr[r]:row_ptr[r + 1]], np.int64)
+        s, n = e[:, 1], e[:, 2]
+        before = np.concatenate([[0], np.cumsum(n)])
+
+        def upto(x):
+            i = np.searchsorted(s, x, side="right") - 1
+            j = np.maximum(i, 0)
+            return np.where(i >= 0, before[j] + np.minimum(n[j], x - s[j] + 1), 0)
+
+        p = np.asarray(q_pos_of_seq[seq], np.int64)
+        c = upto(p)
+        if int(cls[slot]) == LOCAL:
+            c = c - upto(p - int(window[slot]))
+        out.append(c)
+    return out
+
+
+def algorithmic_work(w):
     lay = w.lay
     esz = 4 if lay.dtype == "f32" else 2
-    zq = torch.zeros_like(w.q_prefill)
-    zd = torch.zeros_like(w.q_decode)
-    _, lp = w.prefill(q=zq, out=torch.empty_like(zq), lse=torch.empty_like(w.lse_prefill))
-    _, ld = w.decode(q=zd, out=torch.empty_like(zd), lse=torch.empty_like(w.lse_decode))
-    torch.cuda.synchronize()
-    cnt_p = np.rint(np.exp(lp.double().cpu().numpy())).astype(np.int64)
-    cnt_d = np.rint(np.exp(ld.double().cpu().numpy())).astype(np.int64)
-    D = lay.head_dim
-    prefill_flops = int(cnt_p.sum()) * 4 * D
-    per_slot = cnt_d[:, ::lay.group]                       # one head per slot: K/V read once per slot
-    decode_bytes = int(per_slot.sum()) * 2 * D * esz + 2 * w.q_decode.numel() * esz + 16 * len(w.td["entries"])
-    ent_p, rp = w.tp["entries"], w.tp["row_ptr"]
-    table_keys = int(ent_p[:, 2].sum())
-    prefill_bytes = table_keys * 2 * D * esz + 2 * w.q_prefill.numel() * esz + 16 * len(ent_p)
+    D, G = lay.head_dim, lay.group
+    q_pos = [lay.new_base[s] + np.arange(lay.n_prefill) for s in range(lay.n_seq)]
+    d_pos = [np.asarray([lay.new_base[s] + lay.n_prefill]) for s in range(lay.n_seq)]
+    cp = table_visible_counts(w.tp["row_ptr"], w.tp["entries"], lay.cls, lay.window, lay.n_seq, q_pos)
+    cd = table_visible_counts(w.td["row_ptr"], w.td["entries"], lay.cls, lay.window, lay.n_seq, d_pos)
+    pairs = int(sum(int(c.sum()) for c in cp)) * G
+    dkeys = int(sum(int(c.sum()) for c in cd))
+    ent_p = w.tp["entries"]
+    prefill_bytes = int(ent_p[:, 2].sum()) * 2 * D * esz + 2 * w.q_prefill.numel() * esz + 16 * len(ent_p)
+    decode_bytes = dkeys * 2 * D * esz + 2 * w.q_decode.numel() * esz + 16 * len(w.td["entries"])
     reloc = w.tp["reloc"]
     reloc_bytes = 2 * int(reloc[:, 2].sum()) * D * esz + 16 * len(reloc)
-    return dict(prefill_flops=prefill_flops, prefill_bytes=prefill_bytes, decode_bytes=decode_bytes,
-                relocate_bytes=reloc_bytes,
-                prefill_pairs=int(cnt_p.sum()), decode_keys=int(per_slot.sum()))
+    return dict(prefill_flops=pairs * 4 * D, prefill_bytes=prefill_bytes, decode_bytes=decode_bytes,
+                relocate_bytes=reloc_bytes, prefill_pairs=pairs, decode_keys=dkeys)
 
 
-def cpu_baseline(w, work_budget_s: float):
-    """The fp64 oracle on a bounded sample of the same workload, one core."""
-    import numpy as np
+# ----------------------------------------------------------------------------- CPU baseline (the oracle)
+
+_LAYOUTS = {}
+
+
+def _cpu_task(args):
+    """One (slot, seq) row of the workload through the fp64 oracle: relocation of
+    its segment keys, prefill of every chunk token, the decode token.  Inputs are
+    the row's seeded values drawn by the CPU generator (the same streams and
+    distributions as the GPU's, other draws); only the oracle's work is timed."""
+    import torch
     from threadpoolctl import threadpool_limits
     from oracle import attention as oatt
     from oracle import rope as orope
+    import synth
 
-    lay = w.lay
-    D, G = lay.head_dim, lay.group
-    rows_g = [s * lay.n_seq for s in range(lay.n_slot) if lay.cls[s] != 1]
-    rows_l = [s * lay.n_seq for s in range(lay.n_slot) if lay.cls[s] == 1]
-    order = [r for pair in zip(rows_g, rows_l) for r in pair] + rows_g[len(rows_l):] + rows_l[len(rows_g):]
-    flops = 0
-    pbytes = 0
-    rbytes = 0
-    dbytes = 0
-    t_used = 0.0
-    ent_p, rp = w.tp["entries"], w.tp["row_ptr"]
-    n_rows = 0
-    esz = 4 if lay.dtype == "f32" else 2
+    name, seed, r = args
+    if name not in _LAYOUTS:
+        _LAYOUTS[name] = synth.make_layout(name, seed=seed)
+    lay = _LAYOUTS[name]
+    slot, seq = divmod(r, lay.n_seq)
+    G, D = lay.group, lay.head_dim
+    u = synth.unit_values(lay, slot, seq, device="cpu")
+    K = torch.cat([u["seg_k"], u["new_k"]]).double().numpy()
+    V = torch.cat([u["seg_v"], u["new_v"]]).double().numpy()
+    q = synth.seq_queries(lay, seq, device="cpu")[:, slot * G:(slot + 1) * G].double().numpy()
+    ctx = lay.ctx_len(seq)
+    on = np.concatenate([np.arange(o, o + l) for o, l in zip(lay.seg_online[seq], lay.seg_len[seq])] + [[]])
+    off = np.concatenate([np.arange(o, o + l) for o, l in zip(lay.seg_offline[seq], lay.seg_len[seq])] + [[]])
     with threadpool_limits(1):
-        for r in order:
-            slot, seq = divmod(r, lay.n_seq)
-            K, V = w.unit_host(slot, seq)
-            heads = slice(slot * G, (slot + 1) * G)
-            qp = w.q_prefill[w.h_tok_ptr[seq]:w.h_tok_ptr[seq + 1], heads].double().cpu().numpy()
-            qd = w.q_decode[seq:seq + 1, heads].double().cpu().numpy()
-            ctx = lay.ctx_len(seq)
-            on = np.concatenate([np.arange(o, o + l) for o, l in zip(lay.seg_online[seq], lay.seg_len[seq])])
-            off = np.concatenate([np.arange(o, o + l) for o, l in zip(lay.seg_offline[seq], lay.seg_len[seq])])
-            t0 = time.perf_counter()
-            K[:ctx] = orope.relocate(K[:ctx], off, on, lay.theta)
-            q_pos = lay.new_base[seq] + np.arange(lay.n_prefill)
-            _, _, cnt = oatt.row_attention(lay, slot, seq, K, V, qp, q_pos)
-            _, _, cd = oatt.row_attention(lay, slot, seq, K, V, qd, [lay.new_base[seq] + lay.n_prefill])
-            t_used += time.perf_counter() - t0
-            n_rows += 1
-            flops += int(cnt.sum()) * G * 4 * D
-            pbytes += int(ent_p[rp[r]:rp[r + 1], 2].sum()) * 2 * D * esz
-            rbytes += 2 * ctx * D * esz
-            dbytes += int(cd.sum()) * 2 * D * esz
-            if t_used >= work_budget_s:
-                break
-    t_roof = max(flops / PEAK_BF16_FLOPS, pbytes / PEAK_HBM) + (rbytes + dbytes) / PEAK_HBM
-    return {"value": 100.0 * t_roof / t_used, "unit": "% of roofline", "cores": 1, "kind": "oracle",
-            "sample": f"{n_rows} of {lay.n_slot * lay.n_seq} (slot, seq) rows of the same workload, alternating "
-                      f"global/local: fp64 relocation of their segment keys, prefill of all {lay.n_prefill} "
-                      f"query tokens and the decode token; {t_used:.1f} s on 1 core; oracle prefill "
-                      f"{flops / t_used / 1e9:.2f} GFLOP/s, relocation {rbytes / t_used / 1e9:.3f} GB/s",
-            "seconds": round(t_used, 2)}
+        t0 = time.perf_counter()
+        K[:ctx] = orope.relocate(K[:ctx], off, on, lay.theta)
+        toks = np.unique(np.linspace(0, lay.n_prefill - 1, min(lay.n_prefill, MAX_CPU_QUERIES)).astype(np.int64))
+        qp = lay.new_base[seq] + toks
+        _, _, cnt = oatt.row_attention(lay, slot, seq, K, V, q[toks], qp)
+        _, _, cd = oatt.row_attention(lay, slot, seq, K, V, q[lay.n_prefill:lay.n_prefill + 1],
+                                      [lay.new_base[seq] + lay.n_prefill])
+        dt = time.perf_counter() - t0
+    return dict(row=r, seconds=dt, pid=os.getpid(), pairs=int(cnt.sum()) * G, ctx=ctx, dkeys=int(cd.sum()),
+                q_frac=len(toks) / lay.n_prefill)
 
+
+def cpu_baseline(pool, n_workers, lay, tp, budget_s):
+    """The fp64 oracle on a bounded sample of the same workload's rows, over
+    n_workers host processes (one BLAS thread each); rows alternate between
+    global-like and local slots and are handed out until the summed oracle time
+    reaches budget_s per worker.  The value is the work done over the busiest
+    worker's oracle time, against the same roofline formula as the GPU.  A
+    chunk of more than MAX_CPU_QUERIES tokens runs that many of its queries,
+    evenly spaced; its table bytes are charged in proportion."""
+    D, G = lay.head_dim, lay.group
+    esz = 4 if lay.dtype == "f32" else 2
+    rows_g = [s * lay.n_seq + q for s in range(lay.n_slot) if lay.cls[s] != LOCAL for q in range(lay.n_seq)]
+    rows_l = [s * lay.n_seq + q for s in range(lay.n_slot) if lay.cls[s] == LOCAL for q in range(lay.n_seq)]
+    order = [r for pair in zip(rows_g, rows_l) for r in pair] + rows_g[len(rows_l):] + rows_l[len(rows_g):]
+    per_worker, done = {}, []
+    it = pool.imap_unordered(_cpu_task, [(lay.name, lay.seed, r) for r in order])
+    for res in it:
+        done.append(res)
+        per_worker[res["pid"]] = per_worker.get(res["pid"], 0.0) + res["seconds"]
+        if sum(per_worker.values()) >= budget_s * n_workers:
+            break
+    pool.terminate()
+    span = max(per_worker.values())
+    ent, rp = tp["entries"], tp["row_ptr"]
+    flops = sum(d["pairs"] for d in done) * 4 * D
+    pbytes = sum(int(ent[rp[d["row"]]:rp[d["row"] + 1], 2].sum()) * d["q_frac"] for d in done) * 2 * D * esz
+    rbytes = sum(d["ctx"] for d in done) * 2 * D * esz
+    dbytes = sum(d["dkeys"] for d in done) * 2 * D * esz
+    t_roof = max(flops / PEAK_BF16_FLOPS, pbytes / PEAK_HBM) + (rbytes + dbytes) / PEAK_HBM
+    return {"value": 100.0 * t_roof / span, "unit": "% of roofline", "cores": len(per_worker), "kind": "oracle",
+            "sample": f"{len(done)} of {lay.n_slot * lay.n_seq} (slot, seq) rows of the same workload, alternating "
+                      f"global/local, over {len(per_worker)} processes (one BLAS thread each): fp64 relocation of "
+                      f"their segment keys, prefill of {min(lay.n_prefill, MAX_CPU_QUERIES)} of the {lay.n_prefill} query "
+                      f"tokens (evenly spaced) and the decode token; "
+                      f"row values drawn by the CPU generator from the same seeded streams; busiest process "
+                      f"{span:.1f} s of oracle time; oracle prefill {flops / span / 1e9:.2f} GFLOP/s, "
+                      f"relocation {rbytes / span / 1e9:.3f} GB/s",
+            "seconds": round(span, 2)}
+
+
+# ----------------------------------------------------------------------------- timing
 
 class HipEvent:
     """A HIP timing event recorded on a given stream.
@@ -191,81 +261,94 @@ class HipEvent:
             HipEvent._hip.hipEventDestroy(self.e)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="32k", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the hot path runs on a single MI355X and has no "
-              "multi-GPU mode (run with --gpus 1).", file=sys.stderr)
-        sys.exit(2)
+def _pct(xs, q):
+    return float(np.percentile(np.asarray(xs), q))
 
+
+def run_config(name, seed, steps, warmup, log):
+    """Build one workload on the GPU and time `steps` steps; returns (result dict, workload)."""
     import torch
     import synth
+    import head_aware_paged_page_amd.segpaged as sp
     from head_aware_paged_page_amd.workload import Workload
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    lay = synth.make_layout(args.config, seed=args.seed)
-    print(f"[bench] building workload {args.config} ...", file=sys.stderr, flush=True)
-    w = Workload(lay, device="cuda")
+    lay = synth.make_layout(name, seed=seed)
     t0 = time.perf_counter()
-    reps = 5
-    for _ in range(reps):
-        import head_aware_paged_page_amd.segpaged as sp
-        sp.build_tables(**w.arr_p, page_size=w.ps, free_list=w.free)
-    build_ms = (time.perf_counter() - t0) / reps * 1e3
-    work = algorithmic_work(w, torch)
-    print(f"[bench] work: {work}", file=sys.stderr, flush=True)
-
-    def step():
-        w.relocate()
-        w.prefill(k=w.k_reloc)
-        w.decode(k=w.k_reloc)
-
-    for _ in range(args.warmup):
-        step()
+    log(f"building workload {name} ...")
+    w = Workload(lay, device="cuda")
+    n_rep = 3 if 3 * w.pool_bytes() <= MAX_REPLICA_BYTES else 1
+    reps = w.replicas(n_rep)
     torch.cuda.synchronize()
+    log(f"built in {time.perf_counter() - t0:.1f} s; {n_rep} pool replica(s) of {w.pool_bytes() / 1e9:.2f} GB")
+
+    def host_ms(fn, reps_=5):
+        fn()
+        t = time.perf_counter()
+        for _ in range(reps_):
+            fn()
+        return (time.perf_counter() - t) / reps_ * 1e3
+
+    build_ms = host_ms(lambda: sp.build_tables(**w.arr_p, page_size=w.ps, free_list=w.free))
+    code = sp.SP_F32 if lay.dtype == "f32" else sp.SP_BF16
+    plan_p = host_ms(lambda: sp.workspace_bytes(sp.SP_WS_PREFILL, code, w.D, w.ps, w.G, w.n_seq, w.n_slot,
+                                                w.h_tok_ptr, w.tp["row_ptr"]))
+    plan_d = host_ms(lambda: sp.workspace_bytes(sp.SP_WS_DECODE, code, w.D, w.ps, w.G, w.n_seq, w.n_slot, None,
+                                                w.td["row_ptr"]))
+    work = algorithmic_work(w)
+    log(f"work: {work}")
+
+    def calls(i, ev=None):
+        a, b, c = reps[i % n_rep], reps[(i + 1) % n_rep], reps[(i + 2) % n_rep]
+        if ev:
+            ev[0].record(stream)
+        w.relocate(k_in=a[0], k_out=a[2])
+        if ev:
+            ev[1].record(stream)
+        w.prefill(k=b[2], v=b[1])
+        if ev:
+            ev[2].record(stream)
+        w.decode(k=c[2], v=c[1])
+        if ev:
+            ev[3].record(stream)
+
     stream = torch.cuda.current_stream()
-    ev = [[HipEvent() for _ in range(4)] for _ in range(args.steps)]
+    for i in range(max(warmup, n_rep)):
+        calls(i)
+    torch.cuda.synchronize()
+    ev = [[HipEvent() for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for i in range(args.steps):
-        e = ev[i]
-        e[0].record(stream)
-        w.relocate()
-        e[1].record(stream)
-        w.prefill(k=w.k_reloc)
-        e[2].record(stream)
-        w.decode(k=w.k_reloc)
-        e[3].record(stream)
+    for i in range(steps):
+        calls(i, ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    ms = lambda a, b: sum(HipEvent.elapsed_ms(ev[i][a], ev[i][b]) for i in range(args.steps)) / args.steps
-    t_reloc, t_pref, t_dec = (max(ms(a, a + 1), 1e-6) for a in range(3))   # an empty call may time as 0
-    ms_per_step = wall / args.steps * 1e3
+    per = [[max(HipEvent.elapsed_ms(ev[i][a], ev[i][a + 1]), 1e-6) for i in range(steps)] for a in range(3)]
+    t_reloc, t_pref, t_dec = (sum(x) / steps for x in per)
+    ms_per_step = wall / steps * 1e3
 
     peak_flops = PEAK_FP32_FLOPS if lay.dtype == "f32" else PEAK_BF16_FLOPS
     t_pref_roof = max(work["prefill_flops"] / peak_flops, work["prefill_bytes"] / PEAK_HBM)
     pref_bound = "mfma" if work["prefill_flops"] / peak_flops >= work["prefill_bytes"] / PEAK_HBM else "hbm"
-    calls = {
-        "rope_relocate": {"ms": round(t_reloc, 4), "GB/s": round(work["relocate_bytes"] / t_reloc / 1e6, 1),
+
+    def spread(x):
+        return {"p10_ms": round(_pct(x, 10), 4), "p90_ms": round(_pct(x, 90), 4)}
+
+    calls_out = {
+        "rope_relocate": {"ms": round(t_reloc, 4), **spread(per[0]),
+                          "GB/s": round(work["relocate_bytes"] / t_reloc / 1e6, 1),
                           "frac_hbm": round(work["relocate_bytes"] / t_reloc / 1e-3 / PEAK_HBM, 4),
                           "bytes": work["relocate_bytes"]},
-        "segpaged_prefill": {"ms": round(t_pref, 4), "TFLOP/s": round(work["prefill_flops"] / t_pref / 1e9, 2),
+        "segpaged_prefill": {"ms": round(t_pref, 4), **spread(per[1]),
+                             "TFLOP/s": round(work["prefill_flops"] / t_pref / 1e9, 2),
                              "frac_mfma": round(work["prefill_flops"] / t_pref / 1e-3 / peak_flops, 4),
                              "GB/s": round(work["prefill_bytes"] / t_pref / 1e6, 1),
                              "frac_hbm": round(work["prefill_bytes"] / t_pref / 1e-3 / PEAK_HBM, 4),
                              "flops": work["prefill_flops"], "bytes": work["prefill_bytes"],
-                             "bound": pref_bound},
-        "segpaged_decode": {"ms": round(t_dec, 4), "GB/s": round(work["decode_bytes"] / t_dec / 1e6, 1),
+                             "bound": pref_bound, "plan_host_ms": round(plan_p, 3)},
+        "segpaged_decode": {"ms": round(t_dec, 4), **spread(per[2]),
+                            "GB/s": round(work["decode_bytes"] / t_dec / 1e6, 1),
                             "frac_hbm": round(work["decode_bytes"] / t_dec / 1e-3 / PEAK_HBM, 4),
-                            "bytes": work["decode_bytes"]},
+                            "bytes": work["decode_bytes"], "plan_host_ms": round(plan_d, 3)},
         "segpaged_build_tables": {"host_ms": round(build_ms, 3), "outside_timed_step": True},
     }
     t_roof = t_pref_roof + (work["relocate_bytes"] + work["decode_bytes"]) / PEAK_HBM
@@ -284,48 +367,90 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                 "frac": round(ach * 1e9 / PEAK_HBM, 4)}
     roof["kernel"] = dom
-    roof["traffic"] = committed_traffic(dom, args.config)
+    roof["traffic"] = committed_traffic(dom, name)
 
-    res = {
-        "metric": METRIC, "value": round(value, 3), "unit": "% of roofline", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32" if lay.dtype == "f32" else "bf16", "data": "synthetic",
-        "config": {"workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}", "seed": args.seed,
-                   "slots": lay.n_slot, "sequences": lay.n_seq, "prefill_tokens": int(w.h_tok_ptr[-1]),
-                   "decode_tokens": lay.n_seq},
-        "roofline": roof,
-        "calls": calls,
-    }
     # A row beyond the step, measured on its own: the per-head visible-page
     # pack (the pages the decode tables list, gathered in table order), not
-    # part of the step or its value.  Bytes: every listed K and V page read
-    # once and written once.
-    import head_aware_paged_page_amd.segpaged as sp
+    # part of the step or its value, cycled over the replicas like the step.
     n_ent = int(w.td["row_ptr"][-1])
     k_pk = torch.empty((n_ent,) + tuple(w.k_pool.shape[1:]), dtype=w.k_pool.dtype, device="cuda")
     v_pk = torch.empty((n_ent,) + tuple(w.v_pool.shape[1:]), dtype=w.v_pool.dtype, device="cuda")
-    for _ in range(3):
-        sp.pack_pages(w.k_pool, w.v_pool, w.d_entries, n_ent, k_pk, v_pk)
+    pack_bytes = 2 * (k_pk.numel() + v_pk.numel()) * k_pk.element_size()
+    n_pack = max(n_rep, 1)
+    for i in range(3):
+        sp.pack_pages(reps[i % n_pack][0], reps[i % n_pack][1], w.d_entries, n_ent, k_pk, v_pk)
     torch.cuda.synchronize()
     pe = [HipEvent() for _ in range(2)]
-    reps = 20
+    n_calls = 21
     pe[0].record(stream)
-    for _ in range(reps):
-        sp.pack_pages(w.k_pool, w.v_pool, w.d_entries, n_ent, k_pk, v_pk)
+    for i in range(n_calls):
+        sp.pack_pages(reps[i % n_pack][0], reps[i % n_pack][1], w.d_entries, n_ent, k_pk, v_pk)
     pe[1].record(stream)
     torch.cuda.synchronize()
-    t_pack = HipEvent.elapsed_ms(pe[0], pe[1]) / reps
-    pack_bytes = 2 * (k_pk.numel() + v_pk.numel()) * k_pk.element_size()
-    res["beyond_step"] = {"pack_pages": {"ms": round(t_pack, 4), "GB/s": round(pack_bytes / t_pack / 1e6, 1),
-                                         "frac_hbm": round(pack_bytes / t_pack / 1e-3 / PEAK_HBM, 4),
-                                         "bytes": pack_bytes, "pages": n_ent}}
-    if not args.no_cpu_baseline and lay.n_prefill > 4096:
-        # one row of the fp64 oracle over every query of such a chunk runs for minutes
-        res["cpu_baseline"] = None
-        res["cpu_baseline_note"] = "skipped: the oracle cannot finish one row of this chunk in a bounded sample"
-    elif not args.no_cpu_baseline:
-        print("[bench] timing the oracle on a CPU sample ...", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    t_pack = HipEvent.elapsed_ms(pe[0], pe[1]) / n_calls
+    del k_pk, v_pk
+
+    res = {
+        "value": round(value, 3), "ms_per_step": round(ms_per_step, 4),
+        "config": {"workload": f"{name}: {WORKLOAD_TEXT[name]}", "seed": seed, "slots": lay.n_slot,
+                   "sequences": lay.n_seq, "prefill_tokens": int(w.h_tok_ptr[-1]), "decode_tokens": lay.n_seq,
+                   "pool_replicas": n_rep},
+        "roofline": roof, "calls": calls_out,
+        "beyond_step": {"pack_pages": {"ms": round(t_pack, 4), "GB/s": round(pack_bytes / t_pack / 1e6, 1),
+                                       "frac_hbm": round(pack_bytes / t_pack / 1e-3 / PEAK_HBM, 4),
+                                       "bytes": pack_bytes, "pages": n_ent}},
+        "dtype": "f32" if lay.dtype == "f32" else "bf16",
+    }
+    del reps
+    return res, w
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="32k", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-128k", action="store_true", help="skip the 128K block of the default run")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle seconds per CPU process")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the hot path runs on a single MI355X and has no "
+              "multi-GPU mode (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # The oracle's worker processes are forked before anything touches the GPU,
+    # so none of them holds the device.
+    pool = n_workers = None
+    if not args.no_cpu_baseline:
+        n_workers = max(1, min(16, os.cpu_count() or 1))
+        pool = mp.get_context("fork").Pool(n_workers)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    res0, w = run_config(args.config, args.seed, args.steps, args.warmup, log)
+    lay, tp = w.lay, w.tp
+    del w
+    res = {"metric": METRIC, "value": res0["value"], "unit": "% of roofline", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": res0["ms_per_step"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": res0["dtype"], "data": "synthetic",
+           "config": res0["config"], "roofline": res0["roofline"], "calls": res0["calls"],
+           "beyond_step": res0["beyond_step"]}
+    if args.config == "32k" and not args.no_128k:
+        torch.cuda.empty_cache()
+        r128, w128 = run_config("128k", args.seed, max(3, args.steps // 2), max(2, args.warmup // 2), log)
+        del w128
+        torch.cuda.empty_cache()
+        res["config_128k"] = {k: r128[k] for k in ("value", "ms_per_step", "config", "roofline", "calls",
+                                                    "beyond_step")}
+    if pool is not None:
+        log(f"timing the oracle on a CPU sample ({n_workers} processes) ...")
+        res["cpu_baseline"] = cpu_baseline(pool, n_workers, lay, tp, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

@@ -41,10 +41,13 @@ KERNELS = [
     ("decode_f32_kernel", "segpaged_decode", "decode_f32_kernel"),
     ("page_copy_kernel", "segpaged_pack_pages", "page_copy_kernel"),
 ]
+# The sources a call's kernel timings and traffic depend on: its kernels and the
+# host runtime, whose planner sets split counts and launch shapes.
 KERNEL_SOURCES = {
-    "rope_relocate": ["relocate.hip"],
-    "segpaged_prefill": ["prefill.hip", "device_common.hpp"],
-    "segpaged_decode": ["decode.hip", "device_common.hpp"],
+    "rope_relocate": ["relocate.hip", "runtime.cpp", "internal.hpp"],
+    "segpaged_prefill": ["prefill.hip", "device_common.hpp", "runtime.cpp", "internal.hpp"],
+    "segpaged_decode": ["decode.hip", "device_common.hpp", "runtime.cpp", "internal.hpp"],
+    "segpaged_pack_pages": ["pack.hip", "runtime.cpp", "internal.hpp"],
 }
 
 
@@ -102,9 +105,9 @@ def summarize(a) -> None:
     write = read_counters(a.write)
     stats = list(csv.DictReader(open(os.path.join(a.trace, "run_kernel_stats.csv"))))
     bench_cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
-                 f"python3 bench.py --config {a.workload} --steps 10 --warmup 2 --no-cpu-baseline")
+                 f"python3 bench.py --config {a.workload} --steps 10 --warmup 2 --no-cpu-baseline --no-128k")
     pmc_cmd = ("rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- "
-               f"python3 bench.py --config {a.workload} --steps 2 --warmup 1 --no-cpu-baseline")
+               f"python3 bench.py --config {a.workload} --steps 2 --warmup 1 --no-cpu-baseline --no-128k")
     copy_cmd = ("rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- "
                 f"python3 -m head_aware_paged_page_amd.profiling copy --mib {a.copy_mib}")
     lines = [f"# Kernel time, workload {a.workload} (rocprofv3 kernel trace, --stats)", "",
@@ -144,7 +147,7 @@ def summarize(a) -> None:
     open(txt, "w").write("\n".join(lines) + "\n")
     # one traffic record per call's dominant kernel, keyed by the call's source hash
     main_kernel = {"rope_relocate": "relocate_kernel", "segpaged_prefill": "prefill_bf16_kernel",
-                   "segpaged_decode": "decode_bf16_kernel"}
+                   "segpaged_decode": "decode_bf16_kernel", "segpaged_pack_pages": "page_copy_kernel"}
     for call, short in main_kernel.items():
         if short not in traffic:
             continue

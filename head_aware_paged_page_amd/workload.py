@@ -103,9 +103,10 @@ class Workload:
         sp.rope_relocate(k_in, k_out, self.ps, self.d_reloc, self.lay.theta, stream=stream)
         return k_out
 
-    def prefill(self, k=None, q=None, out=None, lse=None, stream=None):
+    def prefill(self, k=None, q=None, out=None, lse=None, stream=None, v=None):
         k = self.k_pool if k is None else k
-        sp.prefill(self.q_prefill if q is None else q, k, self.v_pool, page_size=self.ps, group=self.G,
+        v = self.v_pool if v is None else v
+        sp.prefill(self.q_prefill if q is None else q, k, v, page_size=self.ps, group=self.G,
                    n_seq=self.n_seq, n_slot=self.n_slot, h_tok_ptr=self.h_tok_ptr, h_row_ptr=self.tp["row_ptr"],
                    d_tok_ptr=self.d_tok_ptr, d_q_pos0=self.d_q_pos0, d_cls=self.d_cls, d_window=self.d_window,
                    d_row_ptr=self.p_row_ptr, d_entries=self.p_entries, scale=self.scale,
@@ -113,14 +114,28 @@ class Workload:
                    workspace=self.workspace, stream=stream)
         return self.out_prefill if out is None else out, self.lse_prefill if lse is None else lse
 
-    def decode(self, k=None, q=None, out=None, lse=None, stream=None):
+    def decode(self, k=None, q=None, out=None, lse=None, stream=None, v=None):
         k = self.k_pool if k is None else k
-        sp.decode(self.q_decode if q is None else q, k, self.v_pool, page_size=self.ps, group=self.G,
+        v = self.v_pool if v is None else v
+        sp.decode(self.q_decode if q is None else q, k, v, page_size=self.ps, group=self.G,
                   n_seq=self.n_seq, n_slot=self.n_slot, h_row_ptr=self.td["row_ptr"], d_q_pos=self.d_q_dec,
                   d_cls=self.d_cls, d_window=self.d_window, d_row_ptr=self.d_row_ptr, d_entries=self.d_entries,
                   scale=self.scale, out=self.out_decode if out is None else out,
                   lse=self.lse_decode if lse is None else lse, workspace=self.workspace, stream=stream)
         return self.out_decode if out is None else out, self.lse_decode if lse is None else lse
+
+    def replicas(self, n: int):
+        """n copies of the pools, [(k_pool, v_pool, k_reloc)], the first being the
+        workload's own; the copies share every table (same physical ids)."""
+        reps = [(self.k_pool, self.v_pool, self.k_reloc)]
+        for _ in range(n - 1):
+            reps.append((self.k_pool.clone(), self.v_pool.clone(), self.k_reloc.clone()))
+        return reps
+
+    def pool_bytes(self) -> int:
+        """Bytes of one replica: the K and V pools and the relocated K pool."""
+        b = self.k_pool.numel() * self.k_pool.element_size() * 2
+        return b + (self.k_reloc.numel() * self.k_reloc.element_size() if self.k_reloc is not None else 0)
 
     # ------------------------------------------------------------------ host views for checking
     def unit_host(self, slot: int, seq: int):

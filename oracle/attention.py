@@ -41,7 +41,7 @@ def row_attention(lay, slot: int, seq: int, K_all, V_all, q, q_pos):
     """Attention of one (slot, seq) row.
 
     K_all / V_all: [n_tokens, D] keys/values of the chain's tokens in position
-    order (segment tokens, then new tokens), as returned by ``row_kv``.
+    order (segment tokens, then new tokens).
     q: [n_q, G, D] queries of this slot's group, q_pos: [n_q] their positions.
     Returns (O [n_q, G, D], LSE [n_q, G], counts [n_q]).
     """
@@ -60,7 +60,3 @@ def row_attention(lay, slot: int, seq: int, K_all, V_all, q, q_pos):
         cnt[i] = len(idx)
     return O, L, cnt
 
-
-def row_kv(seg, new):
-    """Concatenate a chain's segment tokens and new tokens (both in position order)."""
-    return np.concatenate([np.asarray(seg, np.float64), np.asarray(new, np.float64)], axis=0)

@@ -326,10 +326,36 @@ def test_class_reductions_on_gpu():
         assert torch.equal(outd[:, slot * 4:(slot + 1) * 4], outd[:, 0:4])
 
 
-# ---------------------------------------------------------------- full-size configs (sampled rows / queries)
+# ---------------------------------------------------------------- full-size configs
 
-@pytest.mark.parametrize("name", ["32k", "16k", "128k", "batch", "recovery32k"])
-def test_full_config(name):
+@pytest.mark.parametrize("name", ["32k", "16k"])
+def test_full_config_every_row(name):
+    """Every (slot, seq) row of the 32K and 16K workloads, in the launch
+    configuration bench.py times: relocation of every segment key, prefill of
+    every query token and the decode token, against the oracle.  Segment 0 of
+    both workloads keeps its position (offline base = online base = 0), so its
+    relocated keys must equal the cached ones bit for bit in bf16."""
+    w = cached(name)
+    lay = w.lay
+    w.relocate()
+    check_relocate(w)
+    torch.cuda.synchronize()
+    n0 = int(lay.seg_len[0][0])
+    assert lay.seg_online[0][0] == lay.seg_offline[0][0]
+    for slot in range(lay.n_slot):
+        a = w.gather_keys(w.k_reloc, slot, 0)[:n0]
+        b = w.gather_keys(w.k_pool, slot, 0)[:n0]
+        assert np.array_equal(a, b), f"slot {slot}: a zero shift changed bf16 keys"
+    w.prefill()
+    check_prefill(w)
+    w.decode()
+    check_decode(w)
+
+
+@pytest.mark.parametrize("name", ["128k", "batch"])
+def test_full_config_sampled(name):
+    """The 128K and batch workloads at full size: two rows per class (and, at
+    128K, sampled query tokens of the 2048-token chunk) against the oracle."""
     w = cached(name)
     lay = w.lay
     rows = _rows_by_class(lay, 2)
@@ -338,11 +364,201 @@ def test_full_config(name):
         rng = np.random.default_rng(1)
         q_sample = np.unique(np.concatenate([[0, 1, lay.n_prefill - 1], rng.integers(0, lay.n_prefill, 12)]))
     w.relocate()
-    check_relocate(w, rows=rows[:3])
+    check_relocate(w, rows=rows)
     w.prefill()
     check_prefill(w, rows=rows, q_sample=q_sample)
     w.decode()
     check_decode(w, rows=rows)
+
+
+@pytest.mark.parametrize("part", [0, 1])
+def test_recovery32k_every_query_tile(part):
+    """Head-level recovery prefill (30000-token causal chunk over the 10 global
+    slots): for every row, the last token of every 64-token query tile (where
+    the diagonal bound cuts the tile's last key tile) plus one random token in
+    every fourth tile, against the oracle.  The rows are split over two tests."""
+    w = cached("recovery32k")
+    lay = w.lay
+    if part == 0:
+        w.prefill()
+        w.decode()
+    tpt = 256 // lay.group
+    last = np.arange(tpt - 1, lay.n_prefill, tpt)
+    if last[-1] != lay.n_prefill - 1:
+        last = np.append(last, lay.n_prefill - 1)
+    rng = np.random.default_rng(7 + part)
+    starts = np.arange(0, lay.n_prefill, 4 * tpt)
+    extra = np.minimum(starts + rng.integers(0, tpt, len(starts)), lay.n_prefill - 1)
+    q_sample = np.unique(np.concatenate([[0], last, extra]))
+    rows = range(part * 5, part * 5 + 5)
+    check_prefill(w, rows=rows, q_sample=q_sample)
+    check_decode(w, rows=rows)
+
+
+def _table_counts(w, which, q_pos_of_seq):
+    """Visible keys of each (query, row) counted from the host tables alone."""
+    import bench
+    tab = w.tp if which == "prefill" else w.td
+    return bench.table_visible_counts(tab["row_ptr"], tab["entries"], w.lay.cls, w.lay.window, w.lay.n_seq,
+                                      q_pos_of_seq)
+
+
+@pytest.mark.parametrize("name", ["32k", "16k", "128k", "batch"])
+def test_full_size_visible_counts(name):
+    """Q = 0 at full size: exp(LSE) of every (query, head) is the head's visible
+    token count, exactly.  It must equal the oracle's visible set size and the
+    count the benchmark derives from the host tables (its FLOP and byte
+    numerators).  Every row and query at 32K and 16K; at 128K and batch every
+    row, on sampled queries."""
+    w = cached(name)
+    lay = w.lay
+    zq = torch.zeros_like(w.q_prefill)
+    zd = torch.zeros_like(w.q_decode)
+    _, lse_p = w.prefill(q=zq, out=torch.empty_like(zq), lse=torch.empty_like(w.lse_prefill))
+    _, lse_d = w.decode(q=zd, out=torch.empty_like(zd), lse=torch.empty_like(w.lse_decode))
+    torch.cuda.synchronize()
+    cp = np.rint(np.exp(lse_p.double().cpu().numpy())).astype(np.int64)
+    cd = np.rint(np.exp(lse_d.double().cpu().numpy())).astype(np.int64)
+    toks = np.arange(lay.n_prefill)
+    if name in ("128k", "batch"):
+        rng = np.random.default_rng(5)
+        toks = np.unique(np.concatenate([[0, lay.n_prefill - 1], rng.integers(0, lay.n_prefill, 6)]))
+    q_pos = [lay.new_base[s] + toks for s in range(lay.n_seq)]
+    d_pos = [np.asarray([lay.new_base[s] + lay.n_prefill]) for s in range(lay.n_seq)]
+    tab_p = _table_counts(w, "prefill", q_pos)
+    tab_d = _table_counts(w, "decode", d_pos)
+    G = lay.group
+    for slot in range(lay.n_slot):
+        for seq in range(lay.n_seq):
+            r = slot * lay.n_seq + seq
+            t0 = int(w.h_tok_ptr[seq])
+            want = otab.visible_counts(lay, slot, seq, q_pos[seq])
+            got = cp[t0 + toks, slot * G:(slot + 1) * G]
+            assert np.array_equal(got, np.repeat(want[:, None], G, axis=1)), f"prefill row {r}"
+            assert np.array_equal(tab_p[r], want), f"host-table count, prefill row {r}"
+            wd = otab.visible_counts(lay, slot, seq, d_pos[seq])
+            assert np.all(cd[seq, slot * G:(slot + 1) * G] == wd[0]), f"decode row {r}"
+            assert np.array_equal(tab_d[r], wd), f"host-table count, decode row {r}"
+
+
+def _row_call(w, slots, which):
+    """One prefill or decode call over the given slots of a workload (a slot may
+    repeat), straight through the C ABI, reusing the workload's pools and tables.
+    Returns (out, lse) laid out [tokens, len(slots) * G, D] / [tokens, len(slots) * G]."""
+    import head_aware_paged_page_amd.segpaged as sp
+    lay, G = w.lay, w.lay.group
+    assert lay.n_seq == 1
+    tab = w.tp if which == "prefill" else w.td
+    rp, ent = tab["row_ptr"], tab["entries"]
+    ents = [ent[rp[s]:rp[s + 1]] for s in slots]
+    row_ptr = np.concatenate([[0], np.cumsum([len(e) for e in ents])]).astype(np.int32)
+    entries = np.ascontiguousarray(np.concatenate(ents), dtype=np.int32)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    heads = torch.as_tensor(np.concatenate([np.arange(s * G, (s + 1) * G) for s in slots]), device="cuda")
+    q_src = w.q_prefill if which == "prefill" else w.q_decode
+    q = q_src.index_select(1, heads).contiguous()
+    out, lse = torch.empty_like(q), torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    cls, win = dev(lay.cls[slots].astype(np.int32)), dev(lay.window[slots].astype(np.int32))
+    kind = sp.SP_WS_PREFILL if which == "prefill" else sp.SP_WS_DECODE
+    code = sp.SP_BF16 if lay.dtype == "bf16" else sp.SP_F32
+    nb = sp.workspace_bytes(kind, code, w.D, w.ps, G, 1, len(slots), w.h_tok_ptr if which == "prefill" else None,
+                            row_ptr)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    common = dict(page_size=w.ps, group=G, n_seq=1, n_slot=len(slots), h_row_ptr=row_ptr, d_cls=cls, d_window=win,
+                  d_row_ptr=dev(row_ptr), d_entries=dev(entries), scale=w.scale, out=out, lse=lse, workspace=ws)
+    if which == "prefill":
+        sp.prefill(q, w.k_pool, w.v_pool, h_tok_ptr=w.h_tok_ptr, d_tok_ptr=w.d_tok_ptr, d_q_pos0=w.d_q_pos0,
+                   **common)
+    else:
+        sp.decode(q, w.k_pool, w.v_pool, d_q_pos=w.d_q_dec, **common)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("which", ["prefill", "decode"])
+def test_split_count_does_not_change_results(which):
+    """The same 32K global row computed with different kv-split counts: alone in a
+    call (many splits), inside the 64-row call (the bench's split), and repeated
+    256 times in one call (no prefill split: the items then outnumber the CUs).
+
+    The log-sum-exp (fp32 partials, merged in fp32) must agree to 2e-5.  The
+    outputs may differ by the roundings that depend on the split: the softmax
+    weights enter the P.V product in bf16 relative to each split's own running
+    max (at most 2^-9 relative per weight, so 2^-9 * sum_j p_j |v_j| per side),
+    the prefill's split partials are stored normalised in fp16 (2^-11 of the
+    same sum per side), and the bf16 output rounding (one unit in the last
+    place).  sum_j p_j |v_j| is taken from the oracle (attention over |v|)."""
+    w = cached("32k")
+    lay, G = w.lay, w.lay.group
+    slot = int(np.nonzero(lay.cls == GLOBAL)[0][0])
+    o_all, l_all = (w.prefill() if which == "prefill" else w.decode())
+    torch.cuda.synchronize()
+    ref_o = o_all[:, slot * G:(slot + 1) * G].clone()
+    ref_l = l_all[:, slot * G:(slot + 1) * G].clone()
+    o1, l1 = _row_call(w, [slot], which)
+    on, ln = _row_call(w, [slot] * 256, which)
+    K, V = w.unit_host(slot, 0)
+    q_src = w.q_prefill if which == "prefill" else w.q_decode
+    q_pos = lay.new_base[0] + (np.arange(lay.n_prefill) if which == "prefill" else np.asarray([lay.n_prefill]))
+    wabs, _, _ = oatt.row_attention(lay, slot, 0, K, np.abs(V), _host(q_src[:, slot * G:(slot + 1) * G]), q_pos)
+    per_side = 2.0 ** -9 + (2.0 ** -11 if which == "prefill" else 0.0)
+    slack = torch.as_tensor(2 * per_side * wabs, dtype=torch.float32, device="cuda")
+    worst_l = worst_o = worst_frac = 0.0
+    for k in range(257):
+        o, l = (o1, l1) if k == 0 else (on[:, (k - 1) * G:k * G], ln[:, (k - 1) * G:k * G])
+        d = float((l - ref_l).abs().max())
+        worst_l = max(worst_l, d)
+        assert d <= 2e-5, f"call {k}: LSE differs by {d}"
+        a, b = o.float(), ref_o.float()
+        diff = (a - b).abs()
+        bound = torch.maximum(a.abs(), b.abs()) * 2.0 ** -7 + slack
+        worst_o = max(worst_o, float(diff.max()))
+        worst_frac = max(worst_frac, float((diff / bound).max()))
+        assert bool(torch.all(diff <= bound)), f"call {k}: outputs differ by {float(diff.max())}"
+    print(f"[split] {which}: max LSE difference {worst_l:.2e}, max output difference {worst_o:.2e} "
+          f"({worst_frac:.2f} of its bound)")
+
+
+def test_out_of_pool_pages_are_empty():
+    """A table entry whose physical page lies outside the pool (>= n_phys, or
+    negative) is read as a page with no tokens: prefill and decode then equal
+    the oracle over the visible set less that page's tokens."""
+    import head_aware_paged_page_amd.segpaged as sp
+    lay = _small(0)
+    w = _wl(lay)
+    slot, G = 0, lay.group                       # a global row of 57 pages
+    assert lay.cls[slot] == GLOBAL
+    rp_p, rp_d = w.tp["row_ptr"], w.td["row_ptr"]
+    drop_p = {int(rp_p[slot]) + 5: w.n_phys + 5, int(rp_p[slot]) + 30: -1}
+    drop_d = {int(rp_d[slot]) + 11: w.n_phys, int(rp_d[slot]) + 40: -7}
+    ent_p, ent_d = w.tp["entries"].copy(), w.td["entries"].copy()
+    gone_p = [tuple(ent_p[i, 1:3]) for i in drop_p]
+    gone_d = [tuple(ent_d[i, 1:3]) for i in drop_d]
+    for i, v in drop_p.items():
+        ent_p[i, 0] = v
+    for i, v in drop_d.items():
+        ent_d[i, 0] = v
+    w.p_entries = torch.from_numpy(ent_p).cuda()
+    w.d_entries = torch.from_numpy(ent_d).cuda()
+    out, lse = w.prefill()
+    outd, lsed = w.decode()
+    torch.cuda.synchronize()
+    K, V = w.unit_host(slot, 0)
+    tpos, _tp, tsp, tnew = otab.tokens(lay, 0)
+
+    def expect(q, p, gone):
+        m = otab.visible(GLOBAL, 0, [], tpos, tsp, tnew, int(p))
+        for s0, n in gone:
+            m &= ~((tpos >= s0) & (tpos < s0 + n))
+        return oatt.attend(q, K[m], V[m], w.scale)
+
+    for t in range(lay.n_prefill):
+        o, l = expect(_host(w.q_prefill[t, :G]), lay.new_base[0] + t, gone_p)
+        assert np.max(np.abs(_host(out[t, :G]) - o)) <= TOL["bf16"]
+        assert np.max(np.abs(lse[t, :G].double().cpu().numpy() - l)) <= TOL["bf16"]
+    o, l = expect(_host(w.q_decode[0, :G]), lay.new_base[0] + lay.n_prefill, gone_d)
+    assert np.max(np.abs(_host(outd[0, :G]) - o)) <= TOL["bf16"]
+    assert np.max(np.abs(lsed[0, :G].double().cpu().numpy() - l)) <= TOL["bf16"]
 
 
 def test_end_to_end_32k():

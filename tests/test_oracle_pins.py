@@ -181,6 +181,33 @@ def test_gather_oracle_matches_dense_masked_attention(ps):
             assert np.array_equal(cnt, M.sum(axis=1))
 
 
+@pytest.mark.parametrize("ps", [1, 3, 4, 16])
+def test_visible_counts_match_brute_force_mask(ps):
+    """oracle.tables.visible_counts (the expected value of the GPU's count checks)
+    equals the row sums of the brute-force mask, for every class, query position
+    and page size, including retrieval lists that are empty or list every page."""
+    classes = [(GLOBAL, 0), (LOCAL, 1), (LOCAL, 4), (LOCAL, 1000), (RETRIEVAL, 0), (RETRIEVAL, 0), (DENSE, 0)]
+    for seed in range(4):
+        lay = _rand_layout(ps, 4, 11, 7, classes, 100 + seed)
+        nsp = sum(-(-int(l) // ps) for l in lay.seg_len[0])
+        lay.ret_pages[(5, 0)] = np.arange(nsp, dtype=np.int32) if seed % 2 else np.zeros(0, np.int32)
+        q_pos = list(range(int(lay.new_base[0]), int(lay.new_base[0]) + lay.n_new))
+        for slot in range(lay.n_slot):
+            want = _dense_mask(lay, slot, q_pos).sum(axis=1)
+            assert np.array_equal(otab.visible_counts(lay, slot, 0, q_pos), want), (seed, slot)
+
+
+def test_visible_counts_match_hand_fixture(golden_dir):
+    """The visible sets worked out by hand in tests/golden/tiny_tables_by_hand.json
+    fix the counts: global at p = 9 sees 10 tokens, local(3) at p = 10 and 13
+    sees 3, retrieval at p = 11 sees 5, dense at p = 13 sees 14."""
+    g, lay = _tiny_hand(golden_dir)
+    for v in g["expected_visible"]:
+        got = otab.visible_counts(lay, v["slot"], 0, [v["p"]])
+        assert got.tolist() == [len(v["positions"])]
+    assert [len(v["positions"]) for v in g["expected_visible"]] == [10, 3, 5, 14, 3]
+
+
 def test_window_one_returns_own_value_and_zero_query_averages():
     lay = custom_layout(seg_lens=[[9, 4]], offline=[[0, 0]], n_prefill=3, n_decode=1,
                         classes=[(LOCAL, 1), (GLOBAL, 0)], page_size=4, head_dim=8, group=1)
@@ -301,3 +328,4 @@ def test_pack_unpack_round_trip_restores_exactly_the_listed_pages():
     listed[phys] = True
     assert np.array_equal(k2[listed], k[listed]) and np.array_equal(v2[listed], v[listed])
     assert not k2[~listed].any() and not v2[~listed].any()
+

@@ -194,3 +194,32 @@ def test_workspace_query_and_validation():
     with pytest.raises(sp.SegPagedError) as e:
         sp.workspace_bytes(sp.SP_WS_DECODE, sp.SP_BF16, 128, 16, 4, 1, 2, None, np.array([0, 3, 3], np.int32))
     assert e.value.status == sp.SP_EINVAL
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_bench_counts_from_host_tables_match_oracle(seed):
+    """bench.py takes its FLOP and byte numerators from the host tables: the
+    visible keys of each query counted from a row's entries and its class must
+    equal the oracle's visible set sizes, for the prefill and the decode call."""
+    import bench
+    r = np.random.default_rng(50 + seed)
+    ps = int(r.choice([1, 3, 4, 16]))
+    n_seq = int(r.integers(1, 4))
+    lens = [list(r.integers(1, 60, size=int(r.integers(0, 4)))) for _ in range(n_seq)]
+    off = [list(r.integers(-300, 300, size=len(l))) for l in lens]
+    classes = [(GLOBAL, 0), (LOCAL, int(r.integers(1, 70))), (RETRIEVAL, 0), (DENSE, 0), (LOCAL, 1)]
+    ret = {}
+    for q in range(n_seq):
+        nsp = sum(-(-l // ps) for l in lens[q])
+        ret[(2, q)] = np.sort(r.choice(nsp, size=int(r.integers(0, nsp + 1)), replace=False))
+    lay = custom_layout(seg_lens=lens, offline=off, n_prefill=int(r.integers(1, 30)), n_decode=1, classes=classes,
+                        page_size=ps, ret_lists=ret)
+    n = sp.build_tables(**lay.abi_arrays("prefill"), page_size=ps, free_list=None, counts_only=True)["counts"][0]
+    free = np.arange(int(n), dtype=np.int32)
+    for call, toks in (("prefill", np.arange(lay.n_prefill)), ("decode", np.asarray([lay.n_prefill]))):
+        t = _lib_tables(lay, call, free)
+        q_pos = [lay.new_base[q] + toks for q in range(n_seq)]
+        got = bench.table_visible_counts(t["row_ptr"], t["entries"], lay.cls, lay.window, n_seq, q_pos)
+        for row in range(lay.n_slot * n_seq):
+            slot, q = divmod(row, n_seq)
+            assert np.array_equal(got[row], otab.visible_counts(lay, slot, q, q_pos[q])), (call, row)
