@@ -19,6 +19,7 @@ SP_OK, SP_EINVAL, SP_ENOMEM, SP_EHIP, SP_EUNSUPPORTED, SP_EWORKSPACE = 0, -1, -2
 SP_GLOBAL, SP_LOCAL, SP_RETRIEVAL, SP_DENSE = 0, 1, 2, 3
 SP_F32, SP_BF16 = 0, 1
 SP_WS_PREFILL, SP_WS_DECODE = 0, 1
+SP_STATIC_SCRATCH_BYTES = 16 << 20
 
 ENTRY_FIELDS = 4   # sp_entry / sp_reloc are 4 x int32
 
@@ -45,6 +46,7 @@ def lib() -> ctypes.CDLL:
         L.segpaged_workspace_bytes.argtypes = [I, I, I, I, I, I, I, P, P, ctypes.POINTER(SZ)]
         L.segpaged_prefill.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, I64, F, P, P, P, SZ, P]
         L.segpaged_decode.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, I64, F, P, P, P, SZ, P]
+        L.segpaged_decode_static.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, I64, F, P, P, P]
         L.segpaged_pack_pages.argtypes = [I, I, I, I64, P, P, P, I64, P, P, P]
         L.segpaged_unpack_pages.argtypes = [I, I, I, I64, P, P, P, P, P, I64, P]
         L.segpaged_strerror.restype = ctypes.c_char_p
@@ -53,7 +55,7 @@ def lib() -> ctypes.CDLL:
         L.segpaged_last_error.argtypes = []
         L.segpaged_version.restype = I
         for fn in ("segpaged_build_tables", "rope_relocate", "segpaged_workspace_bytes", "segpaged_prefill",
-                   "segpaged_decode", "segpaged_pack_pages", "segpaged_unpack_pages"):
+                   "segpaged_decode", "segpaged_decode_static", "segpaged_pack_pages", "segpaged_unpack_pages"):
             getattr(L, fn).restype = I
         _lib = L
     return _lib
@@ -177,6 +179,18 @@ def decode(q, k_pool, v_pool, *, page_size, group, n_seq, n_slot, h_row_ptr, d_q
                                _dptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "segpaged_decode")
 
+
+
+def decode_static(q, k_pool, v_pool, *, page_size, group, n_seq, n_slot, h_row_ptr, d_q_pos, d_cls, d_window,
+                  d_row_ptr, d_entries, scale, out, lse, stream=None):
+    """segpaged_decode_static: segpaged_decode with the library's static scratch (no workspace)."""
+    D = q.shape[-1]
+    rp = _i32(h_row_ptr)
+    rc = lib().segpaged_decode_static(_dtype_code(q), D, page_size, group, n_seq, n_slot, _ptr(rp),
+                                      _dptr(d_q_pos), _dptr(d_cls), _dptr(d_window), _dptr(d_row_ptr),
+                                      _dptr(d_entries), _dptr(q), _dptr(k_pool), _dptr(v_pool), k_pool.shape[0],
+                                      float(scale), _dptr(out), _dptr(lse), _stream(stream))
+    _check(rc, "segpaged_decode_static")
 
 
 def pack_pages(k_pool, v_pool, d_entries, n_entries: int, k_out, v_out, stream=None):

@@ -243,6 +243,31 @@ int segpaged_decode(int dtype, int head_dim, int page_size, int group, int n_seq
                     float softmax_scale, void *out, float *lse,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * segpaged_decode_static - segpaged_decode without a caller workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, hosts that forbid hipMalloc.  Same arguments, results
+ * and kernels as segpaged_decode, minus the workspace.
+ *
+ * Scratch: a static device array of SP_STATIC_SCRATCH_BYTES in the library,
+ * one per GPU, held until the process ends; its address is looked up on the
+ * first call on each device.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine).  Every call on one GPU shares that GPU's
+ * array, so calls that overlap on one GPU (different streams, or threads
+ * without ordering) race and must not be issued; calls on one stream are safe.
+ * The scratch needs no clearing: nothing of a previous call's contents is read.
+ * Errors: as segpaged_decode; SP_EWORKSPACE (before any GPU work) when the call
+ * needs more scratch than SP_STATIC_SCRATCH_BYTES (segpaged_workspace_bytes
+ * with SP_WS_DECODE gives the need).
+ */
+#define SP_STATIC_SCRATCH_BYTES (16u << 20)
+int segpaged_decode_static(int dtype, int head_dim, int page_size, int group, int n_seq, int n_slot,
+                           const int32_t *h_row_ptr, const int32_t *d_q_pos,
+                           const int32_t *d_cls, const int32_t *d_window,
+                           const int32_t *d_row_ptr, const sp_entry *d_entries,
+                           const void *q, const void *k_pool, const void *v_pool, int64_t n_phys,
+                           float softmax_scale, void *out, float *lse, void *stream);
+
 /* Text of a status code; segpaged_last_error: the calling thread's message for
  * its last failed call ("" if none). */
 const char *segpaged_strerror(int status);
