@@ -24,6 +24,14 @@ SP_STATIC_SCRATCH_BYTES = 16 << 20
 ENTRY_FIELDS = 4   # sp_entry / sp_reloc are 4 x int32
 
 
+class Layout(ctypes.Structure):
+    """sp_layout: the host calls' shared layout arguments (pointers into numpy arrays the caller keeps alive)."""
+    _fields_ = [("n_seq", ctypes.c_int), ("seg_ptr", ctypes.c_void_p), ("segs", ctypes.c_void_p),
+                ("n_new", ctypes.c_void_p), ("n_slot", ctypes.c_int), ("cls", ctypes.c_void_p),
+                ("window", ctypes.c_void_p), ("ret_ptr", ctypes.c_void_p), ("ret_pages", ctypes.c_void_p),
+                ("page_size", ctypes.c_int)]
+
+
 class SegPagedError(RuntimeError):
     def __init__(self, status: int, call: str, msg: str):
         super().__init__(f"{call} failed: status {status} ({msg})")
@@ -42,6 +50,9 @@ def lib() -> ctypes.CDLL:
         P, I, I64, D, F, SZ = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_float,
                                ctypes.c_size_t)
         L.segpaged_build_tables.argtypes = [I, P, P, P, P, P, I, P, P, P, P, I, I64, P, P, P, P, P, P, P]
+        L.segpaged_build_tables_ex.argtypes = [P, P, P, P, I64, P, P, P, P, P, P, P]
+        L.segpaged_tables_from_chains.argtypes = [P, P, P, P, P, P, P, P]
+        L.segpaged_release_pages.argtypes = [P, P, P, P, P, P]
         L.rope_relocate.argtypes = [P, P, I, I, I, I64, I, P, D, P]
         L.segpaged_workspace_bytes.argtypes = [I, I, I, I, I, I, I, P, P, ctypes.POINTER(SZ)]
         L.segpaged_prefill.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, I64, F, P, P, P, SZ, P]
@@ -54,7 +65,8 @@ def lib() -> ctypes.CDLL:
         L.segpaged_last_error.restype = ctypes.c_char_p
         L.segpaged_last_error.argtypes = []
         L.segpaged_version.restype = I
-        for fn in ("segpaged_build_tables", "rope_relocate", "segpaged_workspace_bytes", "segpaged_prefill",
+        for fn in ("segpaged_build_tables", "segpaged_build_tables_ex", "segpaged_tables_from_chains",
+                   "segpaged_release_pages", "rope_relocate", "segpaged_workspace_bytes", "segpaged_prefill",
                    "segpaged_decode", "segpaged_decode_static", "segpaged_pack_pages", "segpaged_unpack_pages"):
             getattr(L, fn).restype = I
         _lib = L
@@ -131,6 +143,74 @@ def build_tables(seg_ptr, segs, n_new, q_lo, q_hi, cls, window, ret_ptr, ret_pag
                 entries=entries[: counts[1]], reloc=reloc[: counts[2]])
 
 
+def _layout(seg_ptr, segs, n_new, cls, window, ret_ptr, ret_pages, page_size):
+    """(sp_layout, arrays it points into); keep the arrays alive while the layout is used."""
+    arrs = [_i32(a) for a in (seg_ptr, segs, n_new, cls, window, ret_ptr, ret_pages)]
+    seg_ptr, segs, n_new, cls, window, ret_ptr, ret_pages = arrs
+    lay = Layout(len(n_new), _ptr(seg_ptr), _ptr(segs), _ptr(n_new), len(cls), _ptr(cls), _ptr(window),
+                 _ptr(ret_ptr), _ptr(ret_pages), int(page_size))
+    return lay, arrs
+
+
+def build_tables_ex(seg_ptr, segs, n_new, q_lo, q_hi, cls, window, ret_ptr, ret_pages, page_size, free_list,
+                    keep_from=None, counts_only=False):
+    """segpaged_build_tables_ex: as build_tables, with window-only storage when
+    keep_from is given (storage then holds -1 for pages not stored).  Returns
+    dict(counts [4], chain_ptr, storage, row_ptr, entries [n, 4], reloc [n, 4])."""
+    L = lib()
+    lay, keep = _layout(seg_ptr, segs, n_new, cls, window, ret_ptr, ret_pages, page_size)
+    q_lo, q_hi, keep_from, free_list = map(_i32, (q_lo, q_hi, keep_from, free_list))
+    counts = np.zeros(4, np.int64)
+    n_free = 0 if free_list is None else len(free_list)
+    head = [ctypes.byref(lay), _ptr(q_lo), _ptr(q_hi), _ptr(keep_from), n_free, _ptr(free_list)]
+    _check(L.segpaged_build_tables_ex(*head, None, None, None, None, None, _ptr(counts)), "segpaged_build_tables_ex")
+    if counts_only:
+        return dict(counts=counts)
+    n_rows = lay.n_slot * lay.n_seq
+    chain_ptr = np.zeros(n_rows + 1, np.int32)
+    storage = np.zeros(max(1, counts[0]), np.int32)
+    row_ptr = np.zeros(n_rows + 1, np.int32)
+    entries = np.zeros((max(1, counts[1]), ENTRY_FIELDS), np.int32)
+    reloc = np.zeros((max(1, counts[2]), ENTRY_FIELDS), np.int32)
+    _check(L.segpaged_build_tables_ex(*head, _ptr(chain_ptr), _ptr(storage), _ptr(row_ptr), _ptr(entries),
+                                      _ptr(reloc), _ptr(counts)), "segpaged_build_tables_ex")
+    del keep
+    return dict(counts=counts, chain_ptr=chain_ptr, storage=storage[: counts[0]], row_ptr=row_ptr,
+                entries=entries[: counts[1]], reloc=reloc[: counts[2]])
+
+
+def tables_from_chains(seg_ptr, segs, n_new, q_lo, q_hi, cls, window, ret_ptr, ret_pages, page_size, chain_ptr,
+                       storage):
+    """segpaged_tables_from_chains: (row_ptr, entries [n, 4]) of a call over existing chains."""
+    L = lib()
+    lay, keep = _layout(seg_ptr, segs, n_new, cls, window, ret_ptr, ret_pages, page_size)
+    q_lo, q_hi, chain_ptr, storage = map(_i32, (q_lo, q_hi, chain_ptr, storage))
+    n = ctypes.c_int64(0)
+    head = [ctypes.byref(lay), _ptr(q_lo), _ptr(q_hi), _ptr(chain_ptr), _ptr(storage)]
+    _check(L.segpaged_tables_from_chains(*head, None, None, ctypes.byref(n)), "segpaged_tables_from_chains")
+    row_ptr = np.zeros(lay.n_slot * lay.n_seq + 1, np.int32)
+    entries = np.zeros((max(1, n.value), ENTRY_FIELDS), np.int32)
+    _check(L.segpaged_tables_from_chains(*head, _ptr(row_ptr), _ptr(entries), ctypes.byref(n)),
+           "segpaged_tables_from_chains")
+    del keep
+    return row_ptr, entries[: n.value]
+
+
+def release_pages(seg_ptr, segs, n_new, cls, window, ret_ptr, ret_pages, page_size, p_next, chain_ptr, storage):
+    """segpaged_release_pages.  ``storage`` (int32 numpy) is updated in place;
+    returns the released physical ids."""
+    L = lib()
+    lay, keep = _layout(seg_ptr, segs, n_new, cls, window, ret_ptr, ret_pages, page_size)
+    p_next, chain_ptr = _i32(p_next), _i32(chain_ptr)
+    assert storage.dtype == np.int32 and storage.flags.c_contiguous
+    released = np.zeros(max(1, len(storage)), np.int32)
+    n = ctypes.c_int64(0)
+    _check(L.segpaged_release_pages(ctypes.byref(lay), _ptr(p_next), _ptr(chain_ptr), _ptr(storage), _ptr(released),
+                                    ctypes.byref(n)), "segpaged_release_pages")
+    del keep
+    return released[: n.value]
+
+
 # --------------------------------------------------------------------------- device calls
 
 def rope_relocate(k_in, k_out, page_size: int, reloc_dev, theta: float, stream=None):
@@ -178,7 +258,6 @@ def decode(q, k_pool, v_pool, *, page_size, group, n_seq, n_slot, h_row_ptr, d_q
                                _dptr(k_pool), _dptr(v_pool), k_pool.shape[0], float(scale), _dptr(out), _dptr(lse),
                                _dptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "segpaged_decode")
-
 
 
 def decode_static(q, k_pool, v_pool, *, page_size, group, n_seq, n_slot, h_row_ptr, d_q_pos, d_cls, d_window,

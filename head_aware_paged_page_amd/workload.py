@@ -20,7 +20,11 @@ from .kvpool import chain_token_index, place
 
 class Workload:
     def __init__(self, lay, device="cuda", fill_nan: bool = True, pool_slack: int = 0, relocated_pool: bool = True,
-                 free=None):
+                 free=None, window_only: bool = False):
+        """window_only: store only the pages some query of the session can read
+        (segpaged_build_tables_ex with keep_from = the prefill chunk's first
+        position); the decode tables then come from segpaged_tables_from_chains
+        over the same storage, and tokens on pages not stored are not placed."""
         import torch
         self.lay = lay
         self.device = device
@@ -33,17 +37,24 @@ class Workload:
 
         arr_p = lay.abi_arrays("prefill")
         arr_d = lay.abi_arrays("decode")
-        cnt = sp.build_tables(**arr_p, page_size=ps, free_list=None, counts_only=True)["counts"]
+        self.window_only = window_only
+        self.keep_from = arr_p["q_lo"] if window_only else None
+        cnt = sp.build_tables_ex(**arr_p, page_size=ps, free_list=None, keep_from=self.keep_from,
+                                 counts_only=True)["counts"]
         if free is None:
-            self.n_phys = int(cnt[0]) + pool_slack
+            self.n_phys = int(cnt[3]) + pool_slack
             self.free = synth.free_list(lay, self.n_phys)
         else:
             self.free = np.ascontiguousarray(free, dtype=np.int32)
             self.n_phys = int(self.free.max()) + 1
         t0 = time.perf_counter()
-        self.tp = sp.build_tables(**arr_p, page_size=ps, free_list=self.free)
+        self.tp = sp.build_tables_ex(**arr_p, page_size=ps, free_list=self.free, keep_from=self.keep_from)
         t1 = time.perf_counter()
-        self.td = sp.build_tables(**arr_d, page_size=ps, free_list=self.free)
+        self.layout_args = {k: arr_p[k] for k in ("seg_ptr", "segs", "n_new", "cls", "window", "ret_ptr",
+                                                  "ret_pages")}
+        rp, ent = sp.tables_from_chains(**self.layout_args, q_lo=arr_d["q_lo"], q_hi=arr_d["q_hi"], page_size=ps,
+                                        chain_ptr=self.tp["chain_ptr"], storage=self.tp["storage"])
+        self.td = dict(row_ptr=rp, entries=ent)
         self.build_seconds = (t1 - t0)
         self.arr_p, self.arr_d = arr_p, arr_d
 
@@ -76,7 +87,11 @@ class Workload:
                 K = torch.cat([u["seg_k"], u["new_k"]])
                 V = torch.cat([u["seg_v"], u["new_v"]])
                 idx, off = self._tok_index[seq]
-                place(self.k_pool, self.v_pool, self.chain_phys(slot, seq), idx, off, K, V)
+                phys = self.chain_phys(slot, seq)
+                stored = phys[idx] >= 0               # tokens on pages that are not stored stay out
+                if not bool(stored.all()):
+                    idx, off, K, V = idx[stored], off[stored], K[stored], V[stored]
+                place(self.k_pool, self.v_pool, phys, idx, off, K, V)
                 del u, K, V
         self.k_reloc = self.k_pool.clone() if relocated_pool else None
 
@@ -146,7 +161,10 @@ class Workload:
         return K, V
 
     def gather_keys(self, pool, slot: int, seq: int):
-        """Keys of one chain read back from a K pool, in position order (fp64 host)."""
+        """Keys of one chain read back from a K pool, in position order (fp64
+        host); NaN for tokens on pages that are not stored."""
         idx, off = self._tok_index[seq]
         phys = self.chain_phys(slot, seq)[idx]
-        return pool[phys, off].double().cpu().numpy()
+        out = pool[phys.clamp(min=0), off].double()
+        out[phys < 0] = float("nan")
+        return out.cpu().numpy()

@@ -152,6 +152,77 @@ int segpaged_build_tables(int n_seq, const int32_t *seg_ptr, const sp_segment *s
                           sp_entry *entries, sp_reloc *reloc, int64_t counts[3]);
 
 /*
+ * The layout every host call below shares: sequences, segments, new-token
+ * capacity, slots and their classes, retrieval lists, page size - the same
+ * arguments, with the same rules, as segpaged_build_tables takes one by one.
+ */
+typedef struct {
+    int n_seq;
+    const int32_t *seg_ptr;        /* [n_seq+1] CSR over segs */
+    const sp_segment *segs;
+    const int32_t *n_new;          /* [n_seq] new-token capacity (prefill chunk + decode tokens) */
+    int n_slot;
+    const int32_t *cls, *window;   /* [n_slot] */
+    const int32_t *ret_ptr, *ret_pages;   /* retrieval lists per row; NULL if no slot is retrieval */
+    int page_size;
+} sp_layout;
+
+/*
+ * segpaged_build_tables_ex - segpaged_build_tables with window-only storage.
+ *
+ * Defines: the is96.com commentary's deployment paragraph (local heads store
+ * only window-sized KV, so one GPU holds several times more sessions) and its
+ * SegPagedAttention paragraphs (a head's pages hold only its own KV).
+ *
+ * keep_from[n_seq] (or NULL for whole chains, which is segpaged_build_tables):
+ * every later query of sequence q is at a position >= keep_from[q]
+ * (0 <= keep_from[q] <= q_lo[q]).  A head then stores only the chain pages
+ * holding a token that some query at a position in [keep_from, E + n_new) can
+ * see: a local(W) head the pages whose last position is >= keep_from - W + 1,
+ * a retrieval head its listed segment pages and the new-token pages, global
+ * and dense heads every page.  Chains keep their logical layout: storage has
+ * one id per chain page, -1 for a page that is not stored; allocation pops the
+ * free list in the usual order, skipping pages that are not stored.  The
+ * relocation list holds only stored segment pages.
+ * counts[4]: chain pages (length of storage), table entries, relocation items,
+ * pages taken from the free list.  Other arguments as segpaged_build_tables.
+ */
+int segpaged_build_tables_ex(const sp_layout *layout, const int32_t *q_lo, const int32_t *q_hi,
+                             const int32_t *keep_from, int64_t n_free, const int32_t *free_list,
+                             int32_t *chain_ptr, int32_t *storage, int32_t *row_ptr,
+                             sp_entry *entries, sp_reloc *reloc, int64_t counts[4]);
+
+/*
+ * segpaged_tables_from_chains - the tables of a call over existing chains
+ * (host): the same table rule as segpaged_build_tables, with the physical ids
+ * read from chain_ptr[n_rows+1] / storage (as built, after any releases).
+ * Two-call convention: row_ptr and entries both NULL returns the entry count.
+ * Errors: SP_EINVAL also when a page the call's queries read is not stored
+ * (-1: released, or outside the window the storage was built for).
+ */
+int segpaged_tables_from_chains(const sp_layout *layout, const int32_t *q_lo, const int32_t *q_hi,
+                                const int32_t *chain_ptr, const int32_t *storage,
+                                int32_t *row_ptr, sp_entry *entries, int64_t *n_entries);
+
+/*
+ * segpaged_release_pages - return pages no later query can read to the free
+ * list (host).
+ *
+ * Defines: the PagedAttention page's walk-through (at the end of a sequence its
+ * blocks return to the free pool) together with window-only storage: once the
+ * next query of sequence q is at position p_next[q] (>= its first new
+ * position), every stored page that no query at a position in
+ * [p_next[q], E + n_new) can see is released: a local head's pages that slid
+ * out of its window, a retrieval head's unlisted segment pages, and - once
+ * p_next[q] >= E + n_new, i.e. the sequence is over - every page of every head.
+ * Released ids are written to released[] in row order, then chain order
+ * (capacity: chain_ptr[n_rows] ids), their storage entries become -1, and
+ * *n_released is set.  Nothing else changes.
+ */
+int segpaged_release_pages(const sp_layout *layout, const int32_t *p_next, const int32_t *chain_ptr,
+                           int32_t *storage, int32_t *released, int64_t *n_released);
+
+/*
  * rope_relocate - move cached segment keys from their offline to their online
  * rotary position (device).
  *

@@ -36,6 +36,26 @@ Readings where the pages are silent:
     at the call (position <= q_hi).
   * The relocation list has one entry per stored segment page, in allocation
     order, with delta = online base - offline base of its segment.
+
+Window-only storage and page release (the is96.com commentary's deployment
+paragraph: local heads keep only window-sized KV, which multiplies the sessions
+one GPU holds; its SegPagedAttention paragraphs: each head's pages hold only its
+own KV; the PagedAttention page's walk-through: at the end of a sequence its
+blocks return to the free pool).  Readings:
+  * A session's queries start at position keep_from (the first token of its
+    prefill chunk) and never move left.  A head then stores only the pages
+    holding a token that some query at a position in [keep_from, end) can see,
+    end = first new position + new-token capacity: a local head the pages
+    reaching into its window, a retrieval head its listed pages, global and
+    dense heads every page.  The chain keeps its logical layout; a page that is
+    not stored has storage id -1.
+  * Allocation pops the free list in the usual order, skipping pages that are
+    not stored.
+  * Release: once the next query of a sequence is at position p_next, a stored
+    page no query at a position in [p_next, end) can see returns to the free
+    list (its storage id becomes -1).  For a local head that is a page that
+    slid out of the window; at p_next >= end (the sequence is over) every page
+    of every head returns, which is the walk-through's end-of-sequence release.
 """
 from __future__ import annotations
 
@@ -116,6 +136,14 @@ def visible(cls: int, window: int, listed, tok_pos, tok_segpage, tok_new, p: int
     raise ValueError(f"unknown class {cls}")
 
 
+def phys_of(storage, chain_ptr, r: int, i: int) -> int:
+    """Physical id of chain page i of row r; raises if that page is not stored."""
+    v = int(storage[int(chain_ptr[r]) + i])
+    if v < 0:
+        raise LookupError(f"row {r}: chain page {i} is not stored")
+    return v
+
+
 def row_table(lay, storage, chain_ptr, slot: int, seq: int, q_lo: int, q_hi: int):
     """Table of one (slot, seq) row: int64 array [n, 3] of (phys, pos_start, n_valid)."""
     r = slot * lay.n_seq + seq
@@ -127,7 +155,7 @@ def row_table(lay, storage, chain_ptr, slot: int, seq: int, q_lo: int, q_hi: int
     for p in range(int(q_lo), int(q_hi) + 1):          # union over the call's queries
         seen |= visible(c, w, listed, tpos, tsp, tnew, p)
     present = np.bincount(tpage[tpos <= int(q_hi)], minlength=len(pages))
-    out = [(int(storage[chain_ptr[r] + i]), pages[i]["pos_start"], int(present[i]))
+    out = [(phys_of(storage, chain_ptr, r, int(i)), pages[i]["pos_start"], int(present[i]))
            for i in np.unique(tpage[seen])]            # chain order = ascending position
     return np.asarray(out, np.int64).reshape(-1, 3)
 
@@ -164,7 +192,7 @@ def reloc_list(lay, storage, chain_ptr, rows=None):
             if seq not in chains:
                 chains[seq] = chain(lay, seq)
             for i, pg in enumerate(chains[seq]):
-                if pg["seg"] < 0:
+                if pg["seg"] < 0 or storage[chain_ptr[r] + i] < 0:      # new-token page, or not stored
                     continue
                 s = pg["seg"]
                 delta = int(lay.seg_online[seq][s]) - int(lay.seg_offline[seq][s])
@@ -179,3 +207,62 @@ def visible_counts(lay, slot: int, seq: int, q_pos):
     c, w = int(lay.cls[slot]), int(lay.window[slot])
     return np.asarray([np.count_nonzero(visible(c, w, listed, tpos, tsp, tnew, int(p))) for p in q_pos],
                       np.int64)
+
+
+# ------------------------------------------------------------------ window-only storage and release
+
+def seq_end(lay, seq: int) -> int:
+    """One past the last position a query of the sequence can take."""
+    return int(lay.new_base[seq]) + lay.n_new
+
+
+def needed_pages(lay, slot: int, seq: int, p_from: int):
+    """Boolean per chain page: does some query at a position in [p_from, end)
+    see at least one of the page's tokens?  (Union of the visible sets.)"""
+    tpos, tpage, tsp, tnew = tokens(lay, seq)
+    listed = lay.ret_pages.get((slot, seq), [])
+    c, w = int(lay.cls[slot]), int(lay.window[slot])
+    seen = np.zeros(len(tpos), bool)
+    for p in range(int(p_from), seq_end(lay, seq)):
+        seen |= visible(c, w, listed, tpos, tsp, tnew, p)
+    need = np.zeros(len(chain(lay, seq)), bool)
+    need[np.unique(tpage[seen])] = True
+    return need
+
+
+def allocate_window(lay, free, keep_from):
+    """Window-only storage: every head stores only the pages some query at a
+    position in [keep_from[seq], end) can see.  Returns (storage, chain_ptr)
+    over the full chains, with -1 for a page that is not stored."""
+    storage, chain_ptr = [], np.zeros(lay.n_slot * lay.n_seq + 1, np.int64)
+    k = 0
+    for slot in range(lay.n_slot):
+        for seq in range(lay.n_seq):
+            r = slot * lay.n_seq + seq
+            for needed in needed_pages(lay, slot, seq, keep_from[seq]):
+                if needed:
+                    if k >= len(free):
+                        raise MemoryError(f"free list holds {len(free)} pages, more needed")
+                    storage.append(int(free[k]))
+                    k += 1
+                else:
+                    storage.append(-1)
+            chain_ptr[r + 1] = len(storage)
+    return np.asarray(storage, np.int64), chain_ptr
+
+
+def release(lay, storage, chain_ptr, p_next):
+    """Return to the free list every stored page that no query at a position in
+    [p_next[seq], end) can see.  Returns (released ids in row order, then chain
+    order; the storage with those ids set to -1)."""
+    storage = np.asarray(storage, np.int64).copy()
+    out = []
+    for slot in range(lay.n_slot):
+        for seq in range(lay.n_seq):
+            r = slot * lay.n_seq + seq
+            for i, needed in enumerate(needed_pages(lay, slot, seq, p_next[seq])):
+                k = int(chain_ptr[r]) + i
+                if storage[k] >= 0 and not needed:
+                    out.append(int(storage[k]))
+                    storage[k] = -1
+    return np.asarray(out, np.int64), storage

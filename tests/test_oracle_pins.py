@@ -329,3 +329,101 @@ def test_pack_unpack_round_trip_restores_exactly_the_listed_pages():
     assert np.array_equal(k2[listed], k[listed]) and np.array_equal(v2[listed], v[listed])
     assert not k2[~listed].any() and not v2[~listed].any()
 
+
+# ---------------------------------------------------------------- window-only storage and page release
+
+def _window_hand(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "window_storage_by_hand.json")))
+    lay = custom_layout(seg_lens=[g["seg_lens"]], offline=[g["offline"]], n_prefill=g["n_prefill"],
+                        n_decode=g["n_decode"], classes=[tuple(c) for c in g["classes"]], page_size=g["page_size"])
+    return g, lay
+
+
+def test_window_storage_by_hand(golden_dir):
+    """tests/golden/window_storage_by_hand.json: stored pages, allocation, the
+    relocation list, the prefill tables, then releases and decode tables step
+    by step until the sequence ends, all worked out by hand."""
+    g, lay = _window_hand(golden_dir)
+    storage, chain_ptr = otab.allocate_window(lay, np.asarray(g["free_list"]), [g["keep_from"]])
+    assert storage.tolist() == g["expected_storage"] and chain_ptr.tolist() == g["expected_chain_ptr"]
+    assert otab.reloc_list(lay, storage, chain_ptr).tolist() == g["expected_reloc"]
+    row_ptr, ent = otab.tables(lay, storage, chain_ptr, [9], [12])
+    assert [ent[row_ptr[r]:row_ptr[r + 1]].tolist() for r in range(3)] == g["expected_prefill_rows"]
+    freed = []
+    for st in g["steps"]:
+        rel, storage = otab.release(lay, storage, chain_ptr, [st["release_at"]])
+        assert rel.tolist() == st["expected_released"]
+        freed += rel.tolist()
+        if "decode_at" in st:
+            p = st["decode_at"]
+            row_ptr, ent = otab.tables(lay, storage, chain_ptr, [p], [p])
+            assert [ent[row_ptr[r]:row_ptr[r + 1]].tolist() for r in range(3)] == st["expected_decode_rows"]
+    assert sorted(freed) == sorted(x for x in g["expected_storage"] if x >= 0) and (storage == -1).all()
+    with pytest.raises(LookupError):          # a released page cannot appear in a table
+        otab.tables(lay, storage, chain_ptr, [15], [15])
+
+
+def test_walkthrough_end_of_sequence_release(golden_dir):
+    """The PagedAttention page's walk-through: when the sequence ends, blocks 7, 1
+    and 3 return to the pool, which then again holds all nine blocks."""
+    g = json.load(open(os.path.join(golden_dir, "paged_block_walkthrough.json")))
+    lay = custom_layout(seg_lens=[[]], offline=[[]], n_prefill=g["prompt_tokens"],
+                        n_decode=g["generated_tokens"], classes=[(GLOBAL, 0)], page_size=g["page_size"])
+    free = np.asarray(g["free_list"])
+    storage, chain_ptr = otab.allocate_window(lay, free, [0])
+    assert storage.tolist() == g["expected_block_table"]
+    # while tokens remain to be generated nothing is released
+    for p_next in range(0, otab.seq_end(lay, 0)):
+        assert len(otab.release(lay, storage, chain_ptr, [p_next])[0]) == 0
+    rel, after = otab.release(lay, storage, chain_ptr, [otab.seq_end(lay, 0)])
+    assert rel.tolist() == [7, 1, 3]
+    assert sorted(free[len(storage):].tolist()) == g["expected_unused_blocks"]
+    assert sorted(free[len(storage):].tolist() + rel.tolist()) == sorted(g["free_list"]) and (after == -1).all()
+
+
+def _needed_closed_form(lay, seq, c, W, listed, p_from):
+    """Chain pages a head still needs once every query is at or after p_from, in
+    closed form: none once the sequence is over; otherwise for local(W) the
+    pages whose last position is at least p_from - W + 1, for retrieval the
+    listed segment pages and the new-token pages, for the rest all pages."""
+    out = []
+    for pg in otab.chain(lay, seq):
+        last = pg["pos_start"] + pg["n_valid"] - 1
+        if p_from >= otab.seq_end(lay, seq):
+            out.append(False)
+        elif c == LOCAL:
+            out.append(last >= p_from - W + 1)
+        elif c == RETRIEVAL:
+            out.append(pg["seg"] < 0 or pg["seg_page"] in set(int(x) for x in listed))
+        else:
+            out.append(True)
+    return np.asarray(out)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_window_storage_and_release_closed_form(seed):
+    """On random layouts the stored pages after allocation, and the live pages
+    after a release at every later position, are exactly the closed-form sets."""
+    r = np.random.default_rng(300 + seed)
+    ps = int(r.choice([1, 2, 4, 16]))
+    lens = [list(r.integers(1, 40, size=int(r.integers(1, 4))))]
+    classes = [(GLOBAL, 0), (LOCAL, int(r.integers(1, 30))), (LOCAL, 1), (RETRIEVAL, 0), (DENSE, 0),
+               (LOCAL, 1000)]
+    nsp = sum(-(-l // ps) for l in lens[0])
+    listed = np.sort(r.choice(nsp, size=min(2, nsp), replace=False))
+    lay = custom_layout(seg_lens=lens, offline=[[0] * len(lens[0])], n_prefill=int(r.integers(1, 9)),
+                        n_decode=int(r.integers(1, 12)), classes=classes, page_size=ps,
+                        ret_lists={(3, 0): listed})
+    k0 = int(lay.new_base[0])
+    storage, chain_ptr = otab.allocate_window(lay, r.permutation(4000), [k0])
+    for slot, (c, W) in enumerate(classes):
+        got = storage[chain_ptr[slot]:chain_ptr[slot + 1]] >= 0
+        assert np.array_equal(got, _needed_closed_form(lay, 0, c, W, listed, k0)), slot
+    assert len(set(storage[storage >= 0].tolist())) == int((storage >= 0).sum())
+    for p_next in range(k0, otab.seq_end(lay, 0) + 2):
+        rel, after = otab.release(lay, storage, chain_ptr, [p_next])
+        for slot, (c, W) in enumerate(classes):
+            live = after[chain_ptr[slot]:chain_ptr[slot + 1]] >= 0
+            want = _needed_closed_form(lay, 0, c, W, listed, p_next)
+            assert np.array_equal(live, want), (slot, p_next)
+        assert sorted(rel.tolist()) == sorted(storage[(storage >= 0) & (after < 0)].tolist())
