@@ -14,9 +14,13 @@ Everything is NumPy in fp64, written to be checked against the pages by eye:
                            forward by the new one).
   * ``oracle.attention`` - softmax attention of each query over exactly its
                            visible tokens (gathered, no mask).
+  * ``oracle.importance`` - the attention importance each context token
+                           receives from the chunk's queries, and the top-k
+                           token selection for the sparse FFN.
+  * ``oracle.pack``      - per-head visible-page pack and unpack.
 
 Every function is pinned by tests under ``tests/`` against closed forms, the
 worked block-table example of the PagedAttention page, hand-written fixtures
 and a brute-force dense masked attention; no function is "parity unpinned".
 """
-from . import tables, rope, attention  # noqa: F401
+from . import tables, rope, attention, importance, pack  # noqa: F401

@@ -427,3 +427,77 @@ def test_window_storage_and_release_closed_form(seed):
             want = _needed_closed_form(lay, 0, c, W, listed, p_next)
             assert np.array_equal(live, want), (slot, p_next)
         assert sorted(rel.tolist()) == sorted(storage[(storage >= 0) & (after < 0)].tolist())
+
+
+# ---------------------------------------------------------------- attention importance and token selection
+from oracle import importance as oimp  # noqa: E402
+
+
+def _imp_layout(ps, seed):
+    classes = [(GLOBAL, 0), (LOCAL, 1), (LOCAL, 5), (RETRIEVAL, 0), (DENSE, 0), (LOCAL, 40)]
+    return _rand_layout(ps, 3, 13, 6, classes, seed)
+
+
+@pytest.mark.parametrize("ps", [1, 3, 4, 16])
+def test_importance_equals_column_sums_of_dense_masked_softmax(ps):
+    """Importance = column sums, over every query row and head, of the dense masked
+    softmax matrix (the mask formulation of the same attention, built
+    independently of the oracle's visible sets)."""
+    for seed in range(3):
+        lay = _imp_layout(ps, seed)
+        D, G = lay.head_dim, lay.group
+        q_pos = list(range(int(lay.new_base[0]), int(lay.new_base[0]) + lay.n_new))
+        n_tok = lay.ctx_len(0) + lay.n_new
+        for slot in range(lay.n_slot):
+            K = RNG.standard_normal((n_tok, D))
+            q = RNG.standard_normal((len(q_pos), G, D))
+            got = oimp.row_importance(lay, slot, 0, K, q, q_pos, n_tok)
+            M = _dense_mask(lay, slot, q_pos)
+            s = np.einsum("igd,td->igt", q, K) / math.sqrt(D)
+            s = np.where(M[:, None, :], s, -np.inf)
+            e = np.exp(s - s.max(axis=2, keepdims=True))
+            P = e / e.sum(axis=2, keepdims=True)
+            want = P.sum(axis=(0, 1))                 # positions are 0 .. n_tok-1 in token order here
+            assert np.max(np.abs(got - want)) <= 1e-12
+            assert abs(got.sum() - len(q_pos) * G) <= 1e-10     # each row's probabilities sum to 1
+
+
+def test_importance_zero_queries_closed_form():
+    """Q = 0: every visible token of a query gets 1/|V(p)|; with positions 0..N-1
+    contiguous, |V(p)| = p + 1 (global) or min(W, p + 1) (local W), so
+    imp(t) = G * sum over queries p >= t (and p < t + W for local) of 1/|V(p)|."""
+    lay = custom_layout(seg_lens=[[7, 5]], offline=[[0, 0]], n_prefill=6, n_decode=1,
+                        classes=[(GLOBAL, 0), (LOCAL, 4)], page_size=4, head_dim=8, group=3)
+    q_pos = list(range(12, 18))
+    n = 18
+    K = RNG.standard_normal((n, 8))
+    for slot, W in ((0, None), (1, 4)):
+        got = oimp.row_importance(lay, slot, 0, K, np.zeros((6, 3, 8)), q_pos, n)
+        want = np.zeros(n)
+        for t in range(n):
+            for p in q_pos:
+                if t <= p and (W is None or t > p - W):
+                    want[t] += 3.0 / ((p + 1) if W is None else min(W, p + 1))
+        assert np.max(np.abs(got - want)) <= 1e-14
+
+
+def test_select_by_hand(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "select_by_hand.json")))
+    score = np.asarray(g["score"], np.float32)
+    for c in g["cases"]:
+        assert oimp.select(score, c["k"]).tolist() == c["expected"]
+    ls = g["layer_sum"]
+    got = oimp.layer_scores(np.asarray(ls["slots"], np.float64))
+    assert got.dtype == np.float32 and got.tolist() == ls["expected"]
+
+
+def test_select_is_the_stable_descending_order():
+    """Brute force on small random arrays with many ties: the selection is the
+    first k of the positions sorted by (score descending, position ascending)."""
+    r = np.random.default_rng(8)
+    for _ in range(200):
+        n = int(r.integers(1, 40))
+        score = r.integers(0, 5, n).astype(np.float32) / 4
+        k = int(r.integers(0, n + 1))
+        ranked = sorted(range(n), key=lambda t: (-float(score[t]), t))
+        assert oimp.select(score, k).tolist() == sorted(ranked[:k])
