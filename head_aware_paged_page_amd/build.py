@@ -9,7 +9,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIB_DIR, "libsegpaged.so")
-SOURCES = ["tables.cpp", "runtime.cpp", "relocate.hip", "prefill.hip", "decode.hip", "attn_f32.hip", "pack.hip", "noalloc.hip"]
+SOURCES = ["tables.cpp", "runtime.cpp", "relocate.hip", "prefill.hip", "decode.hip", "attn_f32.hip", "pack.hip", "noalloc.hip", "importance.hip"]
 ARCH = "gfx950"
 
 

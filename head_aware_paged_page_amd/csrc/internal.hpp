@@ -90,6 +90,39 @@ struct AttnArgs {
 
 int launch_prefill(const AttnArgs &a, const Plan &p, int64_t n_tok, hipStream_t s);
 int launch_decode(const AttnArgs &a, const Plan &p, hipStream_t s);
+// Attention importance (segpaged_token_importance) and token selection.
+struct ImportancePlan {
+    int n_rows = 0, tpt = 0;
+    int64_t n_items = 0, n_part = 0, n_red = 0, e_max = 0;
+    size_t off_item_ptr = 0, off_part_ptr = 0, off_red_ptr = 0, off_part = 0;
+    size_t bytes = 0;
+};
+struct ImportanceArgs {
+    int dtype, head_dim, page_size, group, n_seq, n_slot;
+    const int32_t *h_row_ptr, *h_tok_ptr;
+    const int32_t *d_tok_ptr, *d_q_pos0, *d_cls, *d_window, *d_row_ptr, *d_pos_ptr;
+    const sp_entry *d_entries;
+    const void *q, *k_pool;
+    int64_t n_phys;
+    float scale;
+    const float *lse;
+    int64_t n_pos;
+    float *imp;
+    void *ws;
+};
+int plan_importance(int dtype, int head_dim, int page_size, int group, int n_seq, int n_slot,
+                    const int32_t *h_tok_ptr, const int32_t *h_row_ptr, ImportancePlan *out);
+int launch_importance(const ImportanceArgs &a, const ImportancePlan &p, hipStream_t s);
+struct SelectArgs {
+    int n_layers, slots_per_layer, n_seq;
+    const int32_t *d_pos_ptr, *d_sel_ptr;
+    int64_t n_pos, sel_total;
+    const float *imp;
+    float *score;
+    int32_t *sel;
+};
+int launch_select(const SelectArgs &a, hipStream_t s);
+
 int launch_page_copy(bool unpack, const void *d_entries, int64_t n, const void *src_k, const void *src_v,
                      void *dst_k, void *dst_v, int64_t n_phys, int page_bytes, hipStream_t s);
 

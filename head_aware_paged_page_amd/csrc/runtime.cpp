@@ -283,11 +283,41 @@ extern "C" const char *segpaged_last_error(void) { return sp::g_err; }
 
 extern "C" int segpaged_version(void) { return 100; }
 
+static int check_importance_plan(int dtype, int head_dim, int page_size, int group, int n_seq, int n_slot,
+                                 const int32_t *h_tok_ptr, const int32_t *h_row_ptr, sp::ImportancePlan *ip) {
+    if (dtype != SP_F32 && dtype != SP_BF16) return fail(SP_EINVAL, "dtype %d", dtype);
+    if (n_seq < 1 || n_slot < 1) return fail(SP_EINVAL, "n_seq=%d n_slot=%d must be >= 1", n_seq, n_slot);
+    if (group < 1 || group > 16) return fail(SP_EUNSUPPORTED, "group %d outside 1..16", group);
+    if (dtype == SP_BF16) {
+        if (head_dim != 64 && head_dim != 128) return fail(SP_EUNSUPPORTED, "bf16 head_dim %d (64 or 128)", head_dim);
+        if (page_size != 16 && page_size != 32) return fail(SP_EUNSUPPORTED, "bf16 page_size %d (16 or 32)", page_size);
+    } else if (head_dim < 16 || head_dim > 256 || head_dim % 16 || page_size < 1) {
+        return fail(SP_EUNSUPPORTED, "fp32 head_dim %d page_size %d", head_dim, page_size);
+    }
+    if (!h_row_ptr || !h_tok_ptr) return fail(SP_EINVAL, "h_row_ptr/h_tok_ptr is NULL");
+    if ((int64_t)n_slot * n_seq > INT32_MAX - 1) return fail(SP_EINVAL, "too many rows");
+    const int n_rows = n_slot * n_seq;
+    if (h_row_ptr[0] != 0 || h_tok_ptr[0] != 0) return fail(SP_EINVAL, "row_ptr[0] and tok_ptr[0] must be 0");
+    for (int r = 0; r < n_rows; ++r)
+        if (h_row_ptr[r + 1] <= h_row_ptr[r]) return fail(SP_EINVAL, "row %d has an empty or negative table", r);
+    for (int q = 0; q < n_seq; ++q)
+        if (h_tok_ptr[q + 1] < h_tok_ptr[q]) return fail(SP_EINVAL, "tok_ptr not ascending at %d", q);
+    return sp::plan_importance(dtype, head_dim, page_size, group, n_seq, n_slot, h_tok_ptr, h_row_ptr, ip);
+}
+
 extern "C" int segpaged_workspace_bytes(int kind, int dtype, int head_dim, int page_size, int group, int n_seq,
                                         int n_slot, const int32_t *h_tok_ptr, const int32_t *h_row_ptr,
                                         size_t *bytes) {
     sp::clear_error();
     if (!bytes) return fail(SP_EINVAL, "bytes is NULL");
+    if (kind == SP_WS_IMPORTANCE) {
+        sp::ImportancePlan ip;
+        const int rc = check_importance_plan(dtype, head_dim, page_size, group, n_seq, n_slot, h_tok_ptr, h_row_ptr,
+                                             &ip);
+        if (rc) return rc;
+        *bytes = ip.bytes;
+        return SP_OK;
+    }
     sp::Plan p;
     const int rc = sp::make_plan(kind, dtype, head_dim, page_size, group, n_seq, n_slot, h_tok_ptr, h_row_ptr, &p);
     if (rc) return rc;
@@ -408,4 +438,54 @@ extern "C" int segpaged_unpack_pages(int dtype, int head_dim, int page_size, int
                                      void *v_pool, int64_t n_phys, void *stream) {
     return page_copy(true, dtype, head_dim, page_size, n_entries, d_entries, k_in, v_in, k_pool, v_pool, n_phys,
                      stream);
+}
+
+extern "C" int segpaged_token_importance(int dtype, int head_dim, int page_size, int group, int n_seq, int n_slot,
+                                         const int32_t *h_tok_ptr, const int32_t *h_row_ptr,
+                                         const int32_t *d_tok_ptr, const int32_t *d_q_pos0, const int32_t *d_cls,
+                                         const int32_t *d_window, const int32_t *d_row_ptr,
+                                         const sp_entry *d_entries, const void *q, const void *k_pool,
+                                         int64_t n_phys, float softmax_scale, const float *lse,
+                                         const int32_t *h_pos_ptr, const int32_t *d_pos_ptr, float *imp,
+                                         void *workspace, size_t workspace_bytes, void *stream) {
+    sp::clear_error();
+    sp::ImportancePlan ip;
+    int rc = check_importance_plan(dtype, head_dim, page_size, group, n_seq, n_slot, h_tok_ptr, h_row_ptr, &ip);
+    if (rc) return rc;
+    if (!(softmax_scale > 0.0f) || softmax_scale != softmax_scale) return fail(SP_EINVAL, "softmax_scale must be > 0");
+    if (n_phys < 1) return fail(SP_EINVAL, "n_phys %lld", (long long)n_phys);
+    if (!d_tok_ptr || !d_q_pos0 || !d_cls || !d_window || !d_row_ptr || !d_entries || !q || !k_pool || !lse ||
+        !h_pos_ptr || !d_pos_ptr || !imp || !workspace)
+        return fail(SP_EINVAL, "a pointer is NULL");
+    if (h_pos_ptr[0] != 0) return fail(SP_EINVAL, "pos_ptr[0] must be 0");
+    for (int q2 = 0; q2 < n_seq; ++q2)
+        if (h_pos_ptr[q2 + 1] < h_pos_ptr[q2]) return fail(SP_EINVAL, "pos_ptr not ascending at %d", q2);
+    if (workspace_bytes < ip.bytes)
+        return fail(SP_EWORKSPACE, "workspace %zu bytes, %zu needed", workspace_bytes, ip.bytes);
+    if (((uintptr_t)workspace) % 256) return fail(SP_EINVAL, "workspace must be 256-byte aligned");
+    sp::ImportanceArgs a{dtype, head_dim, page_size, group, n_seq, n_slot, h_row_ptr, h_tok_ptr, d_tok_ptr, d_q_pos0,
+                         d_cls, d_window, d_row_ptr, d_pos_ptr, d_entries, q, k_pool, n_phys, softmax_scale, lse,
+                         (int64_t)h_pos_ptr[n_seq], imp, workspace};
+    return sp::launch_importance(a, ip, (hipStream_t)stream);
+}
+
+extern "C" int segpaged_select_tokens(int n_layers, int slots_per_layer, int n_seq, const int32_t *h_pos_ptr,
+                                      const int32_t *d_pos_ptr, const float *imp, const int32_t *h_sel_ptr,
+                                      const int32_t *d_sel_ptr, float *score, int32_t *sel, void *stream) {
+    sp::clear_error();
+    if (n_layers < 1 || slots_per_layer < 1 || n_seq < 1)
+        return fail(SP_EINVAL, "n_layers=%d slots_per_layer=%d n_seq=%d must be >= 1", n_layers, slots_per_layer,
+                    n_seq);
+    if ((int64_t)n_layers * slots_per_layer > INT32_MAX) return fail(SP_EINVAL, "too many slots");
+    if (!h_pos_ptr || !d_pos_ptr || !imp || !h_sel_ptr || !d_sel_ptr || !score || !sel)
+        return fail(SP_EINVAL, "a pointer is NULL");
+    if (h_pos_ptr[0] != 0 || h_sel_ptr[0] != 0) return fail(SP_EINVAL, "pos_ptr[0] and sel_ptr[0] must be 0");
+    for (int q = 0; q < n_seq; ++q) {
+        const int len = h_pos_ptr[q + 1] - h_pos_ptr[q], k = h_sel_ptr[q + 1] - h_sel_ptr[q];
+        if (len < 0) return fail(SP_EINVAL, "pos_ptr not ascending at %d", q);
+        if (k < 0 || k > len) return fail(SP_EINVAL, "seq %d: k = %d outside [0, %d candidates]", q, k, len);
+    }
+    sp::SelectArgs a{n_layers, slots_per_layer, n_seq, d_pos_ptr, d_sel_ptr, (int64_t)h_pos_ptr[n_seq],
+                     (int64_t)h_sel_ptr[n_seq], imp, score, sel};
+    return sp::launch_select(a, (hipStream_t)stream);
 }

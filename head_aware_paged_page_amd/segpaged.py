@@ -18,7 +18,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "li
 SP_OK, SP_EINVAL, SP_ENOMEM, SP_EHIP, SP_EUNSUPPORTED, SP_EWORKSPACE = 0, -1, -2, -3, -4, -5
 SP_GLOBAL, SP_LOCAL, SP_RETRIEVAL, SP_DENSE = 0, 1, 2, 3
 SP_F32, SP_BF16 = 0, 1
-SP_WS_PREFILL, SP_WS_DECODE = 0, 1
+SP_WS_PREFILL, SP_WS_DECODE, SP_WS_IMPORTANCE = 0, 1, 2
 SP_STATIC_SCRATCH_BYTES = 16 << 20
 
 ENTRY_FIELDS = 4   # sp_entry / sp_reloc are 4 x int32
@@ -58,6 +58,9 @@ def lib() -> ctypes.CDLL:
         L.segpaged_prefill.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, I64, F, P, P, P, SZ, P]
         L.segpaged_decode.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, I64, F, P, P, P, SZ, P]
         L.segpaged_decode_static.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, I64, F, P, P, P]
+        L.segpaged_token_importance.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, I64, F, P, P, P, P,
+                                                P, SZ, P]
+        L.segpaged_select_tokens.argtypes = [I, I, I, P, P, P, P, P, P, P, P]
         L.segpaged_pack_pages.argtypes = [I, I, I, I64, P, P, P, I64, P, P, P]
         L.segpaged_unpack_pages.argtypes = [I, I, I, I64, P, P, P, P, P, I64, P]
         L.segpaged_strerror.restype = ctypes.c_char_p
@@ -67,7 +70,8 @@ def lib() -> ctypes.CDLL:
         L.segpaged_version.restype = I
         for fn in ("segpaged_build_tables", "segpaged_build_tables_ex", "segpaged_tables_from_chains",
                    "segpaged_release_pages", "rope_relocate", "segpaged_workspace_bytes", "segpaged_prefill",
-                   "segpaged_decode", "segpaged_decode_static", "segpaged_pack_pages", "segpaged_unpack_pages"):
+                   "segpaged_decode", "segpaged_decode_static", "segpaged_pack_pages", "segpaged_unpack_pages",
+                   "segpaged_token_importance", "segpaged_select_tokens"):
             getattr(L, fn).restype = I
         _lib = L
     return _lib
@@ -270,6 +274,29 @@ def decode_static(q, k_pool, v_pool, *, page_size, group, n_seq, n_slot, h_row_p
                                       _dptr(d_entries), _dptr(q), _dptr(k_pool), _dptr(v_pool), k_pool.shape[0],
                                       float(scale), _dptr(out), _dptr(lse), _stream(stream))
     _check(rc, "segpaged_decode_static")
+
+
+def token_importance(q, k_pool, *, page_size, group, n_seq, n_slot, h_tok_ptr, h_row_ptr, d_tok_ptr, d_q_pos0,
+                     d_cls, d_window, d_row_ptr, d_entries, scale, lse, h_pos_ptr, d_pos_ptr, imp, workspace,
+                     stream=None):
+    """segpaged_token_importance.  imp: fp32 [n_slot, h_pos_ptr[-1]] (written); lse from segpaged_prefill."""
+    D = q.shape[-1]
+    tp, rp, pp = _i32(h_tok_ptr), _i32(h_row_ptr), _i32(h_pos_ptr)
+    rc = lib().segpaged_token_importance(_dtype_code(q), D, page_size, group, n_seq, n_slot, _ptr(tp), _ptr(rp),
+                                         _dptr(d_tok_ptr), _dptr(d_q_pos0), _dptr(d_cls), _dptr(d_window),
+                                         _dptr(d_row_ptr), _dptr(d_entries), _dptr(q), _dptr(k_pool),
+                                         k_pool.shape[0], float(scale), _dptr(lse), _ptr(pp), _dptr(d_pos_ptr),
+                                         _dptr(imp), _dptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "segpaged_token_importance")
+
+
+def select_tokens(imp, *, n_layers, slots_per_layer, n_seq, h_pos_ptr, d_pos_ptr, h_sel_ptr, d_sel_ptr, score, sel,
+                  stream=None):
+    """segpaged_select_tokens.  score fp32 [n_layers, h_pos_ptr[-1]], sel int32 [n_layers, h_sel_ptr[-1]] (written)."""
+    pp, sp_ = _i32(h_pos_ptr), _i32(h_sel_ptr)
+    rc = lib().segpaged_select_tokens(n_layers, slots_per_layer, n_seq, _ptr(pp), _dptr(d_pos_ptr), _dptr(imp),
+                                      _ptr(sp_), _dptr(d_sel_ptr), _dptr(score), _dptr(sel), _stream(stream))
+    _check(rc, "segpaged_select_tokens")
 
 
 def pack_pages(k_pool, v_pool, d_entries, n_entries: int, k_out, v_out, stream=None):

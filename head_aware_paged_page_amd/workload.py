@@ -139,6 +139,33 @@ class Workload:
                   lse=self.lse_decode if lse is None else lse, workspace=self.workspace, stream=stream)
         return self.out_decode if out is None else out, self.lse_decode if lse is None else lse
 
+    def importance(self, lse=None, k=None, span="all", out=None, stream=None):
+        """segpaged_token_importance over the prefill call (its lse by default):
+        returns (imp [n_slot, n_pos] fp32, pos_ptr); span "all" covers every
+        position of a sequence (segments and new tokens), "segments" only the
+        reused segment positions.  out: a previous call's (imp, pos_ptr) to
+        write into again (no allocation)."""
+        import torch
+        if out is None:
+            lens = [int(self.lay.new_base[s]) + (self.lay.n_new if span == "all" else 0) for s in range(self.n_seq)]
+            pos_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+            code = sp.SP_F32 if self.lay.dtype == "f32" else sp.SP_BF16
+            nb = sp.workspace_bytes(sp.SP_WS_IMPORTANCE, code, self.D, self.ps, self.G, self.n_seq, self.n_slot,
+                                    self.h_tok_ptr, self.tp["row_ptr"])
+            self._imp_ws = torch.empty(nb, dtype=torch.uint8, device=self.device)
+            self._imp_pos = torch.from_numpy(pos_ptr).to(self.device)
+            imp = torch.empty((self.n_slot, int(pos_ptr[-1])), dtype=torch.float32, device=self.device)
+        else:
+            imp, pos_ptr = out
+        sp.token_importance(self.q_prefill, k if k is not None else self.k_pool, page_size=self.ps, group=self.G,
+                            n_seq=self.n_seq, n_slot=self.n_slot, h_tok_ptr=self.h_tok_ptr,
+                            h_row_ptr=self.tp["row_ptr"], d_tok_ptr=self.d_tok_ptr, d_q_pos0=self.d_q_pos0,
+                            d_cls=self.d_cls, d_window=self.d_window, d_row_ptr=self.p_row_ptr,
+                            d_entries=self.p_entries, scale=self.scale,
+                            lse=self.lse_prefill if lse is None else lse, h_pos_ptr=pos_ptr,
+                            d_pos_ptr=self._imp_pos, imp=imp, workspace=self._imp_ws, stream=stream)
+        return imp, pos_ptr
+
     def replicas(self, n: int):
         """n copies of the pools, [(k_pool, v_pool, k_reloc)], the first being the
         workload's own; the copies share every table (same physical ids)."""

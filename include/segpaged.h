@@ -86,8 +86,9 @@ extern "C" {
 #define SP_BF16 1
 
 /* workspace kinds */
-#define SP_WS_PREFILL 0
-#define SP_WS_DECODE  1
+#define SP_WS_PREFILL    0
+#define SP_WS_DECODE     1
+#define SP_WS_IMPORTANCE 2
 
 /* One reused segment of a sequence: len tokens placed at online positions
  * [online_base, online_base + len), whose cached keys were rotated at
@@ -247,11 +248,12 @@ int rope_relocate(const void *k_in, void *k_out, int dtype, int page_size, int h
                   void *stream);
 
 /*
- * segpaged_workspace_bytes - device workspace a prefill or decode call needs.
+ * segpaged_workspace_bytes - device workspace a prefill, decode or importance
+ * call needs.
  *
- * kind SP_WS_PREFILL uses h_tok_ptr[n_seq+1] (query tokens of each sequence);
- * kind SP_WS_DECODE ignores it (one query token per sequence).  h_row_ptr is
- * the host copy of the call's row_ptr.  Writes *bytes (> 0).
+ * kinds SP_WS_PREFILL and SP_WS_IMPORTANCE use h_tok_ptr[n_seq+1] (query tokens
+ * of each sequence); SP_WS_DECODE ignores it (one query token per sequence).
+ * h_row_ptr is the host copy of the call's row_ptr.  Writes *bytes (> 0).
  *
  * The workspace needs no initialisation: a call neither relies on what it
  * holds before the call nor leaves anything a later call relies on (its work
@@ -338,6 +340,57 @@ int segpaged_decode_static(int dtype, int head_dim, int page_size, int group, in
                            const int32_t *d_row_ptr, const sp_entry *d_entries,
                            const void *q, const void *k_pool, const void *v_pool, int64_t n_phys,
                            float softmax_scale, void *out, float *lse, void *stream);
+
+/*
+ * segpaged_token_importance - the attention importance every key position
+ * receives from a prefill chunk's query rows (device).
+ *
+ * Defines: the product profile's section 3, third building block (the elastic
+ * sparse FFN picks the tokens that run the feed-forward network by attention
+ * importance; low-contribution tokens skip it).  The pages give no formula;
+ * the importance of key position t in a slot is the softmax probability mass
+ * the chunk's rows (its tokens x the slot's group heads) give it:
+ *   imp[slot][pos_ptr[s] + t] = sum over rows (i, g) of sequence s that see t of
+ *                               exp(softmax_scale * q[i, h] . k_t - lse[i, h]),  h = slot*group + g
+ * with lse the natural-log log-sum-exp segpaged_prefill returned for the same
+ * call (same q, tables and pools); each row's probabilities then sum to 1.
+ * Positions t < pos_ptr[s+1] - pos_ptr[s] of sequence s are written (0 where no
+ * row sees t); keys at later positions are skipped.  imp is [n_slot][pos_ptr[n_seq]]
+ * fp32.  Other arguments as segpaged_prefill; workspace of
+ * segpaged_workspace_bytes(SP_WS_IMPORTANCE, ...) bytes, 256-byte aligned.
+ * The result does not depend on the launch (every sum runs in a fixed order).
+ * Supported: SP_BF16 with head_dim 64 or 128, page_size 16 or 32, group 1..16;
+ * SP_F32 with head_dim 16..256 (multiple of 16), any page_size.
+ */
+int segpaged_token_importance(int dtype, int head_dim, int page_size, int group, int n_seq, int n_slot,
+                              const int32_t *h_tok_ptr, const int32_t *h_row_ptr,
+                              const int32_t *d_tok_ptr, const int32_t *d_q_pos0,
+                              const int32_t *d_cls, const int32_t *d_window,
+                              const int32_t *d_row_ptr, const sp_entry *d_entries,
+                              const void *q, const void *k_pool, int64_t n_phys, float softmax_scale,
+                              const float *lse, const int32_t *h_pos_ptr, const int32_t *d_pos_ptr, float *imp,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * segpaged_select_tokens - the tokens that run the FFN: in each (layer,
+ * sequence) the k positions of highest layer importance (device).
+ *
+ * Defines: the same sparse-FFN building block (token-level selection by
+ * attention importance).  Slots l * slots_per_layer .. (l + 1) * slots_per_layer - 1
+ * form layer l.  For sequence s with candidates t in [0, pos_ptr[s+1] - pos_ptr[s])
+ * and k = sel_ptr[s+1] - sel_ptr[s]:
+ *   score[l][pos_ptr[s] + t] = imp[l*spl][..] + imp[l*spl + 1][..] + ...  (fp32, slot order)
+ *   sel[l][sel_ptr[s] .. + k) = the k positions of largest score, equal scores
+ *                               taken from the lowest position, in ascending order.
+ * imp: [n_layers * slots_per_layer][pos_ptr[n_seq]] fp32 (non-negative, as
+ * segpaged_token_importance writes it); score: [n_layers][pos_ptr[n_seq]] fp32
+ * (output); sel: [n_layers][sel_ptr[n_seq]] int32 (output).  h_* are host
+ * copies of the d_* arrays.  Errors: SP_EINVAL (k outside [0, candidates],
+ * bad CSR, NULL pointer).
+ */
+int segpaged_select_tokens(int n_layers, int slots_per_layer, int n_seq, const int32_t *h_pos_ptr,
+                           const int32_t *d_pos_ptr, const float *imp, const int32_t *h_sel_ptr,
+                           const int32_t *d_sel_ptr, float *score, int32_t *sel, void *stream);
 
 /* Text of a status code; segpaged_last_error: the calling thread's message for
  * its last failed call ("" if none). */

@@ -28,7 +28,7 @@ import numpy as np
 from .configs import CONFIGS, GLOBAL, LOCAL, RETRIEVAL, DENSE
 
 # stream ids for SeedSequence spawn keys
-_S_CLASS, _S_LENS, _S_RET, _S_FREE, _S_VAL, _S_Q = 1, 2, 3, 4, 5, 6
+_S_CLASS, _S_LENS, _S_RET, _S_FREE, _S_VAL, _S_Q, _S_SCORE = 1, 2, 3, 4, 5, 6, 7
 
 
 def _rng(seed: int, cfg_idx: int, *key: int) -> np.random.Generator:
@@ -252,3 +252,13 @@ def seq_queries(lay: Layout, seq: int, device="cpu"):
     x = torch.randn(lay.n_new, lay.n_slot * lay.group, lay.head_dim, generator=g, device=device,
                     dtype=torch.float32)
     return x.to(_torch_dtype(lay))
+
+
+def score_values(seed: int, n_slots: int, n_pos: int, levels: int = 0) -> np.ndarray:
+    """Seeded non-negative fp32 per-slot scores [n_slots, n_pos] (inputs for the
+    token selection).  levels > 0 draws from that many equally spaced values, so
+    that equal scores (ties) are common."""
+    r = _rng(seed, 98, _S_SCORE, n_slots, n_pos, levels)
+    if levels > 0:
+        return (r.integers(0, levels, size=(n_slots, n_pos)) / levels).astype(np.float32)
+    return r.exponential(1.0, size=(n_slots, n_pos)).astype(np.float32)
