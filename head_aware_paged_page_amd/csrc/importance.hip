@@ -335,26 +335,50 @@ __global__ __launch_bounds__(256) void importance_f32_kernel(ImpF32Params P) {
 }
 
 // ---------------------------------------------------------------- token selection
-// One workgroup per (sequence, layer).  The layer score of each candidate
-// position (its slots' importances added in fp32 in slot order) goes to
-// `score`; the k-th largest score T is found by a radix select over the fp32
-// bit patterns (scores are >= 0, so the bit patterns order like the values),
-// 8 bits per pass from the top; then one ordered pass over the positions
-// writes every position above T and the lowest positions equal to T, in
-// ascending order.
-constexpr int SW = 16;   // waves of a selection workgroup
+// The layer scores (each position's slot importances added in fp32 in slot
+// order) come from a grid-wide kernel; then one workgroup per (sequence,
+// layer) finds the k-th largest score T by a radix select over the fp32 bit
+// patterns (scores are >= 0, so the bit patterns order like the values), 8
+// bits per pass from the top, and one ordered pass writes every position above
+// T and the lowest positions equal to T, in ascending order.  A sequence's
+// scores are staged in LDS when they fit (every pass then reads LDS);
+// otherwise the passes read them from global memory SE positions per thread
+// at a time.  Each thread owns consecutive positions, so the ordered pass
+// needs one pair of block-wide scans per chunk.
+constexpr int SW = 16;                 // waves of a selection workgroup
+constexpr int SE = 16;                 // consecutive positions per thread and chunk
+constexpr int SCHUNK = SW * 64 * SE;
+constexpr int kSelLds = 32768;         // longest candidate list staged in LDS (128 KB)
 
 struct SelParams {
     const float *imp;
     float *score;
     int32_t *sel;
     const int32_t *pos_ptr, *sel_ptr;
-    int spl, n_seq;
+    int spl, n_seq, n_layers;
     int64_t n_pos, sel_total;
 };
 
+__global__ __launch_bounds__(256) void layer_score_kernel(SelParams P) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int layer = blockIdx.y;
+    if (t >= P.n_pos) return;
+    const float *imp = P.imp + (int64_t)layer * P.spl * P.n_pos + t;
+    float v[8];
+    float s = 0.f;
+    int j = 0;
+    for (; j + 8 <= P.spl; j += 8) {     // eight loads in flight, added in slot order
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = imp[(int64_t)(j + i) * P.n_pos];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = (j + i == 0) ? v[i] : s + v[i];
+    }
+    for (; j < P.spl; ++j) s = j == 0 ? imp[0] : s + imp[(int64_t)j * P.n_pos];
+    P.score[(int64_t)layer * P.n_pos + t] = s;
+}
+
+// Exclusive prefix over the workgroup of small non-negative counts (and the total).
 __device__ __forceinline__ int block_exclusive_scan(int x, int *s_wave, int *total) {
-    // ballot-free scan of small non-negative counts: wave prefix by shuffles, then waves in LDS
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int v = x;
 #pragma unroll
@@ -365,9 +389,10 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int *s_wave, int *tot
     if (lane == 63) s_wave[wave] = v;
     __syncthreads();
     int before = 0, all = 0;
+#pragma unroll
     for (int w = 0; w < SW; ++w) {
         const int c = s_wave[w];
-        if (w < wave) before += c;
+        before += w < wave ? c : 0;
         all += c;
     }
     __syncthreads();
@@ -375,42 +400,79 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int *s_wave, int *tot
     return before + v - x;
 }
 
+template <bool IN_LDS>
 __global__ __launch_bounds__(SW * 64) void select_kernel(SelParams P) {
-    __shared__ int hist[256];
+    // one 256-bin histogram per wave (scores of one magnitude share a top
+    // byte, so a single shared histogram would serialise every atomic on a
+    // bin or two); a wave whose active lanes all fall in one bin adds them
+    // with one atomic
+    __shared__ int hist[SW][256];
     __shared__ int s_wave[SW];
     __shared__ int s_bin, s_above;
+    __shared__ uint32_t s_score[IN_LDS ? kSelLds : 1];
     const int seq = blockIdx.x, layer = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int64_t base = P.pos_ptr[seq];
     const int len = P.pos_ptr[seq + 1] - P.pos_ptr[seq];
     const int k = P.sel_ptr[seq + 1] - P.sel_ptr[seq];
-    float *score = P.score + (int64_t)layer * P.n_pos + base;
-    const float *imp = P.imp + (int64_t)layer * P.spl * P.n_pos + base;
-    for (int t = tid; t < len; t += SW * 64) {
-        float s = imp[t];
-        for (int j = 1; j < P.spl; ++j) s += imp[(int64_t)j * P.n_pos + t];
-        score[t] = s;
-    }
     if (k == 0) return;
-    __threadfence_block();
-    __syncthreads();
+    const uint32_t *g_score = (const uint32_t *)(P.score + (int64_t)layer * P.n_pos + base);
+    if (IN_LDS) {
+        for (int t = tid; t < len; t += SW * 64) s_score[t] = g_score[t];
+        __syncthreads();
+    }
+    auto load_chunk = [&](int t0, uint32_t (&u)[SE]) {
+#pragma unroll
+        for (int i = 0; i < SE; ++i) u[i] = t0 + i < len ? (IN_LDS ? s_score[t0 + i] : g_score[t0 + i]) : 0u;
+    };
     uint32_t prefix = 0, mask = 0;
     int remaining = k;                 // how many of the selected lie at or below the current prefix
     for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256; i += SW * 64) hist[i] = 0;
+        for (int i = lane; i < 256; i += 64) hist[wave][i] = 0;
         __syncthreads();
-        for (int t = tid; t < len; t += SW * 64) {
-            const uint32_t u = __float_as_uint(score[t]);
-            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1);
+        for (int c0 = 0; c0 < len; c0 += SCHUNK) {
+            const int t0 = c0 + tid * SE;
+            uint32_t u[SE];
+            load_chunk(t0, u);
+#pragma unroll
+            for (int i = 0; i < SE; ++i) {
+                const bool act = t0 + i < len && (u[i] & mask) == prefix;
+                const int bin = (int)((u[i] >> shift) & 255u);
+                const uint64_t am = __ballot(act);
+                if (!am) continue;
+                const int lb = __builtin_amdgcn_readlane(bin, (int)__builtin_ctzll(am));
+                if (__ballot(act && bin != lb) == 0) {
+                    if (lane == 0) atomicAdd(&hist[wave][lb], (int)__popcll(am));
+                } else if (act) {
+                    atomicAdd(&hist[wave][bin], 1);
+                }
+            }
         }
         __syncthreads();
-        if (tid == 0) {
-            int above = 0, b = 255;
-            for (; b > 0; --b) {
-                if (above + hist[b] >= remaining) break;
-                above += hist[b];
+        // counts per bin, highest bin first, summed over the waves; the bin
+        // where the running count from the top reaches `remaining`
+        int c = 0, v = 0;
+        if (tid < 256) {                     // waves 0..3: bins 255 - tid
+            const int b = 255 - tid;
+#pragma unroll
+            for (int w = 0; w < SW; ++w) c += hist[w][b];
+            v = c;                           // inclusive scan within the wave
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(v, off, 64);
+                if (lane >= off) v += y;
             }
-            s_bin = b;
-            s_above = above;
+            if (lane == 63) s_wave[wave] = v;
+        }
+        __syncthreads();
+        if (tid < 256) {
+            int before = 0;
+            for (int w = 0; w < wave; ++w) before += s_wave[w];
+            const int incl = before + v, excl = incl - c;
+            if (excl < remaining && incl >= remaining) {   // exactly one bin
+                s_bin = 255 - tid;
+                s_above = excl;
+            }
         }
         __syncthreads();
         prefix |= (uint32_t)s_bin << shift;
@@ -421,17 +483,29 @@ __global__ __launch_bounds__(SW * 64) void select_kernel(SelParams P) {
     // T = prefix: every position above T, and the `remaining` lowest positions equal to T
     int32_t *out = P.sel + (int64_t)layer * P.sel_total + P.sel_ptr[seq];
     int eq_before = 0, out_before = 0;
-    for (int t0 = 0; t0 < len; t0 += SW * 64) {
-        const int t = t0 + tid;
-        uint32_t u = 0;
-        if (t < len) u = __float_as_uint(score[t]);
-        const int gt = t < len && u > prefix, eq = t < len && u == prefix;
+    for (int c0 = 0; c0 < len; c0 += SCHUNK) {
+        const int t0 = c0 + tid * SE;
+        uint32_t u[SE];
+        load_chunk(t0, u);
+        int n_eq = 0;
+#pragma unroll
+        for (int i = 0; i < SE; ++i) n_eq += (t0 + i < len && u[i] == prefix) ? 1 : 0;
         int eq_total;
-        const int eq_rank = eq_before + block_exclusive_scan(eq, s_wave, &eq_total);
-        const int take = gt || (eq && eq_rank < remaining);
+        int eq_rank = eq_before + block_exclusive_scan(n_eq, s_wave, &eq_total);
+        int take[SE], n_take = 0;
+#pragma unroll
+        for (int i = 0; i < SE; ++i) {
+            const bool in = t0 + i < len;
+            const bool gt = in && u[i] > prefix, eq = in && u[i] == prefix;
+            take[i] = gt || (eq && eq_rank < remaining);
+            eq_rank += eq ? 1 : 0;
+            n_take += take[i];
+        }
         int take_total;
-        const int idx = out_before + block_exclusive_scan(take, s_wave, &take_total);
-        if (take) out[idx] = t;
+        int idx = out_before + block_exclusive_scan(n_take, s_wave, &take_total);
+#pragma unroll
+        for (int i = 0; i < SE; ++i)
+            if (take[i]) out[idx++] = t0 + i;
         eq_before += eq_total;
         out_before += take_total;
     }
@@ -597,9 +671,15 @@ int launch_select(const SelectArgs &a, hipStream_t stream) {
     P.sel_ptr = a.d_sel_ptr;
     P.spl = a.slots_per_layer;
     P.n_seq = a.n_seq;
+    P.n_layers = a.n_layers;
     P.n_pos = a.n_pos;
     P.sel_total = a.sel_total;
-    hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.n_seq, (unsigned)a.n_layers), dim3(SW * 64), 0, stream, P);
+    if (a.n_pos > 0)
+        hipLaunchKernelGGL(layer_score_kernel, dim3((unsigned)((a.n_pos + 255) / 256), (unsigned)a.n_layers),
+                           dim3(256), 0, stream, P);
+    const dim3 grid((unsigned)a.n_seq, (unsigned)a.n_layers);
+    if (a.max_len <= kSelLds) hipLaunchKernelGGL(select_kernel<true>, grid, dim3(SW * 64), 0, stream, P);
+    else hipLaunchKernelGGL(select_kernel<false>, grid, dim3(SW * 64), 0, stream, P);
     return check_hip(hipGetLastError(), "select launch");
 }
 

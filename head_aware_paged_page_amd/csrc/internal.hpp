@@ -114,7 +114,7 @@ int plan_importance(int dtype, int head_dim, int page_size, int group, int n_seq
                     const int32_t *h_tok_ptr, const int32_t *h_row_ptr, ImportancePlan *out);
 int launch_importance(const ImportanceArgs &a, const ImportancePlan &p, hipStream_t s);
 struct SelectArgs {
-    int n_layers, slots_per_layer, n_seq;
+    int n_layers, slots_per_layer, n_seq, max_len;
     const int32_t *d_pos_ptr, *d_sel_ptr;
     int64_t n_pos, sel_total;
     const float *imp;

@@ -480,12 +480,15 @@ extern "C" int segpaged_select_tokens(int n_layers, int slots_per_layer, int n_s
     if (!h_pos_ptr || !d_pos_ptr || !imp || !h_sel_ptr || !d_sel_ptr || !score || !sel)
         return fail(SP_EINVAL, "a pointer is NULL");
     if (h_pos_ptr[0] != 0 || h_sel_ptr[0] != 0) return fail(SP_EINVAL, "pos_ptr[0] and sel_ptr[0] must be 0");
+    int max_len = 0;
     for (int q = 0; q < n_seq; ++q) {
         const int len = h_pos_ptr[q + 1] - h_pos_ptr[q], k = h_sel_ptr[q + 1] - h_sel_ptr[q];
         if (len < 0) return fail(SP_EINVAL, "pos_ptr not ascending at %d", q);
         if (k < 0 || k > len) return fail(SP_EINVAL, "seq %d: k = %d outside [0, %d candidates]", q, k, len);
+        max_len = std::max(max_len, len);
     }
-    sp::SelectArgs a{n_layers, slots_per_layer, n_seq, d_pos_ptr, d_sel_ptr, (int64_t)h_pos_ptr[n_seq],
+    if (n_seq > 65535 || n_layers > 65535) return fail(SP_EUNSUPPORTED, "at most 65535 sequences and layers");
+    sp::SelectArgs a{n_layers, slots_per_layer, n_seq, max_len, d_pos_ptr, d_sel_ptr, (int64_t)h_pos_ptr[n_seq],
                      (int64_t)h_sel_ptr[n_seq], imp, score, sel};
     return sp::launch_select(a, (hipStream_t)stream);
 }

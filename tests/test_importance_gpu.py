@@ -150,14 +150,16 @@ def test_importance_128k_and_batch():
         torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("levels", [0, 3, 64])
-def test_select_tokens_bit_exact(levels):
+@pytest.mark.parametrize("levels,long", [(0, False), (3, False), (64, False), (0, True), (5, True)])
+def test_select_tokens_bit_exact(levels, long):
     """Seeded score arrays (levels > 0: many exact ties) through the selection:
-    layer scores and selected positions equal the oracle's, bit for bit."""
-    n_layers, spl = 3, 5
-    lens = [1, 37, 1000, 4096, 30000]
+    layer scores and selected positions equal the oracle's, bit for bit.
+    Lists up to 32768 candidates are selected from LDS, longer ones from
+    global memory (long=True adds one of 70000)."""
+    n_layers, spl = 3, 5 if not long else 9
+    lens = [1, 37, 1000, 4096, 30000] + ([70000] if long else [])
     pos_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    ks = [1, 10, 0, 4096, 7501]
+    ks = [1, 10, 0, 4096, 7501] + ([17000] if long else [])
     sel_ptr = np.concatenate([[0], np.cumsum(ks)]).astype(np.int32)
     imp_h = synth.score_values(levels, n_layers * spl, int(pos_ptr[-1]), levels)
     imp = torch.from_numpy(imp_h).cuda()
