@@ -15,10 +15,10 @@ Cache-clean timing.  The chip's last-level cache (256 MB) could serve a call
 data that the previous call just read (decode reads the global slots' pages
 prefill read a moment before).  So the pools exist in R identical replicas and
 step i runs relocate on replica i mod R, prefill on replica (i+1) mod R and
-decode on replica (i+2) mod R: with R = 3, at least one full relocation pass
-(about 1 GB at 32K) lies between two calls that touch the same replica.  A
-workload whose pools are too large for three copies runs with R = 1; its
-calls each move several GB.
+decode on replica (i+2) mod R: with R >= 3 and R replicas of at least 1 GB
+together, at least one full relocation pass lies between two calls that touch
+the same replica.  A workload whose pools are too large for three copies runs
+with R = 1; its calls each move several GB.
 
 Work counted is algorithmic only, from the host tables (never from the GPU):
   prefill FLOPs = 4 * head_dim per (query row, visible key) pair;
@@ -38,11 +38,14 @@ of K and V: about 256 FLOP/B, below the chip's 312 FLOP/B ridge, so the
 prefill of such a chunk is bound by HBM, not by the matrix cores.)
 
 With the default workload (32K) the same line also carries the 128K
-microbenchmark, measured the same way, under "config_128k".
+microbenchmark, measured the same way, under "config_128k", and the same
+workload with window-only storage (every head stores only the pages its
+queries can read) under "window_only", with the KV bytes one session holds.
 """
 from __future__ import annotations
 
 import argparse
+import gc
 import glob
 import json
 import multiprocessing as mp
@@ -75,6 +78,8 @@ WORKLOAD_TEXT = {
                    "page 16) recomputed in full, 30000 context tokens as one causal query chunk + 1 decode token",
 }
 MAX_REPLICA_BYTES = 24 << 30     # pools of all replicas together
+MIN_ROTATION_BYTES = 1 << 30     # replicas together at least this large (4x the last-level cache)
+MAX_REPLICAS = 16                # (a workload of a few MB, the tiny one, stops here)
 MAX_CPU_QUERIES = 128            # query tokens per row the oracle baseline runs (evenly spaced)
 from head_aware_paged_page_amd.profiling import source_hash  # noqa: E402
 
@@ -257,16 +262,20 @@ class HipEvent:
         return f.value
 
     def __del__(self):
-        if HipEvent._hip is not None and self.e:
-            HipEvent._hip.hipEventDestroy(self.e)
+        try:
+            if HipEvent._hip is not None and self.e:
+                HipEvent._hip.hipEventDestroy(self.e)
+        except (AttributeError, TypeError):   # interpreter shutdown: the module is being torn down
+            pass
 
 
 def _pct(xs, q):
     return float(np.percentile(np.asarray(xs), q))
 
 
-def run_config(name, seed, steps, warmup, log):
-    """Build one workload on the GPU and time `steps` steps; returns (result dict, workload)."""
+def run_config(name, seed, steps, warmup, log, window_only=False):
+    """Build one workload on the GPU and time `steps` steps; returns (result dict, workload).
+    window_only: each head stores only the pages its queries can read."""
     import torch
     import synth
     import head_aware_paged_page_amd.segpaged as sp
@@ -274,9 +283,12 @@ def run_config(name, seed, steps, warmup, log):
 
     lay = synth.make_layout(name, seed=seed)
     t0 = time.perf_counter()
-    log(f"building workload {name} ...")
-    w = Workload(lay, device="cuda")
-    n_rep = 3 if 3 * w.pool_bytes() <= MAX_REPLICA_BYTES else 1
+    log(f"building workload {name}{' (window-only storage)' if window_only else ''} ...")
+    w = Workload(lay, device="cuda", window_only=window_only)
+    # enough replicas that about 1 GB of other traffic separates two uses of one
+    n_rep = min(MAX_REPLICAS, max(3, -(-MIN_ROTATION_BYTES // w.pool_bytes())))
+    if n_rep * w.pool_bytes() > MAX_REPLICA_BYTES:
+        n_rep = 1
     reps = w.replicas(n_rep)
     torch.cuda.synchronize()
     log(f"built in {time.perf_counter() - t0:.1f} s; {n_rep} pool replica(s) of {w.pool_bytes() / 1e9:.2f} GB")
@@ -288,7 +300,8 @@ def run_config(name, seed, steps, warmup, log):
             fn()
         return (time.perf_counter() - t) / reps_ * 1e3
 
-    build_ms = host_ms(lambda: sp.build_tables(**w.arr_p, page_size=w.ps, free_list=w.free))
+    build_ms = host_ms(lambda: sp.build_tables_ex(**w.arr_p, page_size=w.ps, free_list=w.free,
+                                                  keep_from=w.keep_from))
     code = sp.SP_F32 if lay.dtype == "f32" else sp.SP_BF16
     plan_p = host_ms(lambda: sp.workspace_bytes(sp.SP_WS_PREFILL, code, w.D, w.ps, w.G, w.n_seq, w.n_slot,
                                                 w.h_tok_ptr, w.tp["row_ptr"]))
@@ -316,12 +329,15 @@ def run_config(name, seed, steps, warmup, log):
         calls(i)
     torch.cuda.synchronize()
     ev = [[HipEvent() for _ in range(4)] for _ in range(steps)]
+    gc.collect()
+    gc.disable()          # a collection inside the timed loop would stall the launches
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(steps):
         calls(i, ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    gc.enable()
     per = [[max(HipEvent.elapsed_ms(ev[i][a], ev[i][a + 1]), 1e-6) for i in range(steps)] for a in range(3)]
     t_reloc, t_pref, t_dec = (sum(x) / steps for x in per)
     ms_per_step = wall / steps * 1e3
@@ -390,15 +406,72 @@ def run_config(name, seed, steps, warmup, log):
     t_pack = HipEvent.elapsed_ms(pe[0], pe[1]) / n_calls
     del k_pk, v_pk
 
+    # Rows beyond the step: attention importance of the reused segment
+    # positions for the chunk's queries (against the prefill's lse), and the
+    # selection of a quarter of them per layer for the FFN.  Importance work:
+    # 2 * head_dim FLOPs per visible (query row, key) pair (the scores; one
+    # exp each), K of every table page read once, q and lse read, one fp32
+    # written per slot and position; selection reads the slots' importances and
+    # writes the layer scores.
+    beyond_imp = None
+    if lay.dtype == "bf16" and lay.n_slot % 8 == 0:
+        w.prefill(k=reps[0][2], v=reps[0][1])
+        lse = w.lse_prefill.clone()
+        imp, pos_ptr = w.importance(lse=lse, k=reps[0][2], span="segments")
+        n_layers, spl = lay.n_slot // 8, 8
+        n_pos = int(pos_ptr[-1])
+        ks = [int(pos_ptr[q + 1] - pos_ptr[q]) // 4 for q in range(lay.n_seq)]
+        sel_ptr = np.concatenate([[0], np.cumsum(ks)]).astype(np.int32)
+        score = torch.empty((n_layers, n_pos), dtype=torch.float32, device="cuda")
+        sel = torch.empty((n_layers, max(1, int(sel_ptr[-1]))), dtype=torch.int32, device="cuda")
+        d_pos, d_sel = torch.from_numpy(pos_ptr).cuda(), torch.from_numpy(sel_ptr).cuda()
+
+        def select():
+            sp.select_tokens(imp, n_layers=n_layers, slots_per_layer=spl, n_seq=lay.n_seq, h_pos_ptr=pos_ptr,
+                             d_pos_ptr=d_pos, h_sel_ptr=sel_ptr, d_sel_ptr=d_sel, score=score, sel=sel)
+        ie = [HipEvent() for _ in range(3)]
+        n_imp = max(n_rep, 6)
+        torch.cuda.synchronize()
+        ie[0].record(stream)
+        for i in range(n_imp):
+            w.importance(lse=lse, k=reps[i % n_rep][2], out=(imp, pos_ptr))
+        ie[1].record(stream)
+        for i in range(n_imp):
+            select()
+        ie[2].record(stream)
+        torch.cuda.synchronize()
+        t_imp = HipEvent.elapsed_ms(ie[0], ie[1]) / n_imp
+        t_sel = HipEvent.elapsed_ms(ie[1], ie[2]) / n_imp
+        esz = 2
+        imp_flops = work["prefill_pairs"] * 2 * lay.head_dim
+        imp_bytes = (int(w.tp["entries"][:, 2].sum()) * lay.head_dim * esz + w.q_prefill.numel() * esz
+                     + w.lse_prefill.numel() * 4 + imp.numel() * 4)
+        sel_bytes = imp.numel() * 4 + score.numel() * 4 + int(sel_ptr[-1]) * n_layers * 4
+        beyond_imp = {
+            "token_importance": {"ms": round(t_imp, 4), "TFLOP/s": round(imp_flops / t_imp / 1e9, 2),
+                                 "frac_mfma": round(imp_flops / t_imp / 1e-3 / PEAK_BF16_FLOPS, 4),
+                                 "GB/s": round(imp_bytes / t_imp / 1e6, 1),
+                                 "frac_hbm": round(imp_bytes / t_imp / 1e-3 / PEAK_HBM, 4),
+                                 "flops": imp_flops, "bytes": imp_bytes},
+            "select_tokens": {"ms": round(t_sel, 4), "GB/s": round(sel_bytes / t_sel / 1e6, 1),
+                              "bytes": sel_bytes, "layers": n_layers, "k_per_layer_seq": ks[:4]},
+        }
+        del imp, score, sel
+
+    page_bytes = w.k_pool[0].numel() * w.k_pool.element_size() * 2
+    stored = int((w.tp["storage"] >= 0).sum())
     res = {
         "value": round(value, 3), "ms_per_step": round(ms_per_step, 4),
+        "kv_bytes_per_session": stored * page_bytes, "stored_pages": stored,
+        "chain_pages": int(len(w.tp["storage"])),
         "config": {"workload": f"{name}: {WORKLOAD_TEXT[name]}", "seed": seed, "slots": lay.n_slot,
                    "sequences": lay.n_seq, "prefill_tokens": int(w.h_tok_ptr[-1]), "decode_tokens": lay.n_seq,
                    "pool_replicas": n_rep},
         "roofline": roof, "calls": calls_out,
         "beyond_step": {"pack_pages": {"ms": round(t_pack, 4), "GB/s": round(pack_bytes / t_pack / 1e6, 1),
                                        "frac_hbm": round(pack_bytes / t_pack / 1e-3 / PEAK_HBM, 4),
-                                       "bytes": pack_bytes, "pages": n_ent}},
+                                       "bytes": pack_bytes, "pages": n_ent},
+                        **(beyond_imp or {})},
         "dtype": "f32" if lay.dtype == "f32" else "bf16",
     }
     del reps
@@ -414,6 +487,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-128k", action="store_true", help="skip the 128K block of the default run")
+    ap.add_argument("--no-window", action="store_true", help="skip the window-only storage block")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle seconds per CPU process")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -448,6 +522,24 @@ def main():
         torch.cuda.empty_cache()
         res["config_128k"] = {k: r128[k] for k in ("value", "ms_per_step", "config", "roofline", "calls",
                                                     "beyond_step")}
+    if args.config in ("32k", "16k", "128k", "batch") and not args.no_window:
+        # Window-only storage of the same workload (every head stores only the
+        # pages its queries can read): the same step, and the KV bytes one
+        # session holds, against whole chains.
+        torch.cuda.empty_cache()
+        rw, ww = run_config(args.config, args.seed, args.steps, args.warmup, log, window_only=True)
+        del ww
+        torch.cuda.empty_cache()
+        whole = res0["kv_bytes_per_session"]
+        res["window_only"] = {
+            "ms_per_step": rw["ms_per_step"], "value": rw["value"],
+            "calls": {k: rw["calls"][k] for k in ("rope_relocate", "segpaged_prefill", "segpaged_decode")},
+            "kv_bytes_per_session": rw["kv_bytes_per_session"], "whole_chain_kv_bytes_per_session": whole,
+            "sessions_ratio": round(whole / rw["kv_bytes_per_session"], 3),
+            "sessions_per_288GB": {"whole_chains": int(288e9 // whole),
+                                   "window_only": int(288e9 // rw["kv_bytes_per_session"])},
+            "note": "relocation moves only the stored segment keys; prefill and decode results are bit-identical "
+                    "to whole-chain storage (value against the same roofline formula, now with fewer bytes)"}
     if pool is not None:
         log(f"timing the oracle on a CPU sample ({n_workers} processes) ...")
         res["cpu_baseline"] = cpu_baseline(pool, n_workers, lay, tp, args.cpu_seconds)

@@ -40,6 +40,11 @@ KERNELS = [
     ("prefill_f32_kernel", "segpaged_prefill", "prefill_f32_kernel"),
     ("decode_f32_kernel", "segpaged_decode", "decode_f32_kernel"),
     ("page_copy_kernel", "segpaged_pack_pages", "page_copy_kernel"),
+    ("importance_bf16_kernel", "segpaged_token_importance", "importance_bf16_kernel"),
+    ("importance_reduce_kernel", "segpaged_token_importance", "importance_reduce_kernel"),
+    ("importance_plan_kernel", "segpaged_token_importance", "importance_plan_kernel"),
+    ("fill_zero_kernel", "segpaged_token_importance", "fill_zero_kernel"),
+    ("select_kernel", "segpaged_select_tokens", "select_kernel"),
 ]
 # The sources a call's kernel timings and traffic depend on: its kernels and the
 # host runtime, whose planner sets split counts and launch shapes.
@@ -48,6 +53,8 @@ KERNEL_SOURCES = {
     "segpaged_prefill": ["prefill.hip", "device_common.hpp", "runtime.cpp", "internal.hpp"],
     "segpaged_decode": ["decode.hip", "device_common.hpp", "runtime.cpp", "internal.hpp"],
     "segpaged_pack_pages": ["pack.hip", "runtime.cpp", "internal.hpp"],
+    "segpaged_token_importance": ["importance.hip", "device_common.hpp", "runtime.cpp", "internal.hpp"],
+    "segpaged_select_tokens": ["importance.hip", "runtime.cpp", "internal.hpp"],
 }
 
 
@@ -60,10 +67,12 @@ def source_hash(call: str) -> str:
 
 
 def short_name(name: str):
+    # the longest matching fragment wins (importance_plan_kernel also contains plan_kernel)
+    best = None
     for frag, call, short in KERNELS:
-        if frag in name:
-            return call, short
-    return None, None
+        if frag in name and (best is None or len(frag) > len(best[0])):
+            best = (frag, call, short)
+    return (best[1], best[2]) if best else (None, None)
 
 
 def copy_main(mib: int) -> None:
@@ -105,9 +114,9 @@ def summarize(a) -> None:
     write = read_counters(a.write)
     stats = list(csv.DictReader(open(os.path.join(a.trace, "run_kernel_stats.csv"))))
     bench_cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
-                 f"python3 bench.py --config {a.workload} --steps 10 --warmup 2 --no-cpu-baseline --no-128k")
+                 f"python3 bench.py --config {a.workload} --steps 10 --warmup 2 --no-cpu-baseline --no-128k --no-window")
     pmc_cmd = ("rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- "
-               f"python3 bench.py --config {a.workload} --steps 2 --warmup 1 --no-cpu-baseline --no-128k")
+               f"python3 bench.py --config {a.workload} --steps 2 --warmup 1 --no-cpu-baseline --no-128k --no-window")
     copy_cmd = ("rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- "
                 f"python3 -m head_aware_paged_page_amd.profiling copy --mib {a.copy_mib}")
     lines = [f"# Kernel time, workload {a.workload} (rocprofv3 kernel trace, --stats)", "",
@@ -147,7 +156,8 @@ def summarize(a) -> None:
     open(txt, "w").write("\n".join(lines) + "\n")
     # one traffic record per call's dominant kernel, keyed by the call's source hash
     main_kernel = {"rope_relocate": "relocate_kernel", "segpaged_prefill": "prefill_bf16_kernel",
-                   "segpaged_decode": "decode_bf16_kernel", "segpaged_pack_pages": "page_copy_kernel"}
+                   "segpaged_decode": "decode_bf16_kernel", "segpaged_pack_pages": "page_copy_kernel",
+                   "segpaged_token_importance": "importance_bf16_kernel"}
     for call, short in main_kernel.items():
         if short not in traffic:
             continue

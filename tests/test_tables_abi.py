@@ -223,3 +223,40 @@ def test_bench_counts_from_host_tables_match_oracle(seed):
         for row in range(lay.n_slot * n_seq):
             slot, q = divmod(row, n_seq)
             assert np.array_equal(got[row], otab.visible_counts(lay, slot, q, q_pos[q])), (call, row)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_visible_sets_from_tables_equal_the_oracle(seed):
+    """The per-query visible token set derived from a library table and the
+    class predicate (a key of an entry (pos_start, n_valid) is seen by a query
+    at p when its position is <= p and, for local(W), > p - W) equals the
+    oracle's visible set, position for position, for every query of the
+    prefill and the decode call."""
+    r = np.random.default_rng(900 + seed)
+    ps = int(r.choice([1, 2, 4, 16]))
+    n_seq = int(r.integers(1, 3))
+    lens = [list(r.integers(1, 50, size=int(r.integers(0, 4)))) for _ in range(n_seq)]
+    off = [list(r.integers(-99, 99, size=len(l))) for l in lens]
+    classes = [(GLOBAL, 0), (LOCAL, int(r.integers(1, 40))), (RETRIEVAL, 0), (DENSE, 0), (LOCAL, 1)]
+    ret = {}
+    for q in range(n_seq):
+        nsp = sum(-(-l // ps) for l in lens[q])
+        ret[(2, q)] = np.sort(r.choice(nsp, size=int(r.integers(0, nsp + 1)), replace=False))
+    lay = custom_layout(seg_lens=lens, offline=off, n_prefill=int(r.integers(1, 20)), n_decode=1, classes=classes,
+                        page_size=ps, ret_lists=ret)
+    n = sp.build_tables(**lay.abi_arrays("prefill"), page_size=ps, free_list=None, counts_only=True)["counts"][0]
+    free = np.random.default_rng(seed).permutation(int(n) + 3).astype(np.int32)
+    for call, toks in (("prefill", np.arange(lay.n_prefill)), ("decode", np.asarray([lay.n_prefill]))):
+        t = _lib_tables(lay, call, free)
+        for row in range(lay.n_slot * n_seq):
+            slot, q = divmod(row, n_seq)
+            ent = t["entries"][t["row_ptr"][row]:t["row_ptr"][row + 1]]
+            keys = np.concatenate([np.arange(e[1], e[1] + e[2]) for e in ent])
+            tpos, _tp, tsp, tnew = otab.tokens(lay, q)
+            listed = lay.ret_pages.get((slot, q), [])
+            for p in lay.new_base[q] + toks:
+                mine = keys[keys <= p]
+                if lay.cls[slot] == LOCAL:
+                    mine = mine[mine > p - lay.window[slot]]
+                want = tpos[otab.visible(int(lay.cls[slot]), int(lay.window[slot]), listed, tpos, tsp, tnew, int(p))]
+                assert np.array_equal(np.sort(mine), np.sort(want)), (call, row, int(p))
