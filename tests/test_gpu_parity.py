@@ -649,3 +649,67 @@ def test_workspace_contents_do_not_matter(fill):
     d = w.decode()[0]
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(d, d_ref)
+
+
+# ---------------------------------------------------------------- edge cases
+
+def test_empty_calls_write_nothing():
+    """A relocation list of length 0 and a prefill call with no query tokens are
+    valid no-ops: SP_OK, and the outputs keep what they held."""
+    import head_aware_paged_page_amd.segpaged as sp
+    lay = _small(2)
+    w = _wl(lay)
+    before = w.k_reloc.clone()
+    sp.rope_relocate(w.k_pool, w.k_reloc, w.ps, w.d_reloc[:0], lay.theta)
+    zero_tok = np.zeros(lay.n_seq + 1, np.int32)
+    out = torch.full_like(w.q_prefill[:1], 7.0)
+    lse = torch.full((1, w.Hq), 7.0, dtype=torch.float32, device="cuda")
+    sp.prefill(w.q_prefill[:1], w.k_pool, w.v_pool, page_size=w.ps, group=w.G, n_seq=lay.n_seq, n_slot=lay.n_slot,
+               h_tok_ptr=zero_tok, h_row_ptr=w.tp["row_ptr"], d_tok_ptr=torch.from_numpy(zero_tok).cuda(),
+               d_q_pos0=w.d_q_pos0, d_cls=w.d_cls, d_window=w.d_window, d_row_ptr=w.p_row_ptr,
+               d_entries=w.p_entries, scale=w.scale, out=out, lse=lse, workspace=w.workspace)
+    torch.cuda.synchronize()
+    # unwritten pool pages hold NaN: compare bit patterns
+    assert torch.equal(w.k_reloc.view(torch.int16), before.view(torch.int16))
+    assert bool((out.float() == 7.0).all()) and bool((lse == 7.0).all())
+
+
+def test_sequence_without_query_tokens():
+    """Two sequences, query tokens for the second only (tok_ptr = [0, 0, n]):
+    the first sequence's rows have no work items, the second matches the oracle."""
+    import head_aware_paged_page_amd.segpaged as sp
+    lay = _small(1)                                   # two sequences, G = 8
+    w = _wl(lay)
+    n = lay.n_prefill
+    tok = np.asarray([0, 0, n], np.int32)
+    q = w.q_prefill[n:2 * n].contiguous()
+    out, lse = torch.empty_like(q), torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    nb = sp.workspace_bytes(sp.SP_WS_PREFILL, sp.SP_BF16, w.D, w.ps, w.G, lay.n_seq, lay.n_slot, tok,
+                            w.tp["row_ptr"])
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    sp.prefill(q, w.k_pool, w.v_pool, page_size=w.ps, group=w.G, n_seq=lay.n_seq, n_slot=lay.n_slot, h_tok_ptr=tok,
+               h_row_ptr=w.tp["row_ptr"], d_tok_ptr=torch.from_numpy(tok).cuda(), d_q_pos0=w.d_q_pos0,
+               d_cls=w.d_cls, d_window=w.d_window, d_row_ptr=w.p_row_ptr, d_entries=w.p_entries, scale=w.scale,
+               out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    for slot in range(lay.n_slot):
+        K, V = w.unit_host(slot, 1)
+        heads = slice(slot * lay.group, (slot + 1) * lay.group)
+        O, L, _ = oatt.row_attention(lay, slot, 1, K, V, _host(q[:, heads]), lay.new_base[1] + np.arange(n))
+        assert np.max(np.abs(_host(out[:, heads]) - O)) <= TOL["bf16"]
+        assert np.max(np.abs(lse[:, heads].double().cpu().numpy() - L)) <= TOL["bf16"]
+
+
+def test_retrieval_head_with_no_listed_page():
+    """A retrieval head whose list is empty sees only the new tokens (causally):
+    its table holds only new-token pages, and prefill and decode match the oracle."""
+    lay = custom_layout(seg_lens=[[300, 90]], offline=[[0, 11]], n_prefill=40, n_decode=1,
+                        classes=[(RETRIEVAL, 0), (GLOBAL, 0)], page_size=16, head_dim=128, group=4, dtype="bf16",
+                        ret_lists={(0, 0): []}, name="ret_empty")
+    w = _wl(lay)
+    ent = w.tp["entries"][w.tp["row_ptr"][0]:w.tp["row_ptr"][1]]
+    assert np.all(ent[:, 1] >= lay.new_base[0])       # new-token pages only
+    w.prefill()
+    check_prefill(w)
+    w.decode()
+    check_decode(w)
