@@ -81,6 +81,11 @@ MAX_REPLICA_BYTES = 24 << 30     # pools of all replicas together
 MIN_ROTATION_BYTES = 1 << 30     # replicas together at least this large (4x the last-level cache)
 MAX_REPLICAS = 16                # (a workload of a few MB, the tiny one, stops here)
 MAX_CPU_QUERIES = 128            # query tokens per row the oracle baseline runs (evenly spaced)
+# After the W warm-up steps, untimed steps go on until this much wall time has
+# passed: an idle MI355X runs its first tens of milliseconds of matrix work at
+# a lower engine clock (about 1.9 GHz against 2.4 for matrix work alone), so
+# the timed steps start from the clocks of a GPU that has been busy.
+CLOCK_SETTLE_S = 0.3
 from head_aware_paged_page_amd.profiling import source_hash  # noqa: E402
 
 
@@ -325,9 +330,17 @@ def run_config(name, seed, steps, warmup, log, window_only=False):
             ev[3].record(stream)
 
     stream = torch.cuda.current_stream()
+    t_warm = time.perf_counter()
     for i in range(max(warmup, n_rep)):
         calls(i)
     torch.cuda.synchronize()
+    n_settle = 0
+    while time.perf_counter() - t_warm < CLOCK_SETTLE_S:
+        for _ in range(8):
+            calls(n_settle)
+            n_settle += 1
+        torch.cuda.synchronize()
+    log(f"warm-up: {max(warmup, n_rep)} steps, then {n_settle} more until {CLOCK_SETTLE_S} s had passed")
     ev = [[HipEvent() for _ in range(4)] for _ in range(steps)]
     gc.collect()
     gc.disable()          # a collection inside the timed loop would stall the launches
@@ -466,7 +479,7 @@ def run_config(name, seed, steps, warmup, log, window_only=False):
         "chain_pages": int(len(w.tp["storage"])),
         "config": {"workload": f"{name}: {WORKLOAD_TEXT[name]}", "seed": seed, "slots": lay.n_slot,
                    "sequences": lay.n_seq, "prefill_tokens": int(w.h_tok_ptr[-1]), "decode_tokens": lay.n_seq,
-                   "pool_replicas": n_rep},
+                   "pool_replicas": n_rep, "settle_steps": n_settle},
         "roofline": roof, "calls": calls_out,
         "beyond_step": {"pack_pages": {"ms": round(t_pack, 4), "GB/s": round(pack_bytes / t_pack / 1e6, 1),
                                        "frac_hbm": round(pack_bytes / t_pack / 1e-3 / PEAK_HBM, 4),
