@@ -44,17 +44,19 @@ KERNELS = [
     ("importance_reduce_kernel", "segpaged_token_importance", "importance_reduce_kernel"),
     ("importance_plan_kernel", "segpaged_token_importance", "importance_plan_kernel"),
     ("fill_zero_kernel", "segpaged_token_importance", "fill_zero_kernel"),
+    ("importance_f32_kernel", "segpaged_token_importance", "importance_f32_kernel"),
+    ("layer_score_kernel", "segpaged_select_tokens", "layer_score_kernel"),
     ("select_kernel", "segpaged_select_tokens", "select_kernel"),
 ]
 # The sources a call's kernel timings and traffic depend on: its kernels and the
 # host runtime, whose planner sets split counts and launch shapes.
 KERNEL_SOURCES = {
-    "rope_relocate": ["relocate.hip", "runtime.cpp", "internal.hpp"],
+    "rope_relocate": ["relocate.hip", "device_common.hpp", "runtime.cpp", "internal.hpp"],
     "segpaged_prefill": ["prefill.hip", "device_common.hpp", "runtime.cpp", "internal.hpp"],
     "segpaged_decode": ["decode.hip", "device_common.hpp", "runtime.cpp", "internal.hpp"],
-    "segpaged_pack_pages": ["pack.hip", "runtime.cpp", "internal.hpp"],
+    "segpaged_pack_pages": ["pack.hip", "device_common.hpp", "runtime.cpp", "internal.hpp"],
     "segpaged_token_importance": ["importance.hip", "device_common.hpp", "runtime.cpp", "internal.hpp"],
-    "segpaged_select_tokens": ["importance.hip", "runtime.cpp", "internal.hpp"],
+    "segpaged_select_tokens": ["importance.hip", "device_common.hpp", "runtime.cpp", "internal.hpp"],
 }
 
 
@@ -121,7 +123,7 @@ def summarize(a) -> None:
                 f"python3 -m head_aware_paged_page_amd.profiling copy --mib {a.copy_mib}")
     lines = [f"# Kernel time, workload {a.workload} (rocprofv3 kernel trace, --stats)", "",
              "command (from the repository root, on one MI355X):", f"  {bench_cmd}", "",
-             "The run holds warm-up, the zero-query pass that counts visible keys, and 10 timed steps.", "",
+             "The run holds the warm-up (2 steps, then untimed steps until 0.3 s have passed), the zero-query", "pass that counts visible keys, and 10 timed steps; the averages cover every call.", "",
              f"{'kernel':28s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
     by_short = {}
     for r in stats:
