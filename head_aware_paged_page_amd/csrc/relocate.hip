@@ -8,8 +8,9 @@
 // delta * w_i.  The angle is formed and reduced modulo 2*pi in fp64, its
 // sine/cosine taken in fp64 and the rotation applied in fp32.
 //
-// HBM-bound streaming: a workgroup takes a run of 4 list items (staged in LDS)
-// and issues all their loads at once (streaming, non-temporal loads and stores:
+// HBM-bound streaming: a workgroup takes a run of list items worth 16 KB of
+// keys (4 pages of 16 bf16 keys of 128 dims; staged in LDS) and issues all
+// their loads at once (streaming, non-temporal loads and stores:
 // every byte is touched once; the table builder lists pages in address order,
 // so a run is mostly one contiguous stretch of the pool).  While the loads are
 // in flight it builds one (cos, sin) table of D/2 angles per distinct delta of
@@ -21,7 +22,14 @@ namespace sp {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPagesPerBlock = 4;
+constexpr int kBlockKeyBytes = 16384;   // keys one workgroup moves (timed best on MI355X at page 16 and 32)
+
+// Pages per workgroup: kBlockKeyBytes of keys when the page shape is known at
+// compile time (PS, DD > 0), else 4.
+template <typename T, int PS, int DD>
+constexpr int pages_per_block() {
+    return (PS && DD) ? (kBlockKeyBytes / (PS * DD * (int)sizeof(T)) > 0 ? kBlockKeyBytes / (PS * DD * (int)sizeof(T)) : 1) : 4;
+}
 constexpr int kBatch = 4;             // units per thread with loads in flight together
 constexpr int kMaxHalf = 128;         // head_dim / 2
 constexpr double kTwoPiHi = 6.283185307179586232;      // 2*pi rounded to fp64
@@ -69,7 +77,7 @@ struct Elem<bf16> {
 
 // PS / DD = 0: page size / head dim taken from the arguments (any legal value);
 // otherwise compile-time, so the index arithmetic is shifts and masks.
-template <typename T, int PS, int DD>
+template <typename T, int PS, int DD, int kPagesPerBlock = pages_per_block<T, PS, DD>()>
 __global__ __launch_bounds__(kThreads) void relocate_kernel(const T *__restrict__ k_in, T *k_out, int ps_arg,
                                                             int D_arg, int64_t n_phys, int n,
                                                             const int4 *__restrict__ list, double log2_theta) {
@@ -174,13 +182,15 @@ int launch_relocate(const void *k_in, void *k_out, int dtype, int page_size, int
                     const sp_reloc *d_list, double theta, hipStream_t stream) {
     if (kThreads % (head_dim / 16) != 0)
         return fail(SP_EUNSUPPORTED, "rope_relocate head_dim %d (a power of two, 16..256)", head_dim);
-    const int64_t blocks = (n + kPagesPerBlock - 1) / kPagesPerBlock;
-    if (blocks > INT32_MAX) return fail(SP_EINVAL, "relocation list too long");
     const double l2t = log2(theta);
-    const dim3 grid((unsigned)blocks), block(kThreads);
-#define SP_RELOC(T, PSV, DV)                                                                                \
-    hipLaunchKernelGGL((relocate_kernel<T, PSV, DV>), grid, block, 0, stream, (const T *)k_in, (T *)k_out, \
-                       page_size, head_dim, n_phys, n, (const int4 *)d_list, l2t)
+    const dim3 block(kThreads);
+#define SP_RELOC(T, PSV, DV)                                                                                   \
+    do {                                                                                                       \
+        constexpr int ppb = pages_per_block<T, PSV, DV>();                                                    \
+        const dim3 grid((unsigned)((n + ppb - 1) / ppb));                                                      \
+        hipLaunchKernelGGL((relocate_kernel<T, PSV, DV>), grid, block, 0, stream, (const T *)k_in, (T *)k_out, \
+                           page_size, head_dim, n_phys, n, (const int4 *)d_list, l2t);                        \
+    } while (0)
 #define SP_RELOC_SHAPES(T)                                                                   \
     if (head_dim == 128 && page_size == 16) SP_RELOC(T, 16, 128);                           \
     else if (head_dim == 128 && page_size == 32) SP_RELOC(T, 32, 128);                      \
