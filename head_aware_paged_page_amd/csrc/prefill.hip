@@ -521,7 +521,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (n_it == 0 && tid == 0) ticket = ticket_issue(P.work_ctr);
         if (grp == 0) {
             const int i_ticket = max(0, n_it - 2);
-            for (int i = 0; i < n_it; ++i) {
+            auto step0 = [&](int i) {
                 if (i == i_ticket && tid == 0) ticket = ticket_issue(P.work_ctr);
                 const int4 e = eread_lds(i + 2);                 // lands during the matrix phase
                 mphase(i);
@@ -529,9 +529,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 vphase(i, i, e);
                 __builtin_amdgcn_sched_barrier(0);
                 sync(i);
+            };
+            // unrolled by the ring size, so that every stage index is a constant
+            for (int j = 0; j < n_it; j += NBUF) {
+                step0(j);
+                if (j + 1 < n_it) step0(j + 1);
+                if (j + 2 < n_it) step0(j + 2);
+                if (j + 3 < n_it) step0(j + 3);
             }
         } else {
-            for (int i = 0; i < n_it; ++i) {
+            auto step1 = [&](int i) {
                 const int pm = (flr >> (8 * (i % NBUF) + 1)) & 0x7f;
                 if (i < n_tiles && pm) fixup(i % NBUF, pm, 4 * 64, 4 * 64);   // before P.V(i), one iteration on
                 vphase(i, i - 1, eread_lds(i + 2));
@@ -539,6 +546,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 mphase(i);
                 __builtin_amdgcn_sched_barrier(0);
                 sync(i);
+            };
+            for (int j = 0; j < n_it; j += NBUF) {
+                step1(j);
+                if (j + 1 < n_it) step1(j + 1);
+                if (j + 2 < n_it) step1(j + 2);
+                if (j + 3 < n_it) step1(j + 3);
             }
         }
 
