@@ -305,7 +305,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         // (P.V of the previous tile, then S = K Q^T of the next) while the other
         // group runs the softmax of its current tile on the vector ALUs, and the
         // roles swap every phase.  Each SIMD thus has one wave feeding its
-        // matrix cores and one keeping its vector ALUs busy at all times.
+        // matrix cores and one keeping its vector ALUs busy at all times; the
+        // wave in its matrix phase runs at a raised priority (s_setprio), so
+        // that its matrix instructions issue ahead of the other's vector work.
         //   group 0: phase 2j   = MFMA(j): PV(j-1), QK(j);  phase 2j+1 = softmax(j)
         //   group 1: phase 2j+1 = MFMA(j);                  phase 2j+2 = softmax(j)
         // Tile m is issued in phase 2m-4 by group 1 and 2m-3 by group 0 (tiles
@@ -524,8 +526,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             auto step0 = [&](int i) {
                 if (i == i_ticket && tid == 0) ticket = ticket_issue(P.work_ctr);
                 const int4 e = eread_lds(i + 2);                 // lands during the matrix phase
+                __builtin_amdgcn_s_setprio(2);                   // matrix issue first on the SIMD
                 mphase(i);
                 __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_setprio(0);
                 vphase(i, i, e);
                 __builtin_amdgcn_sched_barrier(0);
                 sync(i);
@@ -543,8 +547,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 if (i < n_tiles && pm) fixup(i % NBUF, pm, 4 * 64, 4 * 64);   // before P.V(i), one iteration on
                 vphase(i, i - 1, eread_lds(i + 2));
                 __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_setprio(2);
                 mphase(i);
                 __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_setprio(0);
                 sync(i);
             };
             for (int j = 0; j < n_it; j += NBUF) {

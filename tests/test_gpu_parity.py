@@ -193,6 +193,7 @@ SMALL = [
     (2, 64, 64, [[129, 700]], 33, [(GLOBAL, 0), (LOCAL, 65)]),
     (16, 128, 16, [[17]], 9, [(GLOBAL, 0), (LOCAL, 5)]),
     (3, 128, 16, [[450], [90, 91]], 40, [(LOCAL, 64), (GLOBAL, 0)]),
+    (4, 128, 64, [[700, 65], [130]], 50, [(GLOBAL, 0), (LOCAL, 100)]),
 ]
 
 
@@ -213,8 +214,10 @@ def _small(i, dtype="bf16", seed=0):
 @pytest.mark.parametrize("i", range(len(SMALL)))
 def test_small_layouts_bf16(i):
     lay = _small(i)
-    if lay.page_size == 64:
+    if lay.page_size == 64:                 # decode takes pages of 16 and 32 keys
         w = _wl(lay)
+        w.relocate()
+        check_relocate(w)
         w.prefill()
         check_prefill(w)
         return
