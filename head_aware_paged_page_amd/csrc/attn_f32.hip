@@ -3,8 +3,12 @@
 // Same computation as the bf16 kernels - softmax attention of each query over
 // the tokens its head's page table and class make visible (RedKnot product
 // profile, section 3) - with fp32 inputs, fp32 arithmetic and fp32 outputs and
-// no reduced precision anywhere.  One wave per (query token, query head); keys
-// are visited in table order with a running (max, sum) softmax.
+// no reduced precision anywhere.  One wave per (query token, query head) walks
+// the head's table a page at a time: lane t scores key t of the page (the
+// query from LDS, the key row read as float4s), the wave takes the page's max
+// and weights, and lane d then accumulates output dims d, d + 64, ... over the
+// page's keys from the dim-major value page.  The page's K and V loads are
+// issued together; a running (max, sum) carries the softmax across pages.
 #include "device_common.hpp"
 
 namespace sp {
@@ -26,8 +30,18 @@ __device__ __forceinline__ float wave_sum(float v) {
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
     return v;
 }
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+constexpr int kF32MaxDim = 256;
+constexpr int kF32MaxPage = 64;
 
 __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params P) {
+    __shared__ __attribute__((aligned(16))) float sq[kF32MaxDim];
+    __shared__ float sw[kF32MaxPage];
     const int lane = threadIdx.x;
     const int tok = blockIdx.x, head = blockIdx.y;
     const int slot = head / P.G;
@@ -50,43 +64,55 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params P) {
     const int low = is_local ? p - P.window[slot] : INT32_MIN;   // visible iff low < pos <= p
     const int D = P.D, ps = P.ps;
 
-    float qv[4], o[4];
     const float *qrow = P.q + ((int64_t)tok * P.Hq + head) * D;
+    for (int d = lane; d < D; d += 64) sq[d] = qrow[d];
+    __syncthreads();
+
+    float o[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int d = lane + 64 * i;
-        qv[i] = d < D ? qrow[d] : 0.f;
-        o[i] = 0.f;
-    }
+    for (int i = 0; i < 4; ++i) o[i] = 0.f;
     float m = -INFINITY, l = 0.f;
     for (int e = P.row_ptr[r]; e < P.row_ptr[r + 1]; ++e) {
         const int4 en = P.entries[e];
         if (en.x < 0 || en.x >= P.n_phys) continue;
         const int nv = min(en.z, ps);
-        if (en.y > p || en.y + nv - 1 <= low) continue;
-        for (int tk = 0; tk < nv; ++tk) {
-            const int pos = en.y + tk;
-            if (!(pos <= p && pos > low)) continue;
-            const float *krow = P.kp + ((int64_t)en.x * ps + tk) * D;
-            float part = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d = lane + 64 * i;
-                if (d < D) part = fmaf(qv[i], krow[d], part);
+        if (nv <= 0 || en.y > p || en.y + nv - 1 <= low) continue;
+        // score of key `lane` (lanes past the page's tokens or outside the window: -inf)
+        const int pos = en.y + lane;
+        const bool vis = lane < nv && pos <= p && pos > low;
+        float s = -INFINITY;
+        if (vis) {
+            const float4 *krow = (const float4 *)(P.kp + ((int64_t)en.x * ps + lane) * D);
+            const float4 *q4 = (const float4 *)sq;
+            float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+            for (int j = 0; j < D / 4; ++j) {
+                const float4 k = krow[j], qq = q4[j];
+                a0 = fmaf(qq.x, k.x, a0);
+                a1 = fmaf(qq.y, k.y, a1);
+                a2 = fmaf(qq.z, k.z, a2);
+                a3 = fmaf(qq.w, k.w, a3);
             }
-            const float s = wave_sum(part) * P.scale;
-            const float m_new = fmaxf(m, s);
-            const float alpha = expf(m - m_new);
-            const float w = expf(s - m_new);
-            l = l * alpha + w;
-            const float *vcol = P.vp + (int64_t)en.x * D * ps + tk;   // V page is dim-major
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d = lane + 64 * i;
-                if (d < D) o[i] = fmaf(w, vcol[(int64_t)d * ps], o[i] * alpha);
-            }
-            m = m_new;
+            s = ((a0 + a1) + (a2 + a3)) * P.scale;
         }
+        const float m_new = fmaxf(m, wave_max(s));
+        if (m_new == -INFINITY) continue;
+        const float alpha = expf(m - m_new);         // 0 while m is -inf
+        const float w = vis ? expf(s - m_new) : 0.f;
+        l = l * alpha + wave_sum(w);
+        if (lane < ps) sw[lane] = w;
+        __syncthreads();
+        const float *vpage = P.vp + (int64_t)en.x * D * ps;   // V page is dim-major: [D][ps]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d = lane + 64 * i;
+            if (d >= D) continue;
+            const float *vrow = vpage + (int64_t)d * ps;
+            float acc = 0.f;
+            for (int k = 0; k < nv; ++k) acc = fmaf(sw[k], vrow[k], acc);
+            o[i] = o[i] * alpha + acc;
+        }
+        __syncthreads();
+        m = m_new;
     }
     float *orow = P.out + ((int64_t)tok * P.Hq + head) * D;
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -99,7 +125,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params P) {
 }
 
 int launch_f32(const AttnArgs &a, int64_t n_tok, const int32_t *tok_ptr, hipStream_t stream) {
-    if (a.head_dim > 256) return fail(SP_EUNSUPPORTED, "fp32 head_dim %d > 256", a.head_dim);
+    if (a.head_dim > kF32MaxDim || a.head_dim % 4 != 0)
+        return fail(SP_EUNSUPPORTED, "fp32 head_dim %d (a multiple of 4, at most %d)", a.head_dim, kF32MaxDim);
+    if (a.page_size > kF32MaxPage) return fail(SP_EUNSUPPORTED, "fp32 page_size %d > %d", a.page_size, kF32MaxPage);
     if (n_tok > INT32_MAX) return fail(SP_EINVAL, "too many query tokens");
     F32Params P;
     P.q = (const float *)a.q;
