@@ -4,11 +4,11 @@
 // the tokens its head's page table and class make visible (RedKnot product
 // profile, section 3) - with fp32 inputs, fp32 arithmetic and fp32 outputs and
 // no reduced precision anywhere.  One wave per (query token, query head) walks
-// the head's table a page at a time: lane t scores key t of the page (the
-// query from LDS, the key row read as float4s), the wave takes the page's max
-// and weights, and lane d then accumulates output dims d, d + 64, ... over the
-// page's keys from the dim-major value page.  The page's K and V loads are
-// issued together; a running (max, sum) carries the softmax across pages.
+// the head's table a page (at most 64 keys) at a time: lane t scores key t of
+// the page (the query from LDS, the key row read as float4s), the wave takes
+// the page's max and weights, and lane d then accumulates output dims d,
+// d + 64, ... over the page's keys from the dim-major value page.  A running
+// (max, sum) carries the softmax across pages.
 #include "device_common.hpp"
 
 namespace sp {
@@ -37,11 +37,11 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 constexpr int kF32MaxDim = 256;
-constexpr int kF32MaxPage = 64;
 
+template <bool LONG_PAGES>
 __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params P) {
     __shared__ __attribute__((aligned(16))) float sq[kF32MaxDim];
-    __shared__ float sw[kF32MaxPage];
+    __shared__ float sw[64];
     const int lane = threadIdx.x;
     const int tok = blockIdx.x, head = blockIdx.y;
     const int slot = head / P.G;
@@ -77,42 +77,46 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params P) {
         if (en.x < 0 || en.x >= P.n_phys) continue;
         const int nv = min(en.z, ps);
         if (nv <= 0 || en.y > p || en.y + nv - 1 <= low) continue;
-        // score of key `lane` (lanes past the page's tokens or outside the window: -inf)
-        const int pos = en.y + lane;
-        const bool vis = lane < nv && pos <= p && pos > low;
-        float s = -INFINITY;
-        if (vis) {
-            const float4 *krow = (const float4 *)(P.kp + ((int64_t)en.x * ps + lane) * D);
-            const float4 *q4 = (const float4 *)sq;
-            float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-            for (int j = 0; j < D / 4; ++j) {
-                const float4 k = krow[j], qq = q4[j];
-                a0 = fmaf(qq.x, k.x, a0);
-                a1 = fmaf(qq.y, k.y, a1);
-                a2 = fmaf(qq.z, k.z, a2);
-                a3 = fmaf(qq.w, k.w, a3);
+        // the page's keys 64 at a time: score of key k0 + lane (lanes past the
+        // page's tokens or outside the window: -inf)
+        for (int k0 = 0; k0 < (LONG_PAGES ? nv : 1); k0 += 64) {   // pages of at most 64 keys: one pass
+            const int kk = k0 + lane, kn = LONG_PAGES ? min(nv - k0, 64) : nv;
+            const int pos = en.y + kk;
+            const bool vis = kk < nv && pos <= p && pos > low;
+            float s = -INFINITY;
+            if (vis) {
+                const float4 *krow = (const float4 *)(P.kp + ((int64_t)en.x * ps + kk) * D);
+                const float4 *q4 = (const float4 *)sq;
+                float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+                for (int j = 0; j < D / 4; ++j) {
+                    const float4 k = krow[j], qq = q4[j];
+                    a0 = fmaf(qq.x, k.x, a0);
+                    a1 = fmaf(qq.y, k.y, a1);
+                    a2 = fmaf(qq.z, k.z, a2);
+                    a3 = fmaf(qq.w, k.w, a3);
+                }
+                s = ((a0 + a1) + (a2 + a3)) * P.scale;
             }
-            s = ((a0 + a1) + (a2 + a3)) * P.scale;
-        }
-        const float m_new = fmaxf(m, wave_max(s));
-        if (m_new == -INFINITY) continue;
-        const float alpha = expf(m - m_new);         // 0 while m is -inf
-        const float w = vis ? expf(s - m_new) : 0.f;
-        l = l * alpha + wave_sum(w);
-        if (lane < ps) sw[lane] = w;
-        __syncthreads();
-        const float *vpage = P.vp + (int64_t)en.x * D * ps;   // V page is dim-major: [D][ps]
+            const float m_new = fmaxf(m, wave_max(s));
+            if (m_new == -INFINITY) continue;
+            const float alpha = expf(m - m_new);         // 0 while m is -inf
+            const float w = vis ? expf(s - m_new) : 0.f;
+            l = l * alpha + wave_sum(w);
+            sw[lane] = w;
+            __syncthreads();
+            const float *vpage = P.vp + (int64_t)en.x * D * ps + k0;   // V page is dim-major: [D][ps]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int d = lane + 64 * i;
-            if (d >= D) continue;
-            const float *vrow = vpage + (int64_t)d * ps;
-            float acc = 0.f;
-            for (int k = 0; k < nv; ++k) acc = fmaf(sw[k], vrow[k], acc);
-            o[i] = o[i] * alpha + acc;
+            for (int i = 0; i < 4; ++i) {
+                const int d = lane + 64 * i;
+                if (d >= D) continue;
+                const float *vrow = vpage + (int64_t)d * ps;
+                float acc = 0.f;
+                for (int k = 0; k < kn; ++k) acc = fmaf(sw[k], vrow[k], acc);
+                o[i] = o[i] * alpha + acc;
+            }
+            __syncthreads();
+            m = m_new;
         }
-        __syncthreads();
-        m = m_new;
     }
     float *orow = P.out + ((int64_t)tok * P.Hq + head) * D;
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -127,7 +131,6 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params P) {
 int launch_f32(const AttnArgs &a, int64_t n_tok, const int32_t *tok_ptr, hipStream_t stream) {
     if (a.head_dim > kF32MaxDim || a.head_dim % 4 != 0)
         return fail(SP_EUNSUPPORTED, "fp32 head_dim %d (a multiple of 4, at most %d)", a.head_dim, kF32MaxDim);
-    if (a.page_size > kF32MaxPage) return fail(SP_EUNSUPPORTED, "fp32 page_size %d > %d", a.page_size, kF32MaxPage);
     if (n_tok > INT32_MAX) return fail(SP_EINVAL, "too many query tokens");
     F32Params P;
     P.q = (const float *)a.q;
@@ -148,7 +151,9 @@ int launch_f32(const AttnArgs &a, int64_t n_tok, const int32_t *tok_ptr, hipStre
     P.D = a.head_dim;
     P.n_phys = a.n_phys;
     P.scale = a.scale;
-    hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)n_tok, (unsigned)P.Hq), dim3(64), 0, stream, P);
+    const dim3 grid((unsigned)n_tok, (unsigned)P.Hq);
+    if (a.page_size > 64) hipLaunchKernelGGL(attn_f32_kernel<true>, grid, dim3(64), 0, stream, P);
+    else hipLaunchKernelGGL(attn_f32_kernel<false>, grid, dim3(64), 0, stream, P);
     return check_hip(hipGetLastError(), "fp32 attention launch");
 }
 

@@ -242,6 +242,22 @@ def test_small_layouts_fp32(i):
     check_decode(w)
 
 
+def test_fp32_pages_longer_than_a_wave():
+    """fp32 attention over pages of 128 keys (the kernel scores a page 64 keys
+    at a time) and of 64 keys, against the oracle."""
+    for ps, lens, npf in ((128, [[300, 70]], 20), (64, [[129, 700]], 33)):
+        lay = custom_layout(seg_lens=lens, offline=[[17, -900]], n_prefill=npf, n_decode=1,
+                            classes=[(GLOBAL, 0), (LOCAL, 90)], page_size=ps, head_dim=64, group=2, dtype="f32",
+                            ret_lists={}, name=f"f32_ps{ps}", seed=3)
+        w = _wl(lay)
+        w.relocate()
+        check_relocate(w)
+        w.prefill()
+        check_prefill(w)
+        w.decode()
+        check_decode(w)
+
+
 def test_visible_counts_from_zero_queries():
     """Q = 0 makes every visible score 0: weights are exactly 1, so exp(LSE) is the
     visible count (exact in fp32 below 2^24) and the output is the mean of V."""
