@@ -213,3 +213,18 @@ def test_select_tokens_32k_end_to_end():
         lo_taken, hi_left = ref[taken].min(), ref[~taken].max()
         slack = REL["bf16"] * max(lo_taken, hi_left) + 8 * ABS["bf16"]
         assert hi_left <= lo_taken + slack, (l, hi_left, lo_taken)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_importance_random_layouts(seed):
+    """The seeded random layouts of the whole-path test (every class, windows,
+    retrieval lists, a sequence without a reused segment, several q-tiles):
+    every row against the oracle, and every slot's sums."""
+    from test_random_layouts_gpu import _draw
+    lay = _draw(seed)
+    w = _wl(lay)
+    w.prefill()
+    imp, pos_ptr = w.importance()
+    check_row_sums(w, imp)
+    worst = check_importance(w, imp, pos_ptr)
+    print(f"[importance] {lay.name}: worst error {worst:.3f} of its bound")
