@@ -135,3 +135,28 @@ def test_decode_loop_releases_pages_as_the_window_slides():
     end = [E + lay.n_new]                               # the sequence is over: everything returns
     rel = sp.release_pages(**w.layout_args, page_size=ps, p_next=end, chain_ptr=chain_ptr, storage=storage)
     assert n_released + len(rel) == int((w.tp["storage"] >= 0).sum()) and (storage == -1).all()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_window_only_random_layouts(seed):
+    """The seeded random layouts of the whole-path test with window-only storage:
+    prefill and decode bit-identical to whole-chain storage, and the stored
+    keys' relocation identical too."""
+    from test_random_layouts_gpu import _draw
+    lay = _draw(seed)
+    full = _wl(lay)
+    win = _wl(lay, window_only=True)
+    assert win.n_phys <= full.n_phys
+    for w in (full, win):
+        w.relocate()
+        w.prefill(k=w.k_reloc)
+        w.decode(k=w.k_reloc)
+    torch.cuda.synchronize()
+    assert torch.equal(full.out_prefill, win.out_prefill) and torch.equal(full.lse_prefill, win.lse_prefill)
+    assert torch.equal(full.out_decode, win.out_decode) and torch.equal(full.lse_decode, win.lse_decode)
+    for slot in range(lay.n_slot):
+        for seq in range(lay.n_seq):
+            a = win.gather_keys(win.k_reloc, slot, seq)
+            b = full.gather_keys(full.k_reloc, slot, seq)
+            stored = ~np.isnan(a[:, 0])
+            assert np.array_equal(a[stored], b[stored]), (slot, seq)
