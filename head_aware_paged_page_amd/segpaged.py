@@ -13,7 +13,10 @@ import os
 
 import numpy as np
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libsegpaged.so")
+# SEGPAGED_LIB overrides the library path (for instance a build with the host
+# code instrumented by AddressSanitizer).
+_LIB_PATH = os.environ.get("SEGPAGED_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib",
+                                                           "libsegpaged.so")
 
 SP_OK, SP_EINVAL, SP_ENOMEM, SP_EHIP, SP_EUNSUPPORTED, SP_EWORKSPACE = 0, -1, -2, -3, -4, -5
 SP_GLOBAL, SP_LOCAL, SP_RETRIEVAL, SP_DENSE = 0, 1, 2, 3
