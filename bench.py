@@ -9,7 +9,9 @@ resident in HBM before the timed region:
   segpaged_decode  one decode token per sequence over every slot
 The page tables are built once beforehand by segpaged_build_tables on the
 host; its time is reported separately (build_tables), as is the host-side
-launch planning inside each prefill and decode call (plan_host_ms).
+launch planning inside each prefill and decode call (plan_host_ms).  Before
+the K timed steps: W warm-up steps, then untimed steps until 0.3 s have
+passed (settle_steps), so that timing starts from a busy GPU's clocks.
 
 Cache-clean timing.  The chip's last-level cache (256 MB) could serve a call
 data that the previous call just read (decode reads the global slots' pages
