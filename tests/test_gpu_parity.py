@@ -25,9 +25,9 @@ TOL = {"f32": 1e-5, "bf16": 2e-2}
 
 def lse_tol(dtype, L):
     """The output bound holds for the log-sum-exp output too: max abs 2e-2 for bf16
-    inputs; for fp32 inputs 1e-5 relative to |LSE| (at least 1e-5), since LSE is
-    formed as m + log l in fp32."""
-    return TOL["bf16"] if dtype == "bf16" else 1e-5 * max(1.0, float(np.max(np.abs(L))))
+    inputs, 1e-5 for fp32 inputs (measured about 1e-6 at |LSE| up to 8: the fp32
+    m + log l keeps about seven digits)."""
+    return TOL[dtype]
 
 
 def _wl(lay, **kw):
