@@ -14,12 +14,12 @@
 // keeps one 32-key tile of K in registers (B operand of
 // v_mfma_f32_32x32x16_bf16, S = Q K^T) and streams the q-tile's query rows
 // from LDS (A operand), 32 rows at a time.  The accumulator enters each
-// product holding -lse (log2 units), so a score leaves the matrix core as
-// log2 of its probability; one exp2 and one add per (row, key) then fold the
-// probability into the lane's key column, and the two lane halves that hold
-// one key combine at the end.  Queries are held pre-multiplied by
-// scale * log2(e) and rounded to bf16 exactly as the prefill does, so the
-// probabilities of a row sum to one against the prefill's lse.  Items are
+// product holding -lse / scale, so a score leaves the matrix core as
+// q.k - lse / scale; one multiply by scale * log2(e), one exp2 and one add per
+// (row, key) then fold the probability into the lane's key column, and the
+// two lane halves that hold one key combine at the end.  The queries are used
+// as given, as in the prefill, so the probabilities of a row sum to one
+// against the prefill's lse to fp32 rounding.  Items are
 // (row, q-tile, chunk of 1024 keys); a row with several q-tiles writes one
 // partial column per q-tile and a second kernel sums them in q-tile order, so
 // every result is computed in one fixed order (bit-reproducible).
@@ -114,20 +114,19 @@ __global__ __launch_bounds__(IW * 64) void importance_bf16_kernel(ImpParams P, I
     }
     if (my_hi <= my_lo) return;
 
-    // ---- the q-tile's rows (token, head), pre-scaled by scale * log2(e) and
-    // rounded to bf16 as the prefill does, and their -lse in log2 units
+    // ---- the q-tile's rows (token, head) as given (the prefill does not round
+    // them either), and their -lse / scale: a score then enters the MFMA
+    // accumulator as q.k - lse / scale, and c = scale * log2(e) times it is the
+    // log2 of the probability
+    const float cl = P.scale_log2;
     {
-        const float cl = P.scale_log2;
         constexpr int CPR = D / 8;   // 16-byte chunks per row
         for (int idx = tid; idx < IQ * CPR; idx += IW * 64) {
             const int row = idx / CPR, c = idx % CPR;
             u32x4 w = u32x4{0, 0, 0, 0};
             if (row < nrows) {
                 const int tq = row / G, g = row % G;
-                const u32x4 x = *(const u32x4 *)(P.q + ((int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g) * D + 8 * c);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w[e] = pack_bf16x2(bf16_bits_to_f32(x[e] & 0xffffu) * cl, bf16_bits_to_f32(x[e] >> 16) * cl);
+                w = *(const u32x4 *)(P.q + ((int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g) * D + 8 * c);
             }
             sQ[sq_chunk<D>(row, c)] = w;
         }
@@ -135,7 +134,7 @@ __global__ __launch_bounds__(IW * 64) void importance_bf16_kernel(ImpParams P, I
             float nl = -INFINITY;   // rows past the q-tile: every probability 0
             if (row < nrows) {
                 const int tq = row / G, g = row % G;
-                nl = -P.lse[(int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g] * kLog2e;
+                nl = -P.lse[(int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * G + g] * kLog2e / cl;
             }
             sL[row] = nl;
         }
@@ -179,14 +178,14 @@ __global__ __launch_bounds__(IW * 64) void importance_bf16_kernel(ImpParams P, I
             float sum = 0.f;
             if (full) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f(acc[i]);
+                for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f(acc[i] * cl);
             } else {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int row = qb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
                     const int pq = p0 + row / G;
                     const bool vis = valid && pos <= pq && (!is_local || pos > pq - W);
-                    sum += vis ? __builtin_amdgcn_exp2f(acc[i]) : 0.f;
+                    sum += vis ? __builtin_amdgcn_exp2f(acc[i] * cl) : 0.f;
                 }
             }
             col += sum;

@@ -31,10 +31,6 @@ namespace sp {
 namespace {
 
 constexpr int BN = kPrefillKeysPerTile;   // 64 keys per tile
-#ifndef SP_QSCALE
-#define SP_QSCALE 1
-#endif
-constexpr bool kQScale = SP_QSCALE;
 
 struct PrefillParams {
     const bf16 *q, *kp, *vp;
@@ -164,17 +160,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int W = is_local ? P.window[slot] : 0;
         const int nrows = ntok * G;
 
-        // ---- queries of this wave: row = 32*wave + n -> (token, head), read
-        // now and scaled once the first tile loads are out
+        // ---- queries of this wave: row = 32*wave + n -> (token, head)
         const int row = 32 * wave + n;
         const bool row_ok = row < nrows;
         const int tq = row / G, g = row % G;
         const int pq = p0 + tq;                    // this lane's query position
         const int lowq = is_local ? pq - W : INT32_MIN;   // visible iff lowq < pos <= pq
         u32x4 qraw[DK];
-        // The queries are held pre-multiplied by c = scale * log2(e) (rounded
-        // to bf16 once), so the scores leave the matrix cores in the log2
-        // domain of the softmax.
+        // The queries enter the matrix cores as given; each score is scaled by
+        // c = scale * log2(e) into the log2 domain of the softmax in fp32 (one
+        // FMA with the reference shift).  Pre-multiplying q by c and rounding
+        // it to bf16 would save that FMA but add a rounding to every score
+        // that grows with |q.k|: at keys four times the unit scale it pushed
+        // the log-sum-exp error past 2e-2.
         const float cl = P.scale_log2;
         bf16x8 qf[DK];
         {
@@ -284,12 +282,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         };
 
         // ---- running softmax state (log2 domain) and O^T accumulators.  m_ref is
-        // the lane's reference max (-inf until the row's first visible key);
-        // negm holds -m_ref (0 while m_ref is -inf) broadcast over one MFMA
-        // accumulator, the input of the first k-step of S, so the scores arrive
-        // as x - m_ref with x = c * q.k.
+        // the lane's reference max (-inf until the row's first visible key).
         float m_ref = -INFINITY, l_run = 0.f;
-        f32x16 negm = f32x16{0};
         f32x16 acc[DT];
     #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{0};
@@ -330,7 +324,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     #pragma unroll
             for (int s = 0; s < DK; ++s)
     #pragma unroll
-                for (int kt = 0; kt < 2; ++kt) S[kt] = mfma32x32x16(a[s][kt], qf[s], s == 0 ? negm : S[kt]);
+                for (int kt = 0; kt < 2; ++kt) S[kt] = mfma32x32x16(a[s][kt], qf[s], s == 0 ? f32x16{0} : S[kt]);
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * AH, 0);       // reads of k-steps 0 .. AH-1
     #pragma unroll
             for (int i = 0; i < 2 * (DK - AH); ++i) {
@@ -361,7 +355,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             __builtin_amdgcn_sched_group_barrier(0x008, DT, 0);           // MFMAs of k-step 3
         };
         // Online softmax with a rarely moved reference (log2 domain).  The weights
-        // of a tile are exp2(x - m_ref) straight from the score registers; the
+        // of a tile are exp2(x - m_ref), x = c * q.k, formed in the score registers; the
         // reference only moves when one of them would exceed 2^16 (the lane's
         // sum of its weights exceeds 2^16, or is inf) or while the row has no
         // reference yet.  Only then are the scores formed again (the tile is
@@ -411,7 +405,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         auto softmax = [&](int st, bool full, f32x16 (&S)[2], u32x4 (&Pk)[4]) {
             if (!full) mask(st, S);
             const float m_fin = m_ref == -INFINITY ? 0.f : m_ref;
-            if (!kQScale) scale_shift(S, cl, -m_fin);
+            scale_shift(S, cl, -m_fin);                      // x - m_ref, x = c * q.k
             float rs = weights(S, Pk);
             if (__any(!(rs <= kMaxWeight) || m_ref == -INFINITY)) {
                 qk(st, S);                                   // the scores again
@@ -423,7 +417,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                     for (int v = 0; v < 16; ++v) m4[(kt * 16 + v) & 3] = fmaxf(m4[(kt * 16 + v) & 3], S[kt][v]);
                 float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
                 mx = fmaxf(mx, xor_lane(mx, 32));           // the row's other 32 keys
-                const float m_new = fmaxf(m_ref, kQScale ? mx + m_fin : mx * cl);
+                const float m_new = fmaxf(m_ref, mx * cl);
                 if (m_new != -INFINITY) {
                     // nothing is accumulated while m_ref is -inf
                     const float alpha = m_ref == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -431,18 +425,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
                     m_ref = m_new;
-                    if (kQScale) {
-    #pragma unroll
-                        for (int v = 0; v < 16; ++v) negm[v] = -m_new;
-                    }
                 }
                 const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-                if (kQScale) {
-    #pragma unroll
-                    for (int kt = 0; kt < 2; ++kt) S[kt] += m_fin - m_use;
-                } else {
-                    scale_shift(S, cl, -m_use);
-                }
+                scale_shift(S, cl, -m_use);
                 rs = weights(S, Pk);
             }
             l_run += rs;
@@ -460,13 +445,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 if (j < n_tiles) dmas(j, prep(j, j, e3[j]));
         }
     #pragma unroll
-        for (int s = 0; s < DK; ++s) {
-            u32x4 w;
-    #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                w[e] = pack_bf16x2(bf16_bits_to_f32(qraw[s][e] & 0xffffu) * cl, bf16_bits_to_f32(qraw[s][e] >> 16) * cl);
-            qf[s] = u4_as_bf16x8(kQScale ? w : qraw[s]);
-        }
+        for (int s = 0; s < DK; ++s) qf[s] = u4_as_bf16x8(qraw[s]);
         if (n_tiles > 0) {
             if (n_tiles > 2) wait_vmcnt<2 * IPW>();
             else if (n_tiles > 1) wait_vmcnt<IPW>();

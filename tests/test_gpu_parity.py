@@ -24,10 +24,11 @@ TOL = {"f32": 1e-5, "bf16": 2e-2}
 
 
 def lse_tol(dtype, L):
-    """The output bound holds for the log-sum-exp output too: max abs 2e-2 for bf16
-    inputs, 1e-5 for fp32 inputs (measured about 1e-6 at |LSE| up to 8: the fp32
-    m + log l keeps about seven digits)."""
-    return TOL[dtype]
+    """The log-sum-exp is formed from the scores in fp32 with no rounding of the
+    inputs beyond their own precision (the queries enter the matrix cores as
+    given): held to 1e-4 for bf16 inputs and 1e-5 for fp32 (about 1e-6 is
+    measured in both; the fp32 m + log l keeps about seven digits)."""
+    return {"bf16": 1e-4, "f32": 1e-5}[dtype]
 
 
 def _wl(lay, **kw):
@@ -60,7 +61,7 @@ def _seg_positions(lay, seq):
     return on, off
 
 
-def check_prefill(w, rows=None, q_sample=None, k_pool=None, keys_fn=None):
+def check_prefill(w, rows=None, q_sample=None, k_pool=None, keys_fn=None, lse_bound=None):
     """Compare prefill outputs of the sampled rows (and query tokens) with the oracle."""
     lay = w.lay
     torch.cuda.synchronize()
@@ -83,11 +84,11 @@ def check_prefill(w, rows=None, q_sample=None, k_pool=None, keys_fn=None):
         worst = max(worst, err)
         assert np.all(np.isfinite(got)), f"row {r}: non-finite output"
         assert err <= TOL[lay.dtype], f"row {r} (class {lay.cls[slot]}): max abs err {err}"
-        assert np.max(np.abs(lse[t0 + toks, heads] - L)) <= lse_tol(lay.dtype, L)
+        assert np.max(np.abs(lse[t0 + toks, heads] - L)) <= (lse_bound or lse_tol(lay.dtype, L))
     return worst
 
 
-def check_decode(w, rows=None, keys_fn=None):
+def check_decode(w, rows=None, keys_fn=None, lse_bound=None):
     lay = w.lay
     torch.cuda.synchronize()
     out, lse = _host(w.out_decode), w.lse_decode.cpu().numpy()
@@ -104,7 +105,7 @@ def check_decode(w, rows=None, keys_fn=None):
         err = np.max(np.abs(got - O))
         assert np.all(np.isfinite(got)), f"row {r}: non-finite output"
         assert err <= TOL[lay.dtype], f"row {r} (class {lay.cls[slot]}): max abs err {err}"
-        assert np.max(np.abs(lse[seq:seq + 1, heads] - L)) <= lse_tol(lay.dtype, L)
+        assert np.max(np.abs(lse[seq:seq + 1, heads] - L)) <= (lse_bound or lse_tol(lay.dtype, L))
 
 
 def check_relocate(w, rows=None):
@@ -592,11 +593,14 @@ def test_end_to_end_32k():
         K = K.copy()
         K[:ctx] = orope.relocate(K[:ctx], off, on, lay.theta)
         return K
+    # The relocated keys the GPU hands to attention are rounded to bf16, the
+    # oracle's are not: the log-sum-exp inherits that input rounding, so it is
+    # held to the output bound here.
     w.relocate()
     w.prefill(k=w.k_reloc)
-    check_prefill(w, rows=rows, keys_fn=reloc_keys)
+    check_prefill(w, rows=rows, keys_fn=reloc_keys, lse_bound=TOL["bf16"])
     w.decode(k=w.k_reloc)
-    check_decode(w, rows=rows, keys_fn=reloc_keys)
+    check_decode(w, rows=rows, keys_fn=reloc_keys, lse_bound=TOL["bf16"])
 
 
 

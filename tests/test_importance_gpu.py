@@ -3,10 +3,10 @@
 segpaged_token_importance: each slot's importance of every position (the
 softmax probability mass the chunk's rows give it, with the prefill's lse)
 against oracle.importance.row_importance in fp64.  Bound: the device computes
-each probability from bf16 inputs with the queries pre-scaled and rounded to
-bf16 as in the prefill, so each probability (and a sum of them) is held to 2e-2
+each probability from bf16 inputs (the queries as given) against the
+prefill's log-sum-exp, so each probability (and a sum of them) is held to 2e-2
 relative, the bf16 bound, plus 1e-6 absolute; fp32 inputs to 1e-4 relative plus
-1e-7 (the fp32 log-sum-exp the prefill returns is itself held to 1e-5 |LSE|).
+1e-7 (the fp32 log-sum-exp the prefill returns is itself held to 1e-5).
 The probabilities of every row sum to 1, so each slot's importances sum to its
 number of query rows (checked on the GPU result alone).
 
