@@ -581,6 +581,22 @@ def test_out_of_pool_pages_are_empty():
     assert np.max(np.abs(lsed[0, :G].double().cpu().numpy() - l)) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("k_scale", [4.0, 8.0])
+def test_large_key_magnitudes(k_scale):
+    """Keys of standard deviation 4 and 8 against unit queries (logits of that
+    spread): outputs within the bf16 bound and the log-sum-exp within 1e-4,
+    which a query rounded after scaling (c * q to bf16) would not meet."""
+    lay = custom_layout(seg_lens=[[3000, 1000]], offline=[[0, -500]], n_prefill=64, n_decode=1,
+                        classes=[(GLOBAL, 0), (LOCAL, 256)], page_size=16, head_dim=128, group=4, dtype="bf16",
+                        k_scale=k_scale, name=f"kscale{k_scale:g}", seed=5)
+    w = _wl(lay)
+    w.prefill()
+    worst = check_prefill(w)
+    w.decode()
+    check_decode(w)
+    print(f"[kscale] {k_scale}: prefill worst output error {worst:.2e}")
+
+
 def test_end_to_end_32k():
     """GPU chain relocate -> prefill -> decode vs oracle relocation (fp64) -> attention."""
     w = cached("32k")
