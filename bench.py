@@ -11,7 +11,10 @@ The page tables are built once beforehand by segpaged_build_tables on the
 host; its time is reported separately (build_tables), as is the host-side
 launch planning inside each prefill and decode call (plan_host_ms).  Before
 the K timed steps: W warm-up steps, then untimed steps until 0.3 s have
-passed (settle_steps), so that timing starts from a busy GPU's clocks.
+passed (settle_steps), so that timing starts from a busy GPU's clocks; the
+timed steps follow the last settle step without a pause.  Each timed step
+records three HIP events on the call stream (after relocate, prefill and
+decode; the step before it ends where it starts), which time the calls.
 
 Cache-clean timing.  The chip's last-level cache (256 MB) could serve a call
 data that the previous call just read (decode reads the global slots' pages
@@ -240,7 +243,7 @@ class HipEvent:
     Created with hipEventDisableSystemFence: recording it then adds no
     system-scope memory fence between the kernels it separates.  torch's
     events keep that fence, which on this step added about 13 us (5 %) of
-    stall per step across its four records; these add about 5 us.
+    stall per step across four records; these add about 1-1.5 us each.
     """
     _hip = None
     FLAGS = 0x20000000    # hipEventDisableSystemFence (hip_runtime_api.h); timing stays on
@@ -318,20 +321,28 @@ def run_config(name, seed, steps, warmup, log, window_only=False):
     log(f"work: {work}")
 
     def calls(i, ev=None):
+        # ev: the step's three events, after relocate, prefill and decode; the
+        # event before the relocation is the previous step's last (or ev0), so a
+        # step records three markers, not four.
         a, b, c = reps[i % n_rep], reps[(i + 1) % n_rep], reps[(i + 2) % n_rep]
-        if ev:
-            ev[0].record(stream)
         w.relocate(k_in=a[0], k_out=a[2])
         if ev:
-            ev[1].record(stream)
+            ev[0].record(stream)
         w.prefill(k=b[2], v=b[1])
         if ev:
-            ev[2].record(stream)
+            ev[1].record(stream)
         w.decode(k=c[2], v=c[1])
         if ev:
-            ev[3].record(stream)
+            ev[2].record(stream)
 
     stream = torch.cuda.current_stream()
+    # Everything the timed loop needs is made, and the garbage collected, before
+    # the warm-up: a pause between the settle phase and the timed steps (a full
+    # collection takes tens of ms) lets the clocks drop again.
+    ev0 = HipEvent()
+    ev = [[HipEvent() for _ in range(3)] for _ in range(steps)]
+    gc.collect()
+    gc.disable()          # a collection inside the timed loop would stall the launches
     t_warm = time.perf_counter()
     for i in range(max(warmup, n_rep)):
         calls(i)
@@ -342,18 +353,17 @@ def run_config(name, seed, steps, warmup, log, window_only=False):
             calls(n_settle)
             n_settle += 1
         torch.cuda.synchronize()
-    log(f"warm-up: {max(warmup, n_rep)} steps, then {n_settle} more until {CLOCK_SETTLE_S} s had passed")
-    ev = [[HipEvent() for _ in range(4)] for _ in range(steps)]
-    gc.collect()
-    gc.disable()          # a collection inside the timed loop would stall the launches
-    torch.cuda.synchronize()
     t_start = time.perf_counter()
+    ev0.record(stream)
     for i in range(steps):
         calls(i, ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     gc.enable()
-    per = [[max(HipEvent.elapsed_ms(ev[i][a], ev[i][a + 1]), 1e-6) for i in range(steps)] for a in range(3)]
+    log(f"warm-up: {max(warmup, n_rep)} steps, then {n_settle} more until {CLOCK_SETTLE_S} s had passed")
+    marks = [ev0] + [e for step_ev in ev for e in step_ev]      # 3 * steps + 1, in stream order
+    per = [[max(HipEvent.elapsed_ms(marks[3 * i + a], marks[3 * i + a + 1]), 1e-6) for i in range(steps)]
+           for a in range(3)]
     t_reloc, t_pref, t_dec = (sum(x) / steps for x in per)
     ms_per_step = wall / steps * 1e3
 
