@@ -123,36 +123,43 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
         };
         int e_max = 1;
         for (int r = 0; r < n_rows; ++r) e_max = std::max(e_max, h_row_ptr[r + 1] - h_row_ptr[r]);
+        // A row's items depend only on its table length and its sequence's
+        // token count, so rows are counted per (entries, tokens) once and each
+        // candidate is scored per group rather than per row.
+        std::map<std::pair<int, int>, int64_t> groups;
+        for (int r = 0; r < n_rows; ++r) {
+            const int q = r % n_seq;
+            const int nt = h_tok_ptr[q + 1] - h_tok_ptr[q];
+            if (nt > 0) groups[{h_row_ptr[r + 1] - h_row_ptr[r], nt}] += 1;
+        }
         std::map<double, int64_t, std::greater<double>> cls;   // cost -> items, longest first
         std::map<double, int64_t> loads;                       // CU load -> CUs
         auto makespan = [&](int c, int64_t *n_items) {
             cls.clear();
             *n_items = 0;
             int64_t n_parts = 0;
-            for (int r = 0; r < n_rows; ++r) {
-                const int q = r % n_seq;
-                const int nt = h_tok_ptr[q + 1] - h_tok_ptr[q];
+            for (const auto &g : groups) {
+                const int e = g.first.first, nt = g.first.second;
+                const int64_t rows = g.second;
                 const int nq = (nt + p.tok_per_tile - 1) / p.tok_per_tile;
-                if (nq == 0) continue;
                 int ns, it;
-                const int e = h_row_ptr[r + 1] - h_row_ptr[r];
                 row_items(e, nq, c, &ns, &it);
-                *n_items += it;
-                if (ns > 1) n_parts += it;
+                *n_items += rows * it;
+                if (ns > 1) n_parts += rows * it;
                 for (int j = 0; j < nq; ++j) {
                     // q-tile j sees at most the row's pages less those of the
                     // chunk's later tokens (exact for a row without a window)
                     const int t_end = std::min(nt, (j + 1) * p.tok_per_tile);
                     const int64_t v = std::max(1, e - (nt - t_end) / page_size);
                     if (ns == 1) {
-                        cls[cost(v, 2)] += 1;
+                        cls[cost(v, 2)] += rows;
                         continue;
                     }
                     const int64_t ch = ((v + ns - 1) / ns + ppt - 1) / ppt * ppt;
                     const int64_t last = std::max<int64_t>(1, v - (int64_t)(ns - 1) * ch);
-                    cls[cost(ch, 1) + 1.0] += 1;                          // first chunk: the row start
-                    if (ns > 2) cls[cost(ch, 0) + 1.0] += ns - 2;
-                    cls[cost(last, 1) + 1.0] += 1;                        // last chunk: the query tokens
+                    cls[cost(ch, 1) + 1.0] += rows;                       // first chunk: the row start
+                    if (ns > 2) cls[cost(ch, 0) + 1.0] += rows * (ns - 2);
+                    cls[cost(last, 1) + 1.0] += rows;                     // last chunk: the query tokens
                 }
             }
             loads.clear();
