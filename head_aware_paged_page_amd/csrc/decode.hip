@@ -259,7 +259,9 @@ __global__ __launch_bounds__(NWD * 64) __attribute__((amdgpu_waves_per_eu(3, 3))
 
 // Merges the splits of every split row: one wave per (row, head).  The lanes
 // read the split LSEs together (lane s, s+64, ...) and form the weights
-// e^{lse_s - M} in LDS; then O = sum_s w_s o_s / sum_s w_s.
+// e^{lse_s - M} in LDS; then O = sum_s w_s o_s / sum_s w_s.  The partial
+// outputs of the first kPreSplits splits of each lane group are loaded before
+// the LSEs are reduced, so both loads are in flight together.
 template <int D, bool INL>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams P, InlinePlan L) {
     __shared__ float sw[kMaxSplits];
@@ -269,6 +271,21 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams P, Inline
     const int lane = threadIdx.x;
     const int seq = r % P.n_seq, slot = r / P.n_seq, G = P.G;
     const int64_t part0 = INL ? L.part_ptr[r] : P.part_ptr[r];
+    // lane (g, c) accumulates dims 8c .. 8c+7 over splits g, g + SG, ...; the
+    // groups are summed at the end
+    constexpr int CH = D / 8, SG = 64 / CH;
+    constexpr int kPreSplits = 16;
+    const int c = lane % CH, sg = lane / CH;
+    const float *src = P.part_o + (part0 * G + hh) * D + 8 * c;
+    f32x4 pre0[kPreSplits], pre1[kPreSplits];
+#pragma unroll
+    for (int i = 0; i < kPreSplits; ++i) {
+        const int s = sg + i * SG;
+        if (s < ns) {
+            pre0[i] = *(const f32x4 *)(src + (int64_t)s * G * D);
+            pre1[i] = *(const f32x4 *)(src + (int64_t)s * G * D + 4);
+        }
+    }
     float M = -INFINITY;
     for (int s = lane; s < ns; s += 64) M = fmaxf(M, P.part_lse[(part0 + s) * G + hh]);
 #pragma unroll
@@ -282,16 +299,23 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams P, Inline
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) z += __shfl_xor(z, m, 64);
     __syncthreads();
-    // lane (g, c) accumulates dims 8c .. 8c+7 over splits g, g + SG, ..., so the
-    // loads of all splits are in flight together; the groups are then summed
-    constexpr int CH = D / 8, SG = 64 / CH;
-    const int c = lane % CH, sg = lane / CH;
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
-    const float *src = P.part_o + (part0 * G + hh) * D + 8 * c;
+#pragma unroll
+    for (int i = 0; i < kPreSplits; ++i) {
+        const int s = sg + i * SG;
+        if (s < ns) {
+            const float wgt = sw[s];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o[e] += wgt * pre0[i][e];
+                o[4 + e] += wgt * pre1[i][e];
+            }
+        }
+    }
 #pragma unroll 8
-    for (int s = sg; s < ns; s += SG) {
+    for (int s = sg + kPreSplits * SG; s < ns; s += SG) {
         const float wgt = sw[s];
         const f32x4 a0 = *(const f32x4 *)(src + (int64_t)s * G * D), a1 = *(const f32x4 *)(src + (int64_t)s * G * D + 4);
 #pragma unroll

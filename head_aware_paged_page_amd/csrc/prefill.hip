@@ -629,11 +629,8 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, Pre
     float m = -INFINITY, z = 0.f, o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
-#pragma unroll 4
-    for (int s = g0; s < ns; s += SG) {
-        const float x = lse[(int64_t)s * BM];
-        const f16x8 v = *(const f16x8 *)(src + (int64_t)s * BM * D);
-        if (x == -INFINITY) continue;                 // a split that sees no key
+    auto add = [&](float x, const f16x8 &v) {
+        if (x == -INFINITY) return;                   // a split that sees no key
         if (x > m) {
             const float a = __expf(m - x);            // 0 while m is -inf
             z *= a;
@@ -645,7 +642,25 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, Pre
         z += wgt;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] += wgt * (float)v[e];
+    };
+    // the first kPre splits of the lane's group: every load issued before any is used
+    constexpr int kPre = 8;
+    float px[kPre];
+    f16x8 pv[kPre];
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+        const int s = g0 + i * SG;
+        px[i] = -INFINITY;
+        if (s < ns) {
+            px[i] = lse[(int64_t)s * BM];
+            pv[i] = *(const f16x8 *)(src + (int64_t)s * BM * D);
+        }
     }
+#pragma unroll
+    for (int i = 0; i < kPre; ++i)
+        if (g0 + i * SG < ns) add(px[i], pv[i]);
+#pragma unroll 4
+    for (int s = g0 + kPre * SG; s < ns; s += SG) add(lse[(int64_t)s * BM], *(const f16x8 *)(src + (int64_t)s * BM * D));
 #pragma unroll
     for (int off = CH; off < CH * SG; off <<= 1) {    // combine the split groups of the row
         const float m2 = __shfl_xor(m, off, 64);
