@@ -4,11 +4,13 @@
 // the tokens its head's page table and class make visible (RedKnot product
 // profile, section 3) - with fp32 inputs, fp32 arithmetic and fp32 outputs and
 // no reduced precision anywhere.  One wave per (query token, query head) walks
-// the head's table a page (at most 64 keys) at a time: lane t scores key t of
-// the page (the query from LDS, the key row read as float4s), the wave takes
-// the page's max and weights, and lane d then accumulates output dims d,
-// d + 64, ... over the page's keys from the dim-major value page.  A running
-// (max, sum) carries the softmax across pages.
+// the head's table 64 keys at a time: 64 / page_size whole pages for pages of
+// at most 64 keys (lane t scores key t % page_size of the chunk's page
+// t / page_size), or 64 keys of one longer page.  The query sits in LDS, key
+// rows are read as float4s; the wave takes the chunk's max and weights, and
+// lane d then accumulates output dims d, d + 64, ... over the chunk's keys
+// from the dim-major value pages.  A running (max, sum) carries the softmax
+// across chunks.
 #include "device_common.hpp"
 
 namespace sp {
@@ -38,10 +40,26 @@ __device__ __forceinline__ float wave_max(float v) {
 
 constexpr int kF32MaxDim = 256;
 
+// Scores the key at (page phys, slot kk) against the query in LDS.
+__device__ __forceinline__ float f32_score(const F32Params &P, int phys, int kk, const float *sq) {
+    const float4 *krow = (const float4 *)(P.kp + ((int64_t)phys * P.ps + kk) * P.D);
+    const float4 *q4 = (const float4 *)sq;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int j = 0; j < P.D / 4; ++j) {
+        const float4 k = krow[j], qq = q4[j];
+        a0 = fmaf(qq.x, k.x, a0);
+        a1 = fmaf(qq.y, k.y, a1);
+        a2 = fmaf(qq.z, k.z, a2);
+        a3 = fmaf(qq.w, k.w, a3);
+    }
+    return ((a0 + a1) + (a2 + a3)) * P.scale;
+}
+
 template <bool LONG_PAGES>
 __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params P) {
     __shared__ __attribute__((aligned(16))) float sq[kF32MaxDim];
     __shared__ float sw[64];
+    __shared__ int sPhys[64], sNv[64];   // per page of a chunk: id, keys to read from its value page (0: none)
     const int lane = threadIdx.x;
     const int tok = blockIdx.x, head = blockIdx.y;
     const int slot = head / P.G;
@@ -72,50 +90,77 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params P) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = 0.f;
     float m = -INFINITY, l = 0.f;
-    for (int e = P.row_ptr[r]; e < P.row_ptr[r + 1]; ++e) {
-        const int4 en = P.entries[e];
-        if (en.x < 0 || en.x >= P.n_phys) continue;
-        const int nv = min(en.z, ps);
-        if (nv <= 0 || en.y > p || en.y + nv - 1 <= low) continue;
-        // the page's keys 64 at a time: score of key k0 + lane (lanes past the
-        // page's tokens or outside the window: -inf)
-        for (int k0 = 0; k0 < (LONG_PAGES ? nv : 1); k0 += 64) {   // pages of at most 64 keys: one pass
-            const int kk = k0 + lane, kn = LONG_PAGES ? min(nv - k0, 64) : nv;
-            const int pos = en.y + kk;
-            const bool vis = kk < nv && pos <= p && pos > low;
-            float s = -INFINITY;
-            if (vis) {
-                const float4 *krow = (const float4 *)(P.kp + ((int64_t)en.x * ps + kk) * D);
-                const float4 *q4 = (const float4 *)sq;
-                float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-                for (int j = 0; j < D / 4; ++j) {
-                    const float4 k = krow[j], qq = q4[j];
-                    a0 = fmaf(qq.x, k.x, a0);
-                    a1 = fmaf(qq.y, k.y, a1);
-                    a2 = fmaf(qq.z, k.z, a2);
-                    a3 = fmaf(qq.w, k.w, a3);
-                }
-                s = ((a0 + a1) + (a2 + a3)) * P.scale;
-            }
-            const float m_new = fmaxf(m, wave_max(s));
-            if (m_new == -INFINITY) continue;
-            const float alpha = expf(m - m_new);         // 0 while m is -inf
-            const float w = vis ? expf(s - m_new) : 0.f;
-            l = l * alpha + wave_sum(w);
-            sw[lane] = w;
-            __syncthreads();
-            const float *vpage = P.vp + (int64_t)en.x * D * ps + k0;   // V page is dim-major: [D][ps]
+    // one softmax step over a chunk whose visible keys have scores s (-inf
+    // elsewhere) and whose value pages sPhys / sNv describe (n_pg pages,
+    // columns c0 .. c0 + sNv - 1 of each)
+    auto step = [&](float s, bool vis, int n_pg, int c0) {
+        const float m_new = fmaxf(m, wave_max(s));
+        if (m_new == -INFINITY) return;                 // nothing visible yet (wave-uniform)
+        const float alpha = expf(m - m_new);            // 0 while m is -inf
+        const float w = vis ? expf(s - m_new) : 0.f;
+        l = l * alpha + wave_sum(w);
+        sw[lane] = w;
+        __syncthreads();
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d = lane + 64 * i;
-                if (d >= D) continue;
-                const float *vrow = vpage + (int64_t)d * ps;
-                float acc = 0.f;
-                for (int k = 0; k < kn; ++k) acc = fmaf(sw[k], vrow[k], acc);
-                o[i] = o[i] * alpha + acc;
+        for (int i = 0; i < 4; ++i) {
+            const int d = lane + 64 * i;
+            if (d >= D) continue;
+            float acc = 0.f;
+            for (int pg = 0; pg < n_pg; ++pg) {
+                const int nv = sNv[pg];
+                const float *vrow = P.vp + ((int64_t)sPhys[pg] * D + d) * ps + c0;   // V pages are dim-major: [D][ps]
+                const float *wp = sw + (LONG_PAGES ? 0 : pg * ps);
+                for (int k = 0; k < nv; ++k) acc = fmaf(wp[k], vrow[k], acc);
             }
-            __syncthreads();
-            m = m_new;
+            o[i] = o[i] * alpha + acc;
+        }
+        m = m_new;
+    };
+    const int e_beg = P.row_ptr[r], e_end = P.row_ptr[r + 1];
+    if (!LONG_PAGES) {
+        // chunks of ppc whole pages; lane t holds key t % ps of page t / ps
+        const int ppc = max(1, 64 / ps);
+        const int pg = lane / ps, kk = lane % ps;
+        for (int e0 = e_beg; e0 < e_end; e0 += ppc) {
+            const int n_pg = min(ppc, e_end - e0);
+            bool vis = false;
+            int phys = 0, nv = 0;
+            if (pg < n_pg) {
+                const int4 en = P.entries[e0 + pg];
+                if (en.x >= 0 && en.x < P.n_phys) {
+                    phys = en.x;
+                    nv = max(0, min(en.z, ps));
+                    const int pos = en.y + kk;
+                    vis = kk < nv && pos <= p && pos > low;
+                    if (nv > 0 && (en.y > p || en.y + nv - 1 <= low)) nv = 0;   // no key of the page visible
+                }
+            }
+            const float s = vis ? f32_score(P, phys, kk, sq) : -INFINITY;
+            if (kk == 0 && pg < n_pg) {
+                sPhys[pg] = phys;
+                sNv[pg] = nv;
+            }
+            step(s, vis, n_pg, 0);
+            __syncthreads();   // sw, sPhys, sNv are rewritten by the next chunk
+        }
+    } else {
+        for (int e = e_beg; e < e_end; ++e) {
+            const int4 en = P.entries[e];
+            if (en.x < 0 || en.x >= P.n_phys) continue;
+            const int nv = min(en.z, ps);
+            if (nv <= 0 || en.y > p || en.y + nv - 1 <= low) continue;
+            for (int k0 = 0; k0 < nv; k0 += 64) {
+                const int kk = k0 + lane;
+                const int pos = en.y + kk;
+                const bool vis = kk < nv && pos <= p && pos > low;
+                const float s = vis ? f32_score(P, en.x, kk, sq) : -INFINITY;
+                if (lane == 0) {
+                    sPhys[0] = en.x;
+                    sNv[0] = min(nv - k0, 64);
+                }
+                step(s, vis, 1, k0);
+                __syncthreads();
+            }
         }
     }
     float *orow = P.out + ((int64_t)tok * P.Hq + head) * D;
