@@ -21,8 +21,11 @@ data that the previous call just read (decode reads the global slots' pages
 prefill read a moment before).  So the pools exist in R identical replicas and
 step i runs relocate on replica i mod R, prefill on replica (i+1) mod R and
 decode on replica (i+2) mod R: with R >= 3 and R replicas of at least 1 GB
-together, at least one full relocation pass lies between two calls that touch
-the same replica.  A workload whose pools are too large for three copies runs
+together, the prefill and decode of other replicas (allocating reads of some
+300 MB at 32K) and a relocation pass lie between two calls that touch the
+same replica.  (The relocation's non-temporal traffic alone does not evict the
+cache: a decode that rereads one replica with only relocations in between
+runs about 12 % faster.)  A workload whose pools are too large for three copies runs
 with R = 1; its calls each move several GB.
 
 Work counted is algorithmic only, from the host tables (never from the GPU):
