@@ -276,8 +276,10 @@ int segpaged_workspace_bytes(int kind, int dtype, int head_dim, int page_size, i
  *
  * Query tokens of sequence s are rows h_tok_ptr[s] .. h_tok_ptr[s+1]-1 of q,
  * at positions d_q_pos0[s] + (row - tok_ptr[s]).  h_tok_ptr and h_row_ptr are
- * host copies of d_tok_ptr and d_row_ptr (used to plan the launch).  The
- * tables must be those built for this call's query positions.
+ * host copies of d_tok_ptr and d_row_ptr, equal to them: they plan the
+ * launch, and for calls of few rows the kernels take the bounds from them
+ * rather than from the device arrays.  The tables must be those built for
+ * this call's query positions.
  * d_cls, d_window: device copies of the per-slot class and window.
  * lse may be NULL.  workspace: device memory of at least
  * segpaged_workspace_bytes(SP_WS_PREFILL, ...) bytes, 256-byte aligned.
@@ -305,6 +307,7 @@ int segpaged_prefill(int dtype, int head_dim, int page_size, int group, int n_se
  *   q, out [n_seq][n_slot * group][head_dim];  lse [n_seq][n_slot * group].
  * Partial results (m, l, o) of each split go to the workspace and are merged:
  *   O = sum_s e^{lse_s - M} o_s / sum_s e^{lse_s - M},  LSE = M + ln sum_s e^{lse_s - M}.
+ * h_row_ptr is the host copy of d_row_ptr, equal to it: it plans the launch.
  * Supported: SP_BF16 with head_dim 64 or 128, page_size 16 or 32, group 1..16;
  * SP_F32 with head_dim 16..256 (multiple of 16), any page_size.
  */
