@@ -196,6 +196,38 @@ def test_workspace_query_and_validation():
     assert e.value.status == sp.SP_EINVAL
 
 
+def test_workspace_query_limits():
+    # a decode row longer than one call's split capacity (1024 splits of at
+    # most 512 pages), and a query group beyond 16 heads
+    rp = np.array([0, 1024 * 512 + 1], np.int32)
+    with pytest.raises(sp.SegPagedError) as e:
+        sp.workspace_bytes(sp.SP_WS_DECODE, sp.SP_BF16, 128, 16, 4, 1, 1, None, rp)
+    assert e.value.status == sp.SP_EUNSUPPORTED and "split capacity" in str(e.value)
+    assert sp.workspace_bytes(sp.SP_WS_DECODE, sp.SP_BF16, 128, 16, 4, 1, 1, None,
+                              np.array([0, 1024 * 512], np.int32)) > 0
+    with pytest.raises(sp.SegPagedError) as e:
+        sp.workspace_bytes(sp.SP_WS_DECODE, sp.SP_BF16, 128, 16, 17, 1, 1, None, np.array([0, 4], np.int32))
+    assert e.value.status == sp.SP_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_prefill_plan_does_not_depend_on_row_order(seed):
+    # The planner scores rows of equal shape together: a permutation of the
+    # rows of one sequence (same multiset of table lengths) must give the same
+    # plan, hence the same workspace size, for any mix of lengths.
+    r = np.random.default_rng(seed)
+    for _ in range(40):
+        n_slot = int(r.integers(2, 80))
+        lens = r.choice(r.integers(1, 3000, size=int(r.integers(1, 6))), size=n_slot)
+        tok = np.array([0, int(r.integers(1, 700))], np.int32)
+        for ps in (16, 32):
+            rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+            rq = np.concatenate([[0], np.cumsum(r.permutation(lens))]).astype(np.int32)
+            a = sp.workspace_bytes(sp.SP_WS_PREFILL, sp.SP_BF16, 128, ps, 4, 1, n_slot, tok, rp)
+            b = sp.workspace_bytes(sp.SP_WS_PREFILL, sp.SP_BF16, 128, ps, 4, 1, n_slot, tok, rq)
+            assert a == b
+
+
 @pytest.mark.parametrize("seed", range(4))
 def test_bench_counts_from_host_tables_match_oracle(seed):
     """bench.py takes its FLOP and byte numerators from the host tables: the
