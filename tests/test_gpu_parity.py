@@ -245,8 +245,11 @@ def test_small_layouts_fp32(i):
 
 def test_fp32_pages_longer_than_a_wave():
     """fp32 attention over pages of 128 keys (the kernel scores a page 64 keys
-    at a time) and of 64 keys, against the oracle."""
-    for ps, lens, npf in ((128, [[300, 70]], 20), (64, [[129, 700]], 33)):
+    at a time), of 64 keys, and of sizes that do not divide 64 (24: two pages
+    per step and 16 idle lanes; 48: one page per step; 5: twelve pages per
+    step), against the oracle."""
+    for ps, lens, npf in ((128, [[300, 70]], 20), (64, [[129, 700]], 33), (24, [[250, 61]], 30),
+                          (48, [[97, 200]], 25), (5, [[83, 17]], 12)):
         lay = custom_layout(seg_lens=lens, offline=[[17, -900]], n_prefill=npf, n_decode=1,
                             classes=[(GLOBAL, 0), (LOCAL, 90)], page_size=ps, head_dim=64, group=2, dtype="f32",
                             ret_lists={}, name=f"f32_ps{ps}", seed=3)
