@@ -4,7 +4,8 @@ Each seed draws a small layout: 1-3 sequences (one of them possibly without a
 reused segment), 0-3 segments of up to 600 tokens each at random offline
 positions, 1-6 slots of random class (global, local with a random window,
 retrieval with a random page list, dense), query group 1-8, head_dim 64 or
-128, page size 16 or 32, and up to 90 new tokens.  Relocation, prefill (every
+128, page size 16 or 32, and up to 90 new tokens; a second family takes
+groups 3, 5, 6, 12 and 16, pages of up to 64 keys and up to 200 new tokens.  Relocation, prefill (every
 row, every query token) and decode (every row) are compared with the oracle
 at the same bounds as the fixed-layout tests.  Every draw is seeded, so a
 failure names a reproducible case.
@@ -18,12 +19,15 @@ from test_gpu_parity import _wl, check_prefill, check_decode, check_relocate
 pytestmark = pytest.mark.gpu
 
 
-def _draw(seed):
-    r = np.random.default_rng(1000 + seed)
+def _draw(seed, wide=False):
+    """wide: query groups that do not divide a wave's 32 rows (3, 5, 6, 12) and
+    group 16, pages of 16, 32 or 64 keys, and up to 200 new tokens (several
+    query tiles per row)."""
+    r = np.random.default_rng((5000 if wide else 1000) + seed)
     n_seq = int(r.integers(1, 4))
-    ps = int(r.choice([16, 32]))
+    ps = int(r.choice([16, 32, 64] if wide else [16, 32]))
     D = int(r.choice([64, 128]))
-    G = int(r.choice([1, 2, 4, 8]))
+    G = int(r.choice([3, 5, 6, 12, 16] if wide else [1, 2, 4, 8]))
     seg_lens, offline = [], []
     for q in range(n_seq):
         n_segs = int(r.integers(1, 4))
@@ -42,10 +46,10 @@ def _draw(seed):
                 nsp = sum(-(-l // ps) for l in seg_lens[q])
                 k = int(r.integers(0, nsp + 1)) if nsp else 0
                 ret[(slot, q)] = np.sort(r.choice(nsp, size=k, replace=False)) if k else np.zeros(0, np.int64)
-    n_prefill = int(r.integers(1, 91))
+    n_prefill = int(r.integers(1, 201 if wide else 91))
     return custom_layout(seg_lens=seg_lens, offline=offline, n_prefill=n_prefill, n_decode=1, classes=classes,
-                         page_size=ps, head_dim=D, group=G, dtype="bf16", ret_lists=ret, name=f"random{seed}",
-                         seed=seed)
+                         page_size=ps, head_dim=D, group=G, dtype="bf16", ret_lists=ret,
+                         name=f"random{'_wide' if wide else ''}{seed}", seed=seed)
 
 
 @pytest.mark.parametrize("seed", range(24))
@@ -58,3 +62,18 @@ def test_random_layout_whole_path(seed):
     check_prefill(w)
     w.decode()
     check_decode(w)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_layout_wide_groups(seed):
+    """Groups 3, 5, 6, 12 and 16, pages up to 64 keys, several query tiles per
+    row; decode where it takes the page size (16 or 32)."""
+    lay = _draw(seed, wide=True)
+    w = _wl(lay)
+    w.relocate()
+    check_relocate(w)
+    w.prefill()
+    check_prefill(w)
+    if lay.page_size in (16, 32):
+        w.decode()
+        check_decode(w)
