@@ -228,3 +228,22 @@ def test_importance_random_layouts(seed):
     check_row_sums(w, imp)
     worst = check_importance(w, imp, pos_ptr)
     print(f"[importance] {lay.name}: worst error {worst:.3f} of its bound")
+
+
+def _wide_seeds():
+    from test_random_layouts_gpu import _draw
+    return [s for s in range(16) if _draw(s, wide=True).page_size in (16, 32)]
+
+
+@pytest.mark.parametrize("seed", _wide_seeds())
+def test_importance_random_wide_groups(seed):
+    """The wide random layouts (groups 3, 5, 6, 12 and 16, several q-tiles per
+    row) that use pages of 16 or 32 keys: every row against the oracle."""
+    from test_random_layouts_gpu import _draw
+    lay = _draw(seed, wide=True)
+    w = _wl(lay)
+    w.prefill()
+    imp, pos_ptr = w.importance()
+    check_row_sums(w, imp)
+    worst = check_importance(w, imp, pos_ptr)
+    print(f"[importance] {lay.name}: worst error {worst:.3f} of its bound")
