@@ -160,3 +160,25 @@ def test_window_only_random_layouts(seed):
             b = full.gather_keys(full.k_reloc, slot, seq)
             stored = ~np.isnan(a[:, 0])
             assert np.array_equal(a[stored], b[stored]), (slot, seq)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_window_only_random_wide_groups(seed):
+    """The wide random layouts (groups 3 to 16, pages up to 64 keys, several
+    query tiles per row) with window-only storage: prefill (and decode, for
+    pages of 16 or 32 keys) bit-identical to whole-chain storage."""
+    from test_random_layouts_gpu import _draw
+    lay = _draw(seed, wide=True)
+    full = _wl(lay)
+    win = _wl(lay, window_only=True)
+    assert win.n_phys <= full.n_phys
+    dec = lay.page_size in (16, 32)
+    for w in (full, win):
+        w.relocate()
+        w.prefill(k=w.k_reloc)
+        if dec:
+            w.decode(k=w.k_reloc)
+    torch.cuda.synchronize()
+    assert torch.equal(full.out_prefill, win.out_prefill) and torch.equal(full.lse_prefill, win.lse_prefill)
+    if dec:
+        assert torch.equal(full.out_decode, win.out_decode) and torch.equal(full.lse_decode, win.lse_decode)
