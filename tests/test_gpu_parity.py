@@ -695,6 +695,43 @@ def test_workspace_contents_do_not_matter(fill):
 
 # ---------------------------------------------------------------- edge cases
 
+def test_decode_at_split_capacity():
+    """The largest row one decode call takes: 1024 splits of 512 pages, 524 288
+    pages of 16 keys (8.4 M keys).  With every query zero, attention is
+    uniform, so each head's output is the mean of the visible values and the
+    log-sum-exp is ln(count).  The values are set to a pattern exact in bf16,
+    v[pos, d] = ((pos + 3 d) mod 16) / 16, whose mean over the visible
+    positions is counted exactly on the host."""
+    ps, D = 16, 128
+    n_pages = 1024 * 512
+    seg = (n_pages - 1) * ps                 # the two new tokens fill one more page
+    lay = custom_layout(seg_lens=[[seg]], offline=[[0]], n_prefill=1, n_decode=1, classes=[(GLOBAL, 0)],
+                        page_size=ps, head_dim=D, group=4, dtype="bf16", name="decode_capacity", seed=7)
+    w = _wl(lay, relocated_pool=False)
+    assert int(w.td["row_ptr"][-1]) == n_pages
+    ent = torch.from_numpy(np.ascontiguousarray(w.td["entries"]).reshape(-1, 4)).to("cuda")
+    phys, pos0 = ent[:, 0].long(), ent[:, 1].int()
+    slots = torch.arange(ps, device="cuda", dtype=torch.int32)
+    d3 = 3 * torch.arange(D, device="cuda", dtype=torch.int32)
+    for c0 in range(0, n_pages, 1 << 16):                                 # [pages, D, ps], 65 536 pages at a time
+        pos = pos0[c0:c0 + (1 << 16), None] + slots[None, :]
+        vals = ((pos[:, None, :] + d3[None, :, None]) % 16).float().div_(16).to(torch.bfloat16)
+        w.v_pool[phys[c0:c0 + (1 << 16)]] = vals
+    del vals, pos
+    w.q_decode.zero_()
+    out, lse = w.decode()
+    torch.cuda.synchronize()
+    count = seg + 2                          # keys 0 .. the decode token's position
+    per_res = np.bincount(np.arange(16), minlength=16) * (count // 16)
+    per_res[: count % 16] += 1               # how many visible positions have each residue mod 16
+    expect = np.array([np.sum(per_res * ((np.arange(16) + 3 * dd) % 16) / 16.0) / count for dd in range(D)])
+    got = out[0].double().cpu().numpy()                                   # [heads, D]
+    err = np.max(np.abs(got - expect[None, :]))
+    print(f"[decode capacity] {count} keys: max abs error {err:.2e}")
+    assert err <= 1e-2
+    assert np.max(np.abs(lse[0].double().cpu().numpy() - np.log(count))) <= 1e-5
+
+
 def test_empty_calls_write_nothing():
     """A relocation list of length 0 and a prefill call with no query tokens are
     valid no-ops: SP_OK, and the outputs keep what they held."""
