@@ -695,18 +695,19 @@ def test_workspace_contents_do_not_matter(fill):
 
 # ---------------------------------------------------------------- edge cases
 
-def test_decode_at_split_capacity():
+def test_longest_rows_with_zero_queries():
     """The largest row one decode call takes: 1024 splits of 512 pages, 524 288
-    pages of 16 keys (8.4 M keys).  With every query zero, attention is
-    uniform, so each head's output is the mean of the visible values and the
-    log-sum-exp is ln(count).  The values are set to a pattern exact in bf16,
-    v[pos, d] = ((pos + 3 d) mod 16) / 16, whose mean over the visible
-    positions is counted exactly on the host."""
-    ps, D = 16, 128
+    pages of 16 keys (8.4 M keys), through prefill (64 tokens, every one) and
+    decode.  With every query zero, attention is uniform, so each head's output
+    is the mean of the visible values and the log-sum-exp is ln(count): one
+    split missing or doubled would move it by 1e-3 at the decode.  The values
+    are set to a pattern exact in bf16, v[pos, d] = ((pos + 3 d) mod 16) / 16,
+    whose mean over the visible positions is counted exactly on the host."""
+    ps, D, n_new = 16, 128, 65
     n_pages = 1024 * 512
-    seg = (n_pages - 1) * ps                 # the two new tokens fill one more page
-    lay = custom_layout(seg_lens=[[seg]], offline=[[0]], n_prefill=1, n_decode=1, classes=[(GLOBAL, 0)],
-                        page_size=ps, head_dim=D, group=4, dtype="bf16", name="decode_capacity", seed=7)
+    seg = (n_pages - (n_new + ps - 1) // ps) * ps     # the new tokens fill the last five pages
+    lay = custom_layout(seg_lens=[[seg]], offline=[[0]], n_prefill=n_new - 1, n_decode=1, classes=[(GLOBAL, 0)],
+                        page_size=ps, head_dim=D, group=4, dtype="bf16", name="longest_rows", seed=7)
     w = _wl(lay, relocated_pool=False)
     assert int(w.td["row_ptr"][-1]) == n_pages
     ent = torch.from_numpy(np.ascontiguousarray(w.td["entries"]).reshape(-1, 4)).to("cuda")
@@ -718,18 +719,25 @@ def test_decode_at_split_capacity():
         vals = ((pos[:, None, :] + d3[None, :, None]) % 16).float().div_(16).to(torch.bfloat16)
         w.v_pool[phys[c0:c0 + (1 << 16)]] = vals
     del vals, pos
+    w.q_prefill.zero_()
     w.q_decode.zero_()
-    out, lse = w.decode()
+    out_p, lse_p = w.prefill()
+    out_d, lse_d = w.decode()
     torch.cuda.synchronize()
-    count = seg + 2                          # keys 0 .. the decode token's position
-    per_res = np.bincount(np.arange(16), minlength=16) * (count // 16)
-    per_res[: count % 16] += 1               # how many visible positions have each residue mod 16
-    expect = np.array([np.sum(per_res * ((np.arange(16) + 3 * dd) % 16) / 16.0) / count for dd in range(D)])
-    got = out[0].double().cpu().numpy()                                   # [heads, D]
-    err = np.max(np.abs(got - expect[None, :]))
-    print(f"[decode capacity] {count} keys: max abs error {err:.2e}")
+
+    def mean_pattern(count):
+        per_res = np.full(16, count // 16, np.int64)
+        per_res[: count % 16] += 1           # visible positions 0 .. count-1 by residue mod 16
+        return np.array([np.sum(per_res * ((np.arange(16) + 3 * dd) % 16) / 16.0) / count for dd in range(D)])
+
+    counts = [seg + t + 1 for t in range(n_new)]        # token t sees positions 0 .. seg + t
+    got = torch.cat([out_p, out_d]).double().cpu().numpy()                # [tokens, heads, D]
+    lse = torch.cat([lse_p, lse_d]).double().cpu().numpy()               # [tokens, heads]
+    err = max(float(np.max(np.abs(got[t] - mean_pattern(c)[None, :]))) for t, c in enumerate(counts))
+    lerr = max(float(np.max(np.abs(lse[t] - np.log(c)))) for t, c in enumerate(counts))
+    print(f"[longest rows] {counts[-1]} keys: max abs error {err:.2e}, log-sum-exp {lerr:.2e}")
     assert err <= 1e-2
-    assert np.max(np.abs(lse[0].double().cpu().numpy() - np.log(count))) <= 1e-5
+    assert lerr <= 1e-5
 
 
 def test_empty_calls_write_nothing():
