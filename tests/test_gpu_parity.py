@@ -184,6 +184,24 @@ def test_relocate_plus_minus_delta_roundtrip():
             assert np.max(np.abs(a - b)) <= TOL[lay.dtype]
 
 
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_relocate_large_deltas(dtype):
+    """Position deltas near the int32 limit (2^30 - 5, -999 900, -2^30 + 350):
+    the angle is formed and reduced in fp64, so relocated keys still match the
+    fp64 oracle at the dtype's bound; prefill and decode over them too."""
+    lay = custom_layout(seg_lens=[[100, 50, 30]], offline=[[-(2 ** 30) + 5, 10 ** 6, 2 ** 30 - 200]], n_prefill=5,
+                        n_decode=1, classes=[(GLOBAL, 0), (LOCAL, 40)], page_size=16,
+                        head_dim=64 if dtype == "f32" else 128, group=2, dtype=dtype, name=f"bigdelta_{dtype}",
+                        seed=11)
+    w = _wl(lay)
+    w.relocate()
+    check_relocate(w)
+    w.prefill()
+    check_prefill(w)
+    w.decode()
+    check_decode(w)
+
 # ---------------------------------------------------------------- small bf16 layouts: several tiles, ragged tails
 
 SMALL = [
