@@ -175,6 +175,86 @@ def summarize(a) -> None:
     print(open(txt).read())
 
 
+# Hardware counter passes for the instruction mix and pipe activity of the
+# step's kernels (one rocprofv3 --pmc run each: at most 8 SQ counters a pass).
+COUNTER_PASSES = [
+    "GRBM_GUI_ACTIVE SQ_WAVE_CYCLES SQ_BUSY_CU_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU "
+    "SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_SCA SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_ANY",
+    "GRBM_GUI_ACTIVE SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_VALU_TRANS_F32 "
+    "SQ_WAIT_INST_LDS SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_SMEM",
+]
+
+
+def counters(a) -> None:
+    """Per-dispatch averages of the counter passes for the step's main kernels,
+    with the kernel durations of the same runs (--kernel-trace), into
+    profiles/counters_<workload>.txt."""
+    cmd = ("timeout -s KILL 120 rocprofv3 --kernel-trace --pmc {c} --output-format csv -d <dir> -o run -- "
+           f"python3 bench.py --config {a.workload} --steps 2 --warmup 1 --no-cpu-baseline --no-128k --no-window")
+    vals, durs = defaultdict(dict), defaultdict(list)
+    for d in a.passes:
+        for name, cs in read_counters(d).items():
+            _, short = short_name(name)
+            if short:
+                vals[short].update(cs)
+        kt = os.path.join(d, "run_kernel_trace.csv")
+        if os.path.exists(kt):
+            for r in csv.DictReader(open(kt)):
+                _, short = short_name(r["Kernel_Name"])
+                if short:
+                    durs[short].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [f"# Hardware counters per dispatch, workload {a.workload}", "",
+             "commands (from the repository root, on one MI355X; one pass each):"]
+    lines += ["  " + cmd.format(c=f'"{c}"') for c in COUNTER_PASSES]
+    lines += ["", "Averages over every dispatch of the runs (warm-up, settle and timed calls).  SQ counters",
+              "aggregate all SIMDs, GRBM_GUI_ACTIVE sums the 8 XCDs (divided by a dispatch's duration",
+              "it gives 8 times the clock).  Derived, per dispatch, with cycles = GRBM_GUI_ACTIVE / 8:",
+              "  clock = cycles / duration (median duration of the same runs' kernel trace);",
+              "  mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles * 1024 SIMDs);",
+              "  cu_busy = SQ_BUSY_CU_CYCLES / (cycles * 256 CUs);",
+              "  valu / lds / salu share = SQ_ACTIVE_INST_{VALU,LDS,SCA} / SQ_WAVE_CYCLES (wave time",
+              "  spent issuing or executing each kind); wait share = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES;",
+              "  coexec = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES (matrix-busy cycles with",
+              "  vector work alongside); per MFMA = instruction counts divided by SQ_INSTS_MFMA.",
+              "The counting window of a dispatch is somewhat longer than the kernel: for dispatches of",
+              "under about 100 us the clock reads high and the busy fractions low; the instruction",
+              "counts and ratios are exact.", ""]
+    for short in ("prefill_bf16_kernel", "decode_bf16_kernel", "relocate_kernel", "importance_bf16_kernel"):
+        if short not in vals:
+            continue
+        v = vals[short]
+        lines.append(f"## {short}")
+        for k in sorted(v):
+            lines.append(f"  {k:32s} {v[k]:18.1f}")
+        g = v.get("GRBM_GUI_ACTIVE", 0.0) / 8           # one XCD's cycles
+        wc = v.get("SQ_WAVE_CYCLES", 0.0)
+        mf = v.get("SQ_INSTS_MFMA", 0.0)
+        dur = sorted(durs[short])[len(durs[short]) // 2] if durs.get(short) else None
+        der = []
+        if dur and g:
+            der.append(f"clock {g / dur / 1e3:.2f} GHz (median duration {dur:.1f} us)")
+        if g:
+            der.append(f"mfma_busy {v.get('SQ_VALU_MFMA_BUSY_CYCLES', 0.0) / (g * 1024):.3f}")
+            der.append(f"cu_busy {v.get('SQ_BUSY_CU_CYCLES', 0.0) / (g * 256):.3f}")
+        if v.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+            der.append(f"coexec {v.get('SQ_VALU_MFMA_COEXEC_CYCLES', 0.0) / v['SQ_VALU_MFMA_BUSY_CYCLES']:.3f}")
+        if wc:
+            for name, key in (("valu", "SQ_ACTIVE_INST_VALU"), ("lds", "SQ_ACTIVE_INST_LDS"),
+                              ("salu", "SQ_ACTIVE_INST_SCA"), ("wait", "SQ_WAIT_INST_ANY")):
+                if key in v:
+                    der.append(f"{name} share {v[key] / wc:.3f}")
+        if mf:
+            for name, key in (("valu", "SQ_INSTS_VALU"), ("trans", "SQ_INSTS_VALU_TRANS_F32"),
+                              ("salu", "SQ_INSTS_SALU"), ("lds", "SQ_INSTS_LDS"), ("smem", "SQ_INSTS_SMEM")):
+                if key in v:
+                    der.append(f"{name} per MFMA {v[key] / mf:.2f}")
+        lines += ["  derived: " + "; ".join(der), ""]
+    os.makedirs(a.out, exist_ok=True)
+    txt = os.path.join(a.out, f"counters_{a.workload}.txt")
+    open(txt, "w").write("\n".join(lines) + "\n")
+    print(open(txt).read())
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -186,9 +266,15 @@ def main(argv=None) -> None:
         s.add_argument(f"--{k}", required=True)
     s.add_argument("--copy-mib", type=int, default=1024)
     s.add_argument("--out", default=os.path.join(ROOT, "profiles"))
+    k = sub.add_parser("counters")
+    k.add_argument("--workload", required=True)
+    k.add_argument("--passes", nargs="+", required=True, help="one rocprofv3 output directory per counter pass")
+    k.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args(argv)
     if a.cmd == "copy":
         copy_main(a.mib)
+    elif a.cmd == "counters":
+        counters(a)
     else:
         summarize(a)
 
