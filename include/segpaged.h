@@ -49,8 +49,10 @@
  *     exception crosses the ABI.  On error nothing was enqueued and outputs are
  *     unspecified.
  *   - Ownership: the caller owns every buffer.  The library allocates no host or
- *     device memory in the device calls and keeps no state beyond cached device
- *     attributes; calls are thread-safe.
+ *     device memory in the device calls and keeps no state beyond a call
+ *     counter (the epoch that tags the work counters in a workspace) and, for
+ *     segpaged_decode_static, each GPU's scratch address; calls are
+ *     thread-safe (calls that share a workspace must not overlap).
  *   - Device calls enqueue on `stream` (a hipStream_t; NULL = the null stream)
  *     and return without waiting.  Kernel faults surface at the caller's next
  *     synchronisation.  Physical page ids read from device tables are checked
