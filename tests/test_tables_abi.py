@@ -292,3 +292,50 @@ def test_visible_sets_from_tables_equal_the_oracle(seed):
                     mine = mine[mine > p - lay.window[slot]]
                 want = tpos[otab.visible(int(lay.cls[slot]), int(lay.window[slot]), listed, tpos, tsp, tnew, int(p))]
                 assert np.array_equal(np.sort(mine), np.sort(want)), (call, row, int(p))
+
+
+def test_host_calls_from_many_threads():
+    """The host calls keep no shared state (the error text is per thread): the
+    table builder and the workspace query run from 8 threads at once (ctypes
+    releases the interpreter lock during each call) give the results of the
+    same calls made one at a time, and a failing call in one thread leaves the
+    other threads' error text alone."""
+    import threading
+    lay = synth.make_layout("16k")
+    arr = lay.abi_arrays("prefill")
+    n = sp.build_tables(**arr, page_size=lay.page_size, free_list=None, counts_only=True)["counts"][0]
+    free = np.random.default_rng(3).permutation(int(n) + 11).astype(np.int32)
+    want = sp.build_tables(**arr, page_size=lay.page_size, free_list=free)
+    tok = np.arange(lay.n_seq + 1, dtype=np.int32) * lay.n_prefill
+    ws_want = sp.workspace_bytes(sp.SP_WS_PREFILL, sp.SP_BF16, lay.head_dim, lay.page_size, lay.group, lay.n_seq,
+                                 lay.n_slot, tok, want["row_ptr"])
+    errors, bad = [], []
+
+    def work(i):
+        try:
+            for _ in range(5):
+                if i % 4 == 3:       # a failing call: its message must stay in this thread
+                    with pytest.raises(sp.SegPagedError) as e:
+                        sp.workspace_bytes(sp.SP_WS_DECODE, sp.SP_BF16, 96, 16, 4, 1, 1, None,
+                                           np.array([0, 4], np.int32))
+                    if "head_dim" not in str(e.value):
+                        bad.append(str(e.value))
+                    continue
+                got = sp.build_tables(**arr, page_size=lay.page_size, free_list=free)
+                for k in ("row_ptr", "entries", "reloc", "storage"):
+                    if not np.array_equal(got[k], want[k]):
+                        bad.append(k)
+                ws = sp.workspace_bytes(sp.SP_WS_PREFILL, sp.SP_BF16, lay.head_dim, lay.page_size, lay.group,
+                                        lay.n_seq, lay.n_slot, tok, got["row_ptr"])
+                if ws != ws_want:
+                    bad.append("workspace")
+        except Exception as ex:      # surfaced below
+            errors.append(repr(ex))
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    assert not bad, bad[:5]
