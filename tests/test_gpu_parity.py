@@ -758,6 +758,38 @@ def test_longest_rows_with_zero_queries():
     assert lerr <= 1e-5
 
 
+def test_calls_on_two_streams_at_once():
+    """Two workloads (own pools, tables and workspaces) run relocate -> prefill
+    -> decode on two streams at once, several times over: every output equals
+    the same calls made one stream at a time, bit for bit."""
+    lays = [synth.make_layout("16k"), _small(1)]
+    ws = [_wl(l) for l in lays]
+    want = []
+    for w in ws:
+        w.relocate()
+        w.prefill(k=w.k_reloc)
+        w.decode(k=w.k_reloc)
+        torch.cuda.synchronize()
+        want.append([t.clone() for t in (w.k_reloc, w.out_prefill, w.lse_prefill, w.out_decode, w.lse_decode)])
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(5):
+        for w in ws:
+            for t in (w.out_prefill, w.lse_prefill, w.out_decode, w.lse_decode):
+                t.zero_()
+        torch.cuda.synchronize()
+        for w, st in zip(ws, streams):
+            with torch.cuda.stream(st):
+                w.relocate(stream=st)
+                w.prefill(k=w.k_reloc, stream=st)
+                w.decode(k=w.k_reloc, stream=st)
+        torch.cuda.synchronize()
+        for w, ref in zip(ws, want):
+            got = (w.k_reloc, w.out_prefill, w.lse_prefill, w.out_decode, w.lse_decode)
+            for a, b in zip(got, ref):
+                assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                                   b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
 def test_empty_calls_write_nothing():
     """A relocation list of length 0 and a prefill call with no query tokens are
     valid no-ops: SP_OK, and the outputs keep what they held."""
