@@ -51,19 +51,22 @@ template <int D, int ps>
 __device__ __forceinline__ void load_block(const DecodeParams &P, const int4 *sE, int e0, int e_hi, Block<D> &B) {
     const int lane = threadIdx.x & 63;
     const int m = lane & 15, grp = lane >> 4;
-    // entries of the block's pages (one or two), wave-uniform
-    int4 en[2];
+    // entries of the block's pages (one or two), wave-uniform; kept as plain
+    // integers (a select between two int4 values of an array can become an
+    // indexed load from private memory)
+    int px[2], py[2], pz[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int e = e0 + i;
-        en[i] = int4{0, 0, 0, 0};
+        px[i] = py[i] = pz[i] = 0;
         if (i * ps < KB && e < e_hi) {
             const int4 v = sE[i];
-            en[i] = int4{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
-                         __builtin_amdgcn_readfirstlane(v.z), 0};
+            px[i] = __builtin_amdgcn_readfirstlane(v.x);
+            py[i] = __builtin_amdgcn_readfirstlane(v.y);
+            pz[i] = __builtin_amdgcn_readfirstlane(v.z);
         }
-        B.y[i] = en[i].y;
-        B.z[i] = en[i].z;
+        B.y[i] = py[i];
+        B.z[i] = pz[i];
     }
     // K: A operand row m of key tile kt is key 8*(m/4) + 4*kt + m%4; dims 32*s + 8*grp.
     // Slots without a token are read from page 0 and never zeroed: their scores
@@ -72,8 +75,8 @@ __device__ __forceinline__ void load_block(const DecodeParams &P, const int4 *sE
     for (int kt = 0; kt < 2; ++kt) {
         const int j = 8 * (m >> 2) + 4 * kt + (m & 3);
         const int pg = j / ps, tk = j % ps;
-        const int4 e = pg ? en[1] : en[0];
-        const bf16 *src = P.kp + ((int64_t)e.x * ps + tk) * D + 8 * grp;
+        const int phys = pg ? px[1] : px[0];
+        const bf16 *src = P.kp + ((int64_t)phys * ps + tk) * D + 8 * grp;
 #pragma unroll
         for (int s = 0; s < D / 32; ++s) B.k[kt][s] = *(const u32x4 *)(src + 32 * s);
     }
@@ -83,8 +86,8 @@ __device__ __forceinline__ void load_block(const DecodeParams &P, const int4 *sE
     {
         const int j = 8 * grp;
         const int pg = j / ps, tk = j % ps;
-        const int4 e = pg ? en[1] : en[0];
-        const bf16 *src = P.vp + ((int64_t)e.x * D + m) * ps + tk;
+        const int phys = pg ? px[1] : px[0];
+        const bf16 *src = P.vp + ((int64_t)phys * D + m) * ps + tk;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) B.v[dt] = *(const u32x4 *)(src + (int64_t)16 * dt * ps);
     }
@@ -107,7 +110,11 @@ __global__ __launch_bounds__(NWD * 64) __attribute__((amdgpu_waves_per_eu(3, 3))
     __shared__ float sO[NWD][D][17];
     __shared__ int4 sE[kDecodeMaxChunk + 2];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    // The wave index is uniform, but the compiler cannot tell from threadIdx.x:
+    // said explicitly, the block loop below is a scalar loop rather than an
+    // exec-masked one (32K decode kernel 43 -> 35 us).
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, grp = lane >> 4;
 
     int r, sp_i;
