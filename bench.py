@@ -46,9 +46,11 @@ of K and V: about 256 FLOP/B, below the chip's 312 FLOP/B ridge, so the
 prefill of such a chunk is bound by HBM, not by the matrix cores.)
 
 With the default workload (32K) the same line also carries the 128K
-microbenchmark, measured the same way, under "config_128k", and the same
+microbenchmark, measured the same way, under "config_128k", the same
 workload with window-only storage (every head stores only the pages its
-queries can read) under "window_only", with the KV bytes one session holds.
+queries can read) under "window_only", with the KV bytes one session holds,
+and its prefill and decode issued as one call per layer (8 calls of the
+layer's 8 KV heads each, as a model runs them) under "per_layer".
 """
 from __future__ import annotations
 
@@ -286,9 +288,98 @@ def _pct(xs, q):
     return float(np.percentile(np.asarray(xs), q))
 
 
-def run_config(name, seed, steps, warmup, log, window_only=False):
+def layer_calls(w, reps, n_rep, steps, warmup, work):
+    """The same prefill and decode as one call per layer (the slots of one layer,
+    its KV heads, per call), as a model would issue them: n_layers prefill calls,
+    then n_layers decode calls, each on its own slice of the queries and tables,
+    with its own plan and workspace.  The prefill calls of a step run on one pool
+    replica and its decode calls on the next, so consecutive uses of one replica
+    are separated by the traffic of two whole passes.  Returns the summed call
+    times and the per-layer means, against the same algorithmic work (the sum
+    over the layers is the whole call's)."""
+    import torch
+    import head_aware_paged_page_amd.segpaged as sp
+
+    from synth.configs import CONFIGS
+
+    lay = w.lay
+    G, D, ns, ps = lay.group, lay.head_dim, lay.n_seq, w.ps
+    spl = CONFIGS[lay.name]["n_kv"]          # a layer's KV heads: slots l * spl .. (l + 1) * spl - 1
+    n_layers = lay.n_slot // spl
+    code = sp.SP_F32 if lay.dtype == "f32" else sp.SP_BF16
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    def sub(tab, l):   # the layer's rows (slots l*spl .. (l+1)*spl - 1, every sequence) of a table
+        rp, ent = tab["row_ptr"], tab["entries"]
+        r0, r1 = l * spl * ns, (l + 1) * spl * ns
+        return (rp[r0:r1 + 1] - rp[r0]).astype(np.int32), np.ascontiguousarray(ent[rp[r0]:rp[r1]], dtype=np.int32)
+
+    layers = []
+    for l in range(n_layers):
+        heads = slice(l * spl * G, (l + 1) * spl * G)
+        rp_p, en_p = sub(w.tp, l)
+        rp_d, en_d = sub(w.td, l)
+        qp, qd = w.q_prefill[:, heads].contiguous(), w.q_decode[:, heads].contiguous()
+        common = dict(page_size=ps, group=G, n_seq=ns, n_slot=spl,
+                      d_cls=dev(lay.cls[l * spl:(l + 1) * spl].astype(np.int32)),
+                      d_window=dev(lay.window[l * spl:(l + 1) * spl].astype(np.int32)), scale=w.scale)
+        pre = dict(common, h_tok_ptr=w.h_tok_ptr, h_row_ptr=rp_p, d_tok_ptr=w.d_tok_ptr, d_q_pos0=w.d_q_pos0,
+                   d_row_ptr=dev(rp_p), d_entries=dev(en_p), out=torch.empty_like(qp),
+                   lse=torch.empty(qp.shape[:2], dtype=torch.float32, device="cuda"),
+                   workspace=torch.empty(sp.workspace_bytes(sp.SP_WS_PREFILL, code, D, ps, G, ns, spl, w.h_tok_ptr,
+                                                            rp_p), dtype=torch.uint8, device="cuda"))
+        dec = dict(common, h_row_ptr=rp_d, d_q_pos=w.d_q_dec, d_row_ptr=dev(rp_d), d_entries=dev(en_d),
+                   out=torch.empty_like(qd), lse=torch.empty(qd.shape[:2], dtype=torch.float32, device="cuda"),
+                   workspace=torch.empty(sp.workspace_bytes(sp.SP_WS_DECODE, code, D, ps, G, ns, spl, None, rp_d),
+                                         dtype=torch.uint8, device="cuda"))
+        layers.append((qp, qd, pre, dec))
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        b, c = reps[(2 * i) % n_rep], reps[(2 * i + 1) % n_rep]
+        for j, (qp, _, pre, _) in enumerate(layers):
+            sp.prefill(qp, b[2], b[1], **pre)
+            if ev:
+                ev[j].record(stream)
+        for j, (_, qd, _, dec) in enumerate(layers):
+            sp.decode(qd, c[2], c[1], **dec)
+            if ev:
+                ev[len(layers) + j].record(stream)
+
+    n_l = len(layers)
+    ev0 = HipEvent()
+    ev = [[HipEvent() for _ in range(2 * n_l)] for _ in range(steps)]
+    for i in range(max(warmup, n_rep)):
+        step(i)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    marks = [ev0] + [e for row in ev for e in row]
+    per_call = np.array([[HipEvent.elapsed_ms(marks[2 * n_l * i + k], marks[2 * n_l * i + k + 1])
+                          for k in range(2 * n_l)] for i in range(steps)])     # [steps, 2 * n_layers]
+    t_p = float(per_call[:, :n_l].sum(axis=1).mean())
+    t_d = float(per_call[:, n_l:].sum(axis=1).mean())
+    peak_flops = PEAK_FP32_FLOPS if lay.dtype == "f32" else PEAK_BF16_FLOPS
+    n_glob = [int((lay.cls[l * spl:(l + 1) * spl] != LOCAL).sum()) for l in range(n_layers)]
+    return {
+        "calls_per_step": 2 * n_l, "slots_per_call": spl, "non_local_slots_per_layer": n_glob,
+        "segpaged_prefill": {"ms": round(t_p, 4), "TFLOP/s": round(work["prefill_flops"] / t_p / 1e9, 2),
+                             "frac_mfma": round(work["prefill_flops"] / t_p / 1e-3 / peak_flops, 4),
+                             "per_layer_ms": [round(float(x), 4) for x in per_call[:, :n_l].mean(axis=0)]},
+        "segpaged_decode": {"ms": round(t_d, 4), "GB/s": round(work["decode_bytes"] / t_d / 1e6, 1),
+                            "frac_hbm": round(work["decode_bytes"] / t_d / 1e-3 / PEAK_HBM, 4),
+                            "per_layer_ms": [round(float(x), 4) for x in per_call[:, n_l:].mean(axis=0)]},
+        "note": "the step's prefill and decode as one call per layer (8 KV heads each); sums of the calls' times",
+    }
+
+
+def run_config(name, seed, steps, warmup, log, window_only=False, per_layer=False):
     """Build one workload on the GPU and time `steps` steps; returns (result dict, workload).
-    window_only: each head stores only the pages its queries can read."""
+    window_only: each head stores only the pages its queries can read.
+    per_layer: also time the prefill and decode as one call per layer."""
     import torch
     import synth
     import head_aware_paged_page_amd.segpaged as sp
@@ -434,6 +525,11 @@ def run_config(name, seed, steps, warmup, log, window_only=False):
     t_pack = HipEvent.elapsed_ms(pe[0], pe[1]) / n_calls
     del k_pk, v_pk
 
+    per_layer_out = None
+    if per_layer:
+        log("timing the prefill and decode as one call per layer ...")
+        per_layer_out = layer_calls(w, reps, n_rep, steps, warmup, work)
+
     # Rows beyond the step: attention importance of the reused segment
     # positions for the chunk's queries (against the prefill's lse), and the
     # selection of a quarter of them per layer for the FFN.  Importance work:
@@ -502,6 +598,8 @@ def run_config(name, seed, steps, warmup, log, window_only=False):
                         **(beyond_imp or {})},
         "dtype": "f32" if lay.dtype == "f32" else "bf16",
     }
+    if per_layer_out is not None:
+        res["per_layer"] = per_layer_out
     del reps
     return res, w
 
@@ -516,6 +614,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-128k", action="store_true", help="skip the 128K block of the default run")
     ap.add_argument("--no-window", action="store_true", help="skip the window-only storage block")
+    ap.add_argument("--no-layers", action="store_true", help="skip the per-layer calls of the default run")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle seconds per CPU process")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -535,7 +634,8 @@ def main():
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    res0, w = run_config(args.config, args.seed, args.steps, args.warmup, log)
+    res0, w = run_config(args.config, args.seed, args.steps, args.warmup, log,
+                         per_layer=args.config == "32k" and not args.no_layers)
     lay, tp = w.lay, w.tp
     del w
     res = {"metric": METRIC, "value": res0["value"], "unit": "% of roofline", "n_gpus": 1, "steps": args.steps,
@@ -543,6 +643,8 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": res0["dtype"], "data": "synthetic",
            "config": res0["config"], "roofline": res0["roofline"], "calls": res0["calls"],
            "beyond_step": res0["beyond_step"]}
+    if "per_layer" in res0:
+        res["per_layer"] = res0["per_layer"]
     if args.config == "32k" and not args.no_128k:
         torch.cuda.empty_cache()
         r128, w128 = run_config("128k", args.seed, max(3, args.steps // 2), max(2, args.warmup // 2), log)

@@ -560,6 +560,41 @@ def test_split_count_does_not_change_results(which):
           f"({worst_frac:.2f} of its bound)")
 
 
+@pytest.mark.parametrize("which", ["prefill", "decode"])
+def test_per_layer_calls_match_the_whole_call(which):
+    """The 32K step's prefill and decode issued as one call per layer (its 8 KV
+    heads), as the bench's per-layer block times them, against the one 64-slot
+    call: each layer's rows get their own plan (finer kv splits when a layer holds
+    few global rows), so the log-sum-exp must agree to 2e-5 and the outputs to the
+    roundings that depend on the split (as in the split-count test), bounded here
+    by the largest |v| of the pool's written pages instead of the per-row sum of
+    p |v|."""
+    from synth.configs import CONFIGS
+    w = cached("32k")
+    lay, G = w.lay, w.lay.group
+    spl = CONFIGS["32k"]["n_kv"]                 # a layer's KV heads
+    n_layers = lay.n_slot // spl
+    o_all, l_all = (w.prefill() if which == "prefill" else w.decode())
+    torch.cuda.synchronize()
+    o_all, l_all = o_all.clone(), l_all.clone()
+    vmax = float(torch.nan_to_num(w.v_pool.float().abs(), nan=0.0, posinf=0.0).amax())   # unused pages hold NaN
+    per_side = 2.0 ** -9 + (2.0 ** -11 if which == "prefill" else 0.0)
+    worst_l = worst_o = 0.0
+    for layer in range(n_layers):
+        slots = list(range(layer * spl, (layer + 1) * spl))
+        o, l = _row_call(w, slots, which)
+        heads = slice(layer * spl * G, (layer + 1) * spl * G)
+        d = float((l - l_all[:, heads]).abs().max())
+        worst_l = max(worst_l, d)
+        assert d <= 2e-5, f"layer {layer}: LSE differs by {d}"
+        a, b = o.float(), o_all[:, heads].float()
+        diff = (a - b).abs()
+        bound = torch.maximum(a.abs(), b.abs()) * 2.0 ** -7 + 2 * per_side * vmax
+        worst_o = max(worst_o, float(diff.max()))
+        assert bool(torch.all(diff <= bound)), f"layer {layer}: outputs differ by {float(diff.max())}"
+    print(f"[per-layer] {which}: max LSE difference {worst_l:.2e}, max output difference {worst_o:.2e}")
+
+
 def test_out_of_pool_pages_are_empty():
     """A table entry whose physical page lies outside the pool (>= n_phys, or
     negative) is read as a page with no tokens: prefill and decode then equal
