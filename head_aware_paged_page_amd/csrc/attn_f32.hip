@@ -3,14 +3,17 @@
 // Same computation as the bf16 kernels - softmax attention of each query over
 // the tokens its head's page table and class make visible (RedKnot product
 // profile, section 3) - with fp32 inputs, fp32 arithmetic and fp32 outputs and
-// no reduced precision anywhere.  One wave per (query token, query head) walks
-// the head's table 64 keys at a time: 64 / page_size whole pages for pages of
-// at most 64 keys (lane t scores key t % page_size of the chunk's page
-// t / page_size), or 64 keys of one longer page.  The query sits in LDS, key
-// rows are read as float4s; the wave takes the chunk's max and weights, and
-// lane d then accumulates output dims d, d + 64, ... over the chunk's keys
-// from the dim-major value pages.  A running (max, sum) carries the softmax
-// across chunks.
+// no reduced precision anywhere.  A workgroup of kF32Waves waves takes one
+// (query token, query head); its waves share the head's table in chunks of 64
+// keys (wave w takes chunks w, w + kF32Waves, ...): 64 / page_size whole pages
+// for pages of at most 64 keys (lane t scores key t % page_size of the chunk's
+// page t / page_size), or 64 keys of one longer page.  The query sits in LDS,
+// key rows are read as float4s; the wave takes the chunk's max and weights,
+// and lane d then accumulates output dims d, d + 64, ... over the chunk's keys
+// from the dim-major value pages.  A running (max, sum) carries each wave's
+// softmax across its chunks, and the waves' states are merged at the end
+// (log-sum-exp weights, in fp32), so the chain of dependent loads a call waits
+// for is a quarter of the table's.
 #include "device_common.hpp"
 
 namespace sp {
@@ -39,6 +42,14 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 constexpr int kF32MaxDim = 256;
+constexpr int kF32Waves = 4;   // waves per (query token, query head)
+
+// Orders this wave's LDS writes before its lanes read each other's (one wave's
+// LDS operations complete in order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+}
 
 // Scores the key at (page phys, slot kk) against the query in LDS.
 __device__ __forceinline__ float f32_score(const F32Params &P, int phys, int kk, const float *sq) {
@@ -56,11 +67,17 @@ __device__ __forceinline__ float f32_score(const F32Params &P, int phys, int kk,
 }
 
 template <bool LONG_PAGES>
-__global__ __launch_bounds__(64) void attn_f32_kernel(F32Params P) {
+__global__ __launch_bounds__(64 * kF32Waves) void attn_f32_kernel(F32Params P) {
+    constexpr int NW = kF32Waves;
     __shared__ __attribute__((aligned(16))) float sq[kF32MaxDim];
-    __shared__ float sw[64];
-    __shared__ int sPhys[64], sNv[64];   // per page of a chunk: id, keys to read from its value page (0: none)
-    const int lane = threadIdx.x;
+    __shared__ float sw_all[NW][64];
+    __shared__ int sPhys_all[NW][64], sNv_all[NW][64];   // per page of a chunk: id, keys to read from its value page (0: none)
+    __shared__ float sM[NW], sL[NW];
+    __shared__ float sO[NW][kF32MaxDim];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    float *sw = sw_all[wave];
+    int *sPhys = sPhys_all[wave], *sNv = sNv_all[wave];
     const int tok = blockIdx.x, head = blockIdx.y;
     const int slot = head / P.G;
     int seq, p;
@@ -83,7 +100,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params P) {
     const int D = P.D, ps = P.ps;
 
     const float *qrow = P.q + ((int64_t)tok * P.Hq + head) * D;
-    for (int d = lane; d < D; d += 64) sq[d] = qrow[d];
+    for (int d = threadIdx.x; d < D; d += 64 * NW) sq[d] = qrow[d];
     __syncthreads();
 
     float o[4];
@@ -100,7 +117,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params P) {
         const float w = vis ? expf(s - m_new) : 0.f;
         l = l * alpha + wave_sum(w);
         sw[lane] = w;
-        __syncthreads();
+        wave_lds_sync();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int d = lane + 64 * i;
@@ -121,7 +138,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params P) {
         // chunks of ppc whole pages; lane t holds key t % ps of page t / ps
         const int ppc = max(1, 64 / ps);
         const int pg = lane / ps, kk = lane % ps;
-        for (int e0 = e_beg; e0 < e_end; e0 += ppc) {
+        for (int e0 = e_beg + wave * ppc; e0 < e_end; e0 += NW * ppc) {
             const int n_pg = min(ppc, e_end - e0);
             bool vis = false;
             int phys = 0, nv = 0;
@@ -141,10 +158,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params P) {
                 sNv[pg] = nv;
             }
             step(s, vis, n_pg, 0);
-            __syncthreads();   // sw, sPhys, sNv are rewritten by the next chunk
+            wave_lds_sync();   // sw, sPhys, sNv are rewritten by the next chunk
         }
     } else {
-        for (int e = e_beg; e < e_end; ++e) {
+        for (int e = e_beg + wave; e < e_end; e += NW) {
             const int4 en = P.entries[e];
             if (en.x < 0 || en.x >= P.n_phys) continue;
             const int nv = min(en.z, ps);
@@ -159,18 +176,41 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params P) {
                     sNv[0] = min(nv - k0, 64);
                 }
                 step(s, vis, 1, k0);
-                __syncthreads();
+                wave_lds_sync();
             }
         }
     }
-    float *orow = P.out + ((int64_t)tok * P.Hq + head) * D;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    // merge the waves' (max, sum, unnormalised output) states
+    if (lane == 0) {
+        sM[wave] = m;
+        sL[wave] = l;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int d = lane + 64 * i;
-        if (d < D) orow[d] = o[i] * inv;
+        if (d < D) sO[wave][d] = o[i];
     }
-    if (P.lse && lane == 0) P.lse[(int64_t)tok * P.Hq + head] = l > 0.f ? m + logf(l) : -INFINITY;
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sM[w]);
+    float z = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) z += sL[w] * expf(sM[w] - M);   // a wave that saw nothing has l = 0
+    }
+    const float inv = z > 0.f ? 1.f / z : 0.f;
+    float *orow = P.out + ((int64_t)tok * P.Hq + head) * D;
+    for (int d = threadIdx.x; d < D; d += 64 * NW) {
+        float acc = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                if (sM[w] != -INFINITY) acc += sO[w][d] * expf(sM[w] - M);
+        }
+        orow[d] = acc * inv;
+    }
+    if (P.lse && threadIdx.x == 0) P.lse[(int64_t)tok * P.Hq + head] = z > 0.f ? M + logf(z) : -INFINITY;
 }
 
 int launch_f32(const AttnArgs &a, int64_t n_tok, const int32_t *tok_ptr, hipStream_t stream) {
@@ -197,8 +237,8 @@ int launch_f32(const AttnArgs &a, int64_t n_tok, const int32_t *tok_ptr, hipStre
     P.n_phys = a.n_phys;
     P.scale = a.scale;
     const dim3 grid((unsigned)n_tok, (unsigned)P.Hq);
-    if (a.page_size > 64) hipLaunchKernelGGL(attn_f32_kernel<true>, grid, dim3(64), 0, stream, P);
-    else hipLaunchKernelGGL(attn_f32_kernel<false>, grid, dim3(64), 0, stream, P);
+    if (a.page_size > 64) hipLaunchKernelGGL(attn_f32_kernel<true>, grid, dim3(64 * kF32Waves), 0, stream, P);
+    else hipLaunchKernelGGL(attn_f32_kernel<false>, grid, dim3(64 * kF32Waves), 0, stream, P);
     return check_hip(hipGetLastError(), "fp32 attention launch");
 }
 
