@@ -13,7 +13,7 @@
 // from the dim-major value pages.  A running (max, sum) carries each wave's
 // softmax across its chunks, and the waves' states are merged at the end
 // (log-sum-exp weights, in fp32), so the chain of dependent loads a call waits
-// for is a quarter of the table's.
+// for is an eighth of the table's.
 #include "device_common.hpp"
 
 namespace sp {
@@ -42,7 +42,7 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 constexpr int kF32MaxDim = 256;
-constexpr int kF32Waves = 4;   // waves per (query token, query head)
+constexpr int kF32Waves = 8;   // waves per (query token, query head)
 
 // Orders this wave's LDS writes before its lanes read each other's (one wave's
 // LDS operations complete in order; this keeps the compiler from moving them).
