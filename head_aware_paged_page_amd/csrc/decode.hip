@@ -264,54 +264,69 @@ __global__ __launch_bounds__(NWD * 64) __attribute__((amdgpu_waves_per_eu(3, 3))
     }
 }
 
-// Merges the splits of every split row: one wave per (row, head).  The lanes
-// read the split LSEs together (lane s, s+64, ...) and form the weights
-// e^{lse_s - M} in LDS; then O = sum_s w_s o_s / sum_s w_s.  The partial
-// outputs of the first kPreSplits splits of each lane group are loaded before
-// the LSEs are reduced, so both loads are in flight together.
+// Merges the splits of every split row: one workgroup of kMergeWaves waves per
+// (row, head).  The threads read the split LSEs together (thread s, s + 256,
+// ...) and form the weights e^{lse_s - M} in LDS; then O = sum_s w_s o_s /
+// sum_s w_s.  Lane (g, c) of wave w accumulates dims 8c .. 8c+7 over splits
+// w*SG + g, + kMergeWaves*SG, ..., so a row cut into many splits (a small
+// call splits its rows finely) is summed by 16 lane groups at once; the
+// groups are added by lane exchanges within a wave and through LDS across
+// waves.  The partial outputs of a lane's first kPreSplits splits are loaded
+// before the LSEs are reduced, so both loads are in flight together.
+constexpr int kMergeWaves = 4;
+
 template <int D, bool INL>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams P, InlinePlan L) {
+__global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeParams P, InlinePlan L) {
+    constexpr int CH = D / 8, SG = 64 / CH, TG = SG * kMergeWaves;
+    constexpr int kPreSplits = 8;
     __shared__ float sw[kMaxSplits];
+    __shared__ float sMr[kMergeWaves], sZr[kMergeWaves];
+    __shared__ float sO[kMergeWaves][D];
     const int r = blockIdx.x, hh = blockIdx.y;
     const int ns = INL ? L.nsplit[r] : P.nsplit[r];
     if (ns == 1) return;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int seq = r % P.n_seq, slot = r / P.n_seq, G = P.G;
     const int64_t part0 = INL ? L.part_ptr[r] : P.part_ptr[r];
-    // lane (g, c) accumulates dims 8c .. 8c+7 over splits g, g + SG, ...; the
-    // groups are summed at the end
-    constexpr int CH = D / 8, SG = 64 / CH;
-    constexpr int kPreSplits = 16;
-    const int c = lane % CH, sg = lane / CH;
+    const int c = lane % CH, g = wave * SG + lane / CH;
     const float *src = P.part_o + (part0 * G + hh) * D + 8 * c;
     f32x4 pre0[kPreSplits], pre1[kPreSplits];
 #pragma unroll
     for (int i = 0; i < kPreSplits; ++i) {
-        const int s = sg + i * SG;
+        const int s = g + i * TG;
         if (s < ns) {
             pre0[i] = *(const f32x4 *)(src + (int64_t)s * G * D);
             pre1[i] = *(const f32x4 *)(src + (int64_t)s * G * D + 4);
         }
     }
     float M = -INFINITY;
-    for (int s = lane; s < ns; s += 64) M = fmaxf(M, P.part_lse[(part0 + s) * G + hh]);
+    for (int s = tid; s < ns; s += 64 * kMergeWaves) M = fmaxf(M, P.part_lse[(part0 + s) * G + hh]);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+    if (lane == 0) sMr[wave] = M;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) M = fmaxf(M, sMr[w]);
     float z = 0.f;
-    for (int s = lane; s < ns; s += 64) {
+    for (int s = tid; s < ns; s += 64 * kMergeWaves) {
         const float wgt = M == -INFINITY ? 0.f : __expf(P.part_lse[(part0 + s) * G + hh] - M);
         sw[s] = wgt;
         z += wgt;
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) z += __shfl_xor(z, m, 64);
-    __syncthreads();
+    if (lane == 0) sZr[wave] = z;
+    __syncthreads();   // the weights and the partial sums of z
+    z = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) z += sZr[w];
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
 #pragma unroll
     for (int i = 0; i < kPreSplits; ++i) {
-        const int s = sg + i * SG;
+        const int s = g + i * TG;
         if (s < ns) {
             const float wgt = sw[s];
 #pragma unroll
@@ -321,8 +336,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams P, Inline
             }
         }
     }
-#pragma unroll 8
-    for (int s = sg + kPreSplits * SG; s < ns; s += SG) {
+#pragma unroll 4
+    for (int s = g + kPreSplits * TG; s < ns; s += TG) {
         const float wgt = sw[s];
         const f32x4 a0 = *(const f32x4 *)(src + (int64_t)s * G * D), a1 = *(const f32x4 *)(src + (int64_t)s * G * D + 4);
 #pragma unroll
@@ -335,14 +350,22 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams P, Inline
     for (int off = CH; off < 64; off <<= 1)
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], off, 64);
+    if (lane < CH) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sO[wave][8 * c + e] = o[e];
+    }
+    __syncthreads();
+    if (wave != 0 || lane >= CH) return;
+#pragma unroll
+    for (int w = 1; w < kMergeWaves; ++w)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] += sO[w][8 * c + e];
     const float inv = z > 0.f ? 1.f / z : 0.f;
     const int64_t orow = (int64_t)seq * P.Hq + (int64_t)slot * G + hh;
-    if (sg == 0) {
-        u32x4 pk;
+    u32x4 pk;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(o[2 * i] * inv, o[2 * i + 1] * inv);
-        *(u32x4 *)(P.out + orow * D + 8 * c) = pk;
-    }
+    for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(o[2 * i] * inv, o[2 * i + 1] * inv);
+    *(u32x4 *)(P.out + orow * D + 8 * c) = pk;
     if (P.lse && lane == 0) P.lse[orow] = z > 0.f ? M + logf(z) : -INFINITY;
 }
 
@@ -396,10 +419,10 @@ int launch_decode(const AttnArgs &a, const Plan &p, hipStream_t stream) {
     if (a.head_dim == DD && a.page_size == PSV) {                                                               \
         if (inl) {                                                                                              \
             hipLaunchKernelGGL((decode_bf16_kernel<DD, PSV, true>), grid, dim3(NWD * 64), 0, stream, P, L);    \
-            if (p.n_parts) hipLaunchKernelGGL((decode_merge_kernel<DD, true>), mgrid, dim3(64), 0, stream, P, L); \
+            if (p.n_parts) hipLaunchKernelGGL((decode_merge_kernel<DD, true>), mgrid, dim3(64 * kMergeWaves), 0, stream, P, L); \
         } else {                                                                                                \
             hipLaunchKernelGGL((decode_bf16_kernel<DD, PSV, false>), grid, dim3(NWD * 64), 0, stream, P, L);   \
-            if (p.n_parts) hipLaunchKernelGGL((decode_merge_kernel<DD, false>), mgrid, dim3(64), 0, stream, P, L); \
+            if (p.n_parts) hipLaunchKernelGGL((decode_merge_kernel<DD, false>), mgrid, dim3(64 * kMergeWaves), 0, stream, P, L); \
         }                                                                                                       \
     }
     SP_DECODE_CASE(128, 16) else SP_DECODE_CASE(128, 32) else SP_DECODE_CASE(64, 16) else SP_DECODE_CASE(64, 32)

@@ -25,16 +25,18 @@ constexpr int kDecodeWaves = 4;
 
 // Split planning: the prefill splits long rows so that their pieces fill the
 // 256 CUs of the chip once; decode aims at about one streaming split per CU.
-// Every split still streams at least kMinSplitKeys keys.
+// Every split still streams at least kMinSplitKeysPrefill / kMinSplitKeysDecode keys.
 constexpr int kPlanCUs = 256;
 constexpr int kPrefillSetupTiles = 6;      // fixed cost of a prefill item (set-up, result, hand-off), in 64-key tiles
 constexpr int kPrefillEdgeTiles = 3;       // extra cost of a row end inside an item (bounds, fix-ups), in tiles
 constexpr double kMergeTiles = 1.5;        // merge pass per split prefill item, in 64-key tiles of one CU
 constexpr int kTargetDecodeItems = 384;
 constexpr int kDecodeWgPerCU = 2;          // decode workgroups per CU the plan aims for
-constexpr int kMinSplitKeys = 512;
+constexpr int kMinSplitKeysPrefill = 64;
+constexpr int kMinSplitKeysDecode = 512;
 constexpr int kMaxSplits = 1024;
 constexpr int kDecodeMaxChunk = 512;       // pages of one decode split (its entries are staged in LDS)
+constexpr int kDeepMergeSplits = 32;       // prefill rows split this many ways are merged a row per workgroup
 
 // Number of kv splits and work items of one row; identical on host and device.
 __host__ __device__ inline void row_items(int n_entries, int n_qtiles, int chunk_pages,
@@ -57,7 +59,8 @@ struct Plan {
     int chunk_pages = 0;     // pages per kv split (INT32_MAX = no split)
     int64_t n_items = 0;     // work items (= workgroups of the attention kernel)
     int64_t n_parts = 0;     // work items whose result is a partial to merge
-    int merge_rows = 0;      // prefill: most query rows one split item merges
+    int merge_rows = 0;      // prefill: most query rows one split item merges (rows split fewer than kDeepMergeSplits ways)
+    int merge_rows_deep = 0; // the same for rows split kDeepMergeSplits ways or more
     // Work items are numbered long-first: the items of split rows (row order),
     // then those of unsplit rows.  item_ptr[r] / item_ptr2[r] = first item of
     // row r in the first / second range (zero-length for rows of the other).

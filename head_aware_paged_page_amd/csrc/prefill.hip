@@ -599,6 +599,105 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // many rows with few splits each, SG > 1 few rows with many splits.  The
 // partials are normalised (|o| <= max |v|), so fp16 keeps them to about
 // 5e-4 relative.
+// A q-tile cut into kDeepMergeSplits or more kv splits (a small call splits
+// its rows finely) is merged one row per workgroup: lane (g, c) of wave w
+// merges dims 8c .. 8c+7 of the row over splits w*SGW + g, + 4*SGW, ...
+// online (running max, rescaled sums), so 16 lane groups share the splits;
+// the groups are combined by lane exchanges within a wave and through LDS
+// across the four waves.  Same arithmetic as the per-wave merge below.
+template <int D, bool INL>
+__device__ __forceinline__ void prefill_merge_deep(const PrefillParams &P, const PrefillInlinePlan &L, int BM, int r,
+                                                   int local, int ns) {
+    constexpr int CH = D / 8, SGW = 64 / CH, NWm = 4, TG = SGW * NWm;
+    __shared__ float smd[NWm][CH], szd[NWm][CH];
+    __shared__ float sod[NWm][CH][8];
+    const int qt = local / ns, sp_i = local % ns;
+    const int per = (BM + ns - 1) / ns;
+    if ((int)blockIdx.y >= per) return;                     // the whole workgroup: no row of this split here
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane % CH, g = wave * SGW + lane / CH;
+    const int seq = r % P.n_seq, slot = r / P.n_seq;
+    const int row = sp_i * per + blockIdx.y;
+    const int rl = min(row, BM - 1);
+    const int tok_base = INL ? L.tok_ptr[seq] : P.tok_ptr[seq];
+    const int t0 = qt * P.tpt;
+    const int ntok = min(P.tpt, (INL ? L.tok_ptr[seq + 1] : P.tok_ptr[seq + 1]) - tok_base - t0);
+    const int nrows = ntok * P.G;
+    const int64_t part0 = (int64_t)(INL ? L.part_ptr[r] : P.part_ptr[r]) + (int64_t)qt * ns;
+    const float *lse = P.part_lse + part0 * BM + rl;
+    const _Float16 *src = P.part_o + (part0 * BM + rl) * D + 8 * c;
+    float m = -INFINITY, z = 0.f, o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+    auto add = [&](float x, const f16x8 &v) {
+        if (x == -INFINITY) return;                   // a split that sees no key
+        if (x > m) {
+            const float a = __expf(m - x);            // 0 while m is -inf
+            z *= a;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] *= a;
+            m = x;
+        }
+        const float wgt = __expf(x - m);
+        z += wgt;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] += wgt * (float)v[e];
+    };
+    constexpr int kPre = 4;
+    float px[kPre];
+    f16x8 pv[kPre];
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+        const int s = g + i * TG;
+        px[i] = -INFINITY;
+        if (s < ns) {
+            px[i] = lse[(int64_t)s * BM];
+            pv[i] = *(const f16x8 *)(src + (int64_t)s * BM * D);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kPre; ++i)
+        if (g + i * TG < ns) add(px[i], pv[i]);
+#pragma unroll 4
+    for (int s = g + kPre * TG; s < ns; s += TG) add(lse[(int64_t)s * BM], *(const f16x8 *)(src + (int64_t)s * BM * D));
+    auto combine = [&](float m2, float z2, const float *o2) {   // this state += another, by their max
+        const float mm = fmaxf(m, m2);
+        const float a = mm == -INFINITY ? 0.f : __expf(m - mm);
+        const float b = mm == -INFINITY ? 0.f : __expf(m2 - mm);
+        z = z * a + z2 * b;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = o[e] * a + o2[e] * b;
+        m = mm;
+    };
+#pragma unroll
+    for (int off = CH; off < 64; off <<= 1) {         // the wave's split groups
+        float o2[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(o[e], off, 64);
+        const float m2 = __shfl_xor(m, off, 64), z2 = __shfl_xor(z, off, 64);
+        combine(m2, z2, o2);
+    }
+    if (lane < CH) {
+        smd[wave][c] = m;
+        szd[wave][c] = z;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sod[wave][c][e] = o[e];
+    }
+    __syncthreads();
+    if (wave != 0 || lane >= CH || row >= min(nrows, (sp_i + 1) * per)) return;
+#pragma unroll
+    for (int w = 1; w < NWm; ++w) combine(smd[w][c], szd[w][c], sod[w][c]);
+    const float inv = z > 0.f ? 1.f / z : 0.f;
+    const int tq = row / P.G, gh = row % P.G;
+    const int64_t orow = (int64_t)(tok_base + t0 + tq) * P.Hq + (int64_t)slot * P.G + gh;
+    u32x4 pk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(o[2 * i] * inv, o[2 * i + 1] * inv);
+    *(u32x4 *)(P.out + orow * D + 8 * c) = pk;
+    if (P.lse && c == 0) P.lse[orow] = z > 0.f ? m + logf(z) : -INFINITY;
+}
+
 template <int D, int SG, bool INL>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, PrefillInlinePlan L, int BM) {
     constexpr int CH = D / 8, RPW = 64 / (CH * SG), RPB = 4 * RPW;   // rows per wave / workgroup
@@ -608,6 +707,10 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams P, Pre
     else item_of(P.item_ptr, P.item_ptr2, P.n_rows, blockIdx.x, &r, &local);
     const int ns = INL ? L.nsplit[r] : P.nsplit[r];
     if (ns == 1) return;
+    if (ns >= kDeepMergeSplits) {
+        prefill_merge_deep<D, INL>(P, L, BM, r, local, ns);
+        return;
+    }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c = lane % CH, g0 = (lane / CH) % SG;
     const int qt = local / ns, sp_i = local % ns;
@@ -810,10 +913,11 @@ int launch_prefill(const AttnArgs &a, const Plan &p, int64_t n_tok, hipStream_t 
     P.epoch = epoch;
     P.n_items = (int)p.n_items;
     // merge: split groups per row from the rows each split item merges
+    // (rows split kDeepMergeSplits ways or more take one row per workgroup)
     const bool merge_wide = p.merge_rows <= 16;
     const int merge_rpb = 4 * 64 / (a.head_dim / 8) / (merge_wide ? 4 : 1);   // rows per merge workgroup
     const dim3 mgrid((unsigned)std::max<int64_t>(1, p.n_parts),
-                     (unsigned)std::max(1, (p.merge_rows + merge_rpb - 1) / merge_rpb));
+                     (unsigned)std::max(1, std::max((p.merge_rows + merge_rpb - 1) / merge_rpb, p.merge_rows_deep)));
     const dim3 grid_persist((unsigned)std::min<int64_t>(p.n_items, kPlanCUs));
 #define SP_PREFILL_CASE(DD, PSV)                                                                     \
     if (a.head_dim == DD && a.page_size == PSV) {                                                    \

@@ -99,7 +99,7 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
             work += h_row_ptr[r + 1] - h_row_ptr[r];
         }
     }
-    const int min_chunk = std::max(1, kMinSplitKeys / page_size);
+    const int min_chunk = std::max(1, (kind == SP_WS_PREFILL ? kMinSplitKeysPrefill : kMinSplitKeysDecode) / page_size);
     if (kind == SP_WS_PREFILL) {
         // One persistent workgroup per CU takes the items long-first from a
         // counter: list scheduling, longest item first.  Every candidate chunk
@@ -253,7 +253,9 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
         items += it;
         if (ns > 1) {
             parts += it;
-            p.merge_rows = std::max(p.merge_rows, (p.rows_per_tile + ns - 1) / ns);
+            const int per = (p.rows_per_tile + ns - 1) / ns;
+            if (kind == SP_WS_PREFILL && ns >= kDeepMergeSplits) p.merge_rows_deep = std::max(p.merge_rows_deep, per);
+            else p.merge_rows = std::max(p.merge_rows, per);
         }
     }
     if (items > INT32_MAX) return fail(SP_EINVAL, "too many work items");
