@@ -116,9 +116,9 @@ def summarize(a) -> None:
     write = read_counters(a.write)
     stats = list(csv.DictReader(open(os.path.join(a.trace, "run_kernel_stats.csv"))))
     bench_cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
-                 f"python3 bench.py --config {a.workload} --steps 10 --warmup 2 --no-cpu-baseline --no-128k --no-window")
+                 f"python3 bench.py --config {a.workload} --steps 10 --warmup 2 --no-cpu-baseline --no-128k --no-window --no-layers")
     pmc_cmd = ("rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- "
-               f"python3 bench.py --config {a.workload} --steps 2 --warmup 1 --no-cpu-baseline --no-128k --no-window")
+               f"python3 bench.py --config {a.workload} --steps 2 --warmup 1 --no-cpu-baseline --no-128k --no-window --no-layers")
     copy_cmd = ("rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- "
                 f"python3 -m head_aware_paged_page_amd.profiling copy --mib {a.copy_mib}")
     lines = [f"# Kernel time, workload {a.workload} (rocprofv3 kernel trace, --stats)", "",
@@ -190,7 +190,7 @@ def counters(a) -> None:
     with the kernel durations of the same runs (--kernel-trace), into
     profiles/counters_<workload>.txt."""
     cmd = ("timeout -s KILL 120 rocprofv3 --kernel-trace --pmc {c} --output-format csv -d <dir> -o run -- "
-           f"python3 bench.py --config {a.workload} --steps 2 --warmup 1 --no-cpu-baseline --no-128k --no-window")
+           f"python3 bench.py --config {a.workload} --steps 2 --warmup 1 --no-cpu-baseline --no-128k --no-window --no-layers")
     vals, durs = defaultdict(dict), defaultdict(list)
     for d in a.passes:
         for name, cs in read_counters(d).items():
