@@ -3,8 +3,11 @@
 
 One step = the whole hot path over one batch of synthetic input, all inputs
 resident in HBM before the timed region:
-  rope_relocate    every reused segment key, offline -> online position
-                   (out of place, so every step does identical work)
+  rope_relocate    every reused segment key, offline -> online position, in
+                   place in the pool (as a server rotates the cached keys it
+                   reuses); a replica's successive uses rotate by +delta and
+                   -delta in turn, so its keys keep their values and every
+                   step does identical work
   segpaged_prefill the new-token chunk of every (layer, KV head) slot, one call
   segpaged_decode  one decode token per sequence over every slot
 The page tables are built once beforehand by segpaged_build_tables on the
@@ -419,7 +422,10 @@ def run_config(name, seed, steps, warmup, log, window_only=False, per_layer=Fals
         # event before the relocation is the previous step's last (or ev0), so a
         # step records three markers, not four.
         a, b, c = reps[i % n_rep], reps[(i + 1) % n_rep], reps[(i + 2) % n_rep]
-        w.relocate(k_in=a[0], k_out=a[2])
+        # the replica's keys rotated in place, by +delta and -delta on its
+        # successive uses, so its pool keeps its values
+        w.relocate(k_in=a[0], k_out=a[0], back=bool(uses[i % n_rep] % 2))
+        uses[i % n_rep] += 1
         if ev:
             ev[0].record(stream)
         w.prefill(k=b[2], v=b[1])
@@ -429,6 +435,7 @@ def run_config(name, seed, steps, warmup, log, window_only=False, per_layer=Fals
         if ev:
             ev[2].record(stream)
 
+    uses = [0] * n_rep
     stream = torch.cuda.current_stream()
     # Everything the timed loop needs is made, and the garbage collected, before
     # the warm-up: a pause between the settle phase and the timed steps (a full

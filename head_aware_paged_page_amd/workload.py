@@ -112,10 +112,16 @@ class Workload:
         self.lse_decode = torch.empty(self.q_decode.shape[:2], dtype=torch.float32, device=device)
 
     # ------------------------------------------------------------------ calls
-    def relocate(self, k_in=None, k_out=None, stream=None):
+    def relocate(self, k_in=None, k_out=None, stream=None, back=False):
+        """rope_relocate of the workload's list, in place when k_in is k_out;
+        back=True rotates by the negated deltas (undoes a relocation in place)."""
         k_in = self.k_pool if k_in is None else k_in
         k_out = self.k_reloc if k_out is None else k_out
-        sp.rope_relocate(k_in, k_out, self.ps, self.d_reloc, self.lay.theta, stream=stream)
+        if back and getattr(self, "_d_reloc_back", None) is None:
+            self._d_reloc_back = self.d_reloc.clone()
+            self._d_reloc_back[:, 1] = -self._d_reloc_back[:, 1]
+        lst = self._d_reloc_back if back else self.d_reloc
+        sp.rope_relocate(k_in, k_out, self.ps, lst, self.lay.theta, stream=stream)
         return k_out
 
     def prefill(self, k=None, q=None, out=None, lse=None, stream=None, v=None):

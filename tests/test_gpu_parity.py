@@ -185,6 +185,28 @@ def test_relocate_plus_minus_delta_roundtrip():
 
 
 
+def test_relocate_in_place_matches_out_of_place():
+    """rope_relocate with the output buffer the input buffer (the bench's form:
+    each pool replica rotated in place, by +delta and -delta in turn) writes
+    exactly the bits the out-of-place call writes, on every page of the pool
+    (a thread rewrites only the elements it read); and back by -delta in place
+    returns the original keys within the relocation bound."""
+    for name in ("tiny", "32k"):
+        w = cached(name) if name != "tiny" else _wl(synth.make_layout(name))
+        w.relocate()                                         # k_pool -> k_reloc
+        tmp = w.k_pool.clone()
+        w.relocate(k_in=tmp, k_out=tmp)                      # in place
+        torch.cuda.synchronize()
+        ib = torch.int32 if tmp.dtype == torch.float32 else torch.int16
+        assert torch.equal(tmp.view(ib), w.k_reloc.view(ib)), f"{name}: in-place bits differ"
+        w.relocate(k_in=tmp, k_out=tmp, back=True)           # and back
+        torch.cuda.synchronize()
+        lay = w.lay
+        for r in _rows_by_class(lay, 1) if name != "tiny" else range(lay.n_slot):
+            slot, seq = divmod(r, lay.n_seq)
+            assert np.max(np.abs(w.gather_keys(tmp, slot, seq) - w.gather_keys(w.k_pool, slot, seq))) <= TOL[lay.dtype]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_relocate_large_deltas(dtype):
     """Position deltas near the int32 limit (2^30 - 5, -999 900, -2^30 + 350):
