@@ -240,9 +240,13 @@ int segpaged_release_pages(const sp_layout *layout, const int32_t *p_next, const
  *   k'[i+D/2]   = k[i+D/2] cos(delta w_i) + k[i] sin(delta w_i)
  *
  * k_in, k_out  K pools [n_phys][page_size][head_dim] of `dtype`; k_out may equal
- *              k_in (in place) but must not otherwise overlap it.  Only the
- *              first n_valid rows of each listed page are written.
- * d_list[n]    device relocation items (from segpaged_build_tables).
+ *              k_in (in place: each thread writes back exactly the elements
+ *              it read, so the result is bit-identical to out of place) but
+ *              must not otherwise overlap it.  Only the first n_valid rows of
+ *              each listed page are written.
+ * d_list[n]    device relocation items (from segpaged_build_tables); a page
+ *              listed twice is rotated by both deltas in place, and written
+ *              by two workgroups in no fixed order out of place.
  * head_dim     a power of two, 16..256; page_size 1..1024; rope_theta > 0.
  */
 int rope_relocate(const void *k_in, void *k_out, int dtype, int page_size, int head_dim,
