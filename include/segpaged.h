@@ -244,9 +244,10 @@ int segpaged_release_pages(const sp_layout *layout, const int32_t *p_next, const
  *              it read, so the result is bit-identical to out of place) but
  *              must not otherwise overlap it.  Only the first n_valid rows of
  *              each listed page are written.
- * d_list[n]    device relocation items (from segpaged_build_tables); a page
- *              listed twice is rotated by both deltas in place, and written
- *              by two workgroups in no fixed order out of place.
+ * d_list[n]    device relocation items (from segpaged_build_tables, which
+ *              lists each stored page once).  A page listed twice is read and
+ *              written by two workgroups in no fixed order, in place or out of
+ *              place, so its result is undefined: list each page once.
  * head_dim     a power of two, 16..256; page_size 1..1024; rope_theta > 0.
  */
 int rope_relocate(const void *k_in, void *k_out, int dtype, int page_size, int head_dim,
