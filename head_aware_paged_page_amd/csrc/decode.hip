@@ -15,7 +15,7 @@
 // The keys fed to the first product are permuted so that each lane's scores are
 // the 8 consecutive keys its B operand of the second product needs.  Each wave
 // streams 32-key blocks (one or two pages) with the next block's loads in
-// flight; the four waves of a workgroup merge through LDS at the end.
+// flight; the waves of a workgroup merge through LDS at the end.
 #include "device_common.hpp"
 
 namespace sp {
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(NWD * 64) __attribute__((amdgpu_waves_per_eu(3, 3))
         use(blk_regs);
     }
 
-    // ---- combine the four waves
+    // ---- combine the workgroup's waves
     float l = l_run + xor_lane(l_run, 16);
     l += xor_lane(l, 32);
     if (grp == 0) {

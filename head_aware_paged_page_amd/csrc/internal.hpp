@@ -21,7 +21,7 @@ int check_hip(hipError_t e, const char *what);
 constexpr int kPrefillRowsPerWave = 32;   // query rows (token x head) per wave
 constexpr int kPrefillKeysPerTile = 64;   // keys staged in LDS per iteration
 constexpr int kDecodeKeysPerBlock = 32;   // keys one wave consumes per step
-constexpr int kDecodeWaves = 4;
+constexpr int kDecodeWaves = 8;
 
 // Split planning: the prefill splits long rows so that their pieces fill the
 // 256 CUs of the chip once; decode aims at about one streaming split per CU.
@@ -31,7 +31,7 @@ constexpr int kPrefillSetupTiles = 6;      // fixed cost of a prefill item (set-
 constexpr int kPrefillEdgeTiles = 3;       // extra cost of a row end inside an item (bounds, fix-ups), in tiles
 constexpr double kMergeTiles = 1.5;        // merge pass per split prefill item, in 64-key tiles of one CU
 constexpr int kTargetDecodeItems = 384;
-constexpr int kDecodeWgPerCU = 2;          // decode workgroups per CU the plan aims for
+constexpr int kDecodeWgPerCU = 1;          // decode workgroups (of kDecodeWaves waves) per CU the plan aims for
 constexpr int kMinSplitKeysPrefill = 64;
 constexpr int kMinSplitKeysDecode = 512;
 constexpr int kMaxSplits = 1024;

@@ -203,13 +203,14 @@ int make_plan(int kind, int dtype, int head_dim, int page_size, int group, int n
         }
         p.chunk_pages = best_c;
     } else {
-        // Every item is resident at once (three fit on a CU), and a CU's share
-        // of the HBM stream depends on how many it holds: one decode workgroup
-        // per CU streams at about 4.5 TB/s chip-wide, two at about 6.6, and a
-        // CU holding one more than the rest finishes last.  So the chunk is the
-        // finest whose items fit kDecodeWgPerCU per CU (the item count falls
-        // as the chunk grows, so a bisection finds it); rows that alone
-        // outnumber that fall back to a fixed item target.
+        // Every item is resident at once, and a CU's share of the HBM stream
+        // depends on how many decode waves it holds: four per CU stream at
+        // about 4.5 TB/s chip-wide, eight at about 6.6, and a CU holding more
+        // than the rest finishes last.  So the chunk is the finest whose items
+        // fit kDecodeWgPerCU per CU (one workgroup of eight waves; two of four
+        // measured slightly slower, their items and partials twice as many);
+        // the item count falls as the chunk grows, so a bisection finds it.
+        // Rows that alone outnumber that fall back to a fixed item target.
         int e_max = 1;
         for (int r = 0; r < n_rows; ++r) e_max = std::max(e_max, h_row_ptr[r + 1] - h_row_ptr[r]);
         auto n_items = [&](int c) {
