@@ -715,6 +715,32 @@ def test_many_rows_with_splits():
     check_decode(w, rows=rows)
 
 
+def test_deep_merges_with_workspace_plans():
+    """200 slots (more than either plan in the kernel arguments holds, so the
+    plan kernel writes both plans to the workspace): one global row of 40 000
+    keys and 199 short local rows.  The prefill planner cuts the long row at
+    least 32 ways (checked through the workspace size the ABI reports: its
+    partials), so the merge takes its row-per-workgroup path reading the
+    workspace plan; the decode splits it too, merged by four waves per head."""
+    import head_aware_paged_page_amd.segpaged as sp
+    classes = [(GLOBAL, 0)] + [(LOCAL, 64)] * 199
+    lay = custom_layout(seg_lens=[[40000]], offline=[[0]], n_prefill=64, n_decode=1, classes=classes,
+                        page_size=16, head_dim=64, group=2, dtype="bf16", name="deep_merges", seed=5)
+    assert lay.n_slot * lay.n_seq == 200
+    w = _wl(lay)
+    # prefill workspace: a few KB of plan arrays, then per split item a fp16
+    # partial of 256 rows x 64 dims and 256 fp32 log-sum-exps (a lower bound
+    # on the item count: 57 here)
+    nb = sp.workspace_bytes(sp.SP_WS_PREFILL, sp.SP_BF16, 64, 16, 2, 1, 200, w.h_tok_ptr, w.tp["row_ptr"])
+    parts = (nb - 4 * 4 * 201 - 512) // (256 * 64 * 2 + 256 * 4)
+    assert parts >= 32, f"the long row is split {parts} ways"
+    rows = [0, 1, 100, 199]
+    w.prefill()
+    check_prefill(w, rows=rows)
+    w.decode()
+    check_decode(w, rows=rows)
+
+
 def _raw(t):
     return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu().numpy()
 
